@@ -1,0 +1,168 @@
+#!/usr/bin/env python3
+"""Bench: batch-1 cachedStep tokens/s of GPT-2 124M (fp32 and int8 group-64) on one
+MI355X, as absolute numbers and as a fraction of the HBM roofline, with the CPU
+oracle timed on the host beside it.
+
+A step is one cachedStep call: one token through the 12 blocks and the tied head.
+The workload is the 128-position session (uniform-random token ids, seed 101) of
+the seed-0 N(0, 0.02) checkpoint: the timed steps walk positions 0..127 and start
+over from an empty cache.  Inputs are resident in HBM before timing starts.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+FP32_MFMA_PEAK_TF = 157.3  # MI355X dense fp32 matrix
+
+# Algorithmic bytes of one batch-1 step at position p (shapes only):
+#   fp32: 48 block matrices 339,738,624 B + tied head 154,389,504 B + LayerNorm/bias
+#         485,376 B + two embedding rows 6,144 B = 494,619,648 B;
+#   int8: codes 123,532,032 B + group scales 7,720,752 B + LayerNorm/bias 485,376 B
+#         + embedding rows 6,144 B = 131,744,304 B;
+#   both: key/value rows read for positions 0..p (73,728 B each, the new one
+#         included) and 201,028 B of logits written.
+F32_FIXED = 494_619_648
+Q8_FIXED = 123_532_032 + 7_720_752 + 485_376 + 6_144
+KV_PER_POS = 73_728
+LOGITS = 201_028
+PREFILL_FLOP = 21_743_271_936 + 304_349_184  # block GEMMs + causal attention at T = 128
+
+
+def step_bytes(fixed: int, p: int) -> int:
+    return fixed + KV_PER_POS * (p + 1) + LOGITS
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1280)
+    ap.add_argument("--warmup", type=int, default=128)
+    ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU-oracle baseline leg")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the decode step is a single-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import stream_gpt_transformer_amd as g
+    import synth
+
+    dev = torch.device("cuda", int(os.environ.get("LOCAL_RANK", 0)))
+    torch.cuda.set_device(dev)
+    w = synth.make_checkpoint(0, synth.GPT2)
+    toks = synth.make_tokens(synth.SEED_SESSION, 128)
+    ck = torch.from_numpy(w).to(dev)
+    m = g.Model(ck, g.GPT2_PACK_F32 | g.GPT2_PACK_Q8)
+    torch.cuda.synchronize()
+    del ck
+    stream = torch.cuda.current_stream()
+    cache = m.new_cache(128)
+    logits = torch.empty(g.GPT2_VOCAB, dtype=torch.float32, device=dev)
+    h, ws, c, lp, s = m.handle, m.ws.data_ptr(), cache.data_ptr(), logits.data_ptr(), stream.cuda_stream
+    PER = g.GPT2_CACHE_WORDS_PER_POS
+
+    def run(fn, n, start=0):
+        for i in range(start, start + n):
+            p = i % 128
+            rc = fn(h, c, p * PER, int(toks[p]), p, ws, lp, s)
+            if rc:
+                raise g.Gpt2Error(rc, fn.__name__)
+
+    def timed(fn, steps, warmup):
+        run(fn, warmup)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run(fn, steps)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        nbytes = sum(step_bytes(F32_FIXED if fn is g.gpt2_cached_step else Q8_FIXED, i % 128) for i in range(steps))
+        return ms, nbytes
+
+    ms32, b32 = timed(g.gpt2_cached_step, args.steps, args.warmup)
+    ms8, b8 = timed(g.gpt2_q8_cached_step, args.steps, args.warmup)
+    tok32 = args.steps / (ms32 * 1e-3)
+    tok8 = args.steps / (ms8 * 1e-3)
+    gbs32 = b32 / (ms32 * 1e-3) / 1e9
+    gbs8 = b8 / (ms8 * 1e-3) / 1e9
+
+    # prefill: median of 20 infer(128) calls after warm-up
+    ptoks = synth.make_tokens(synth.SEED_PREFILL, 128).tolist()
+    for _ in range(3):
+        g.gpt2_infer(h, ptoks, ws, lp, s)
+    pts = []
+    for _ in range(20):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.gpt2_infer(h, ptoks, ws, lp, s)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pts.append(e0.elapsed_time(e1))
+    pms = statistics.median(pts)
+
+    cpu = None
+    if not args.skip_cpu:
+        import oracle
+        oracle.build() if not os.path.exists(oracle.LIB) else None
+        nthreads = min(os.cpu_count() or 1, 16)
+        oracle.set_threads(nthreads)
+        ocache = np.zeros(128 * PER, np.float32)
+        t0 = time.perf_counter()
+        n = 0
+        while n < 128 and time.perf_counter() - t0 < args.cpu_seconds:
+            rc, _ = oracle.cached_step(synth.GPT2, w, ocache, n * PER, int(toks[n]), n)
+            assert rc == 0
+            n += 1
+        el = time.perf_counter() - t0
+        cpu = {"value": round(n / el, 3), "unit": "tok/s", "cores": oracle.max_threads(), "kind": "oracle",
+               "sample": f"fp32 cachedStep positions 0..{n - 1} of the same 128-token session "
+                         f"({el:.1f} s, OpenMP over independent outputs)"}
+
+    out = {
+        "metric": "batch-1 cachedStep tok/s (fp32 & int8-g64) + % of HBM roofline",
+        "value": round(tok32, 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms32 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seed-0 N(0,0.02) weights, seeded uniform token ids)",
+        "config": {"workload": "GPT-2 124M batch-1 cachedStep, 128-position session, fp32",
+                   "positions": "0..127 cycled", "batch": 1},
+        "roofline": {"bound": "hbm", "achieved": round(gbs32, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs32 / HBM_PEAK_GBS, 4), "traffic": None},
+        "int8_g64": {"value": round(tok8, 1), "unit": "tok/s", "ms_per_step": round(ms8 / args.steps, 5),
+                     "roofline": {"bound": "hbm", "achieved": round(gbs8, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(gbs8 / HBM_PEAK_GBS, 4)}},
+        "prefill": {"value": round(128 / (pms * 1e-3), 1), "unit": "tok/s", "ms_median": round(pms, 4),
+                    "roofline": {"bound": "mfma", "achieved": round(PREFILL_FLOP / (pms * 1e-3) / 1e12, 2),
+                                 "peak": FP32_MFMA_PEAK_TF, "unit": "TFLOP/s",
+                                 "frac": round(PREFILL_FLOP / (pms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TF, 4)}},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    m.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

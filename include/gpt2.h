@@ -1,0 +1,185 @@
+/* gpt2.h — GPT-2 124M single-token cached decode, full-prefix inference and the
+ * int8 group-64 decode step on one AMD Instinct MI355X (gfx950).
+ *
+ * The model (LeanExe GPT-2 README, opening paragraph): 12 transformer blocks,
+ * width 768, 12 heads, feed-forward width 3,072, a 50,257-token vocabulary,
+ * binary32 arithmetic, weights supplied at run time.  Each block applies
+ * LayerNorm, the query/key/value projection, causal attention, the output
+ * projection with a residual add, LayerNorm and a tanh-GELU feed-forward network
+ * with a residual add; a final LayerNorm and the shared token-embedding matrix
+ * give the next-token logits.
+ *
+ * Conventions for every function below:
+ *  - Device pointers are plain addresses of device memory that the CALLER owns
+ *    (allocated by the caller, e.g. with torch); the library never allocates or
+ *    frees device memory.  Device pointers must be 16-byte aligned, except the
+ *    logits outputs, which need 4-byte alignment (rows of a [T][50257] array).
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued on it
+ *    and the call returns without waiting; GPT2_OK means "validated and
+ *    enqueued".  A device fault would surface at the caller's next
+ *    synchronisation.
+ *  - Validation is done on the host from the scalar arguments only.  On any error
+ *    the function returns a negative GPT2_E* code before enqueuing anything, and
+ *    no output is written (the pages' entry points return empty arrays on invalid
+ *    input).  Weight VALUES are never validated: non-finite binary32 weights are
+ *    legal input and propagate (LeanExe README: the execution theorem covers every
+ *    weight array of the right size, including exceptional values).
+ *  - Calls that share a workspace or a cache must be ordered on one stream;
+ *    concurrent streams need separate workspaces and caches.
+ */
+#ifndef GPT2_MI_H
+#define GPT2_MI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Shape constants (LeanExe GPT-2 README, opening and checkpoint paragraphs). */
+#define GPT2_LAYERS 12
+#define GPT2_DMODEL 768
+#define GPT2_HEADS 12
+#define GPT2_DFF 3072
+#define GPT2_VOCAB 50257
+#define GPT2_MAX_POS 128              /* positions 0..127 are accepted */
+#define GPT2_CKPT_WORDS 124439808u    /* packed checkpoint words ...   */
+#define GPT2_CKPT_BYTES 497759232u    /* ... and bytes                 */
+#define GPT2_CACHE_WORDS_PER_POS 18432 /* 12 layers x (768 keys + 768 values) */
+#define GPT2_MAX_BATCH 64
+
+enum {
+  GPT2_PACK_F32 = 1, /* binary32 [out][in] matrices for the fp32 step, infer and the batched step */
+  GPT2_PACK_Q8 = 2   /* int8 group-64 codes and scales for gpt2_q8_cached_step */
+};
+
+enum {
+  GPT2_OK = 0,
+  GPT2_EWEIGHTS = -1,  /* checkpoint length is not 497,759,232 bytes, or null */
+  GPT2_ETOKEN = -2,    /* token id >= 50,257, or a token array of length 0 or > 128 */
+  GPT2_EPOSITION = -3, /* position outside 0..127 */
+  GPT2_ECACHE = -4,    /* cache length != position * 18,432 words, or null cache */
+  GPT2_ENOTPACKED = -5,/* the model was not packed in the form this call needs */
+  GPT2_EARG = -6,      /* other invalid argument (null/misaligned pointer, short buffer, batch size) */
+  GPT2_EHIP = -7       /* a HIP call failed while enqueuing */
+};
+
+typedef struct gpt2_model gpt2_model; /* opaque host handle */
+
+/* Bytes of device memory the caller provides for the packed weights (flags: a
+ * nonzero OR of GPT2_PACK_*).  0 for invalid flags. */
+size_t gpt2_packed_nbytes(int flags);
+
+/* Bytes of device workspace one stream needs (activations of up to 64 sessions,
+ * the 128-row prefill buffers).  The workspace is scratch: its contents between
+ * calls do not matter. */
+size_t gpt2_workspace_nbytes(void);
+
+/* Re-lay the packed checkpoint for the device.
+ *  ckpt_dev     : 124,439,808 little-endian binary32 words in the order of the
+ *                 LeanExe README's checkpoint paragraph — token embeddings [50257][768],
+ *                 all 1,024 position rows [1024][768], 12 blocks, final LayerNorm
+ *                 gamma and beta.  Inside a block (GPT-2's own order, matrices
+ *                 [input][output]): ln1 gamma, ln1 beta, qkv weight [768][2304] with
+ *                 q|k|v columns, qkv bias, output-projection weight [768][768], its
+ *                 bias, ln2 gamma, ln2 beta, fc weight [768][3072], fc bias,
+ *                 mlp-projection weight [3072][768], its bias.
+ *  ckpt_nbytes  : must be 497,759,232 (GPT2_EWEIGHTS otherwise).
+ *  packed_dev   : >= gpt2_packed_nbytes(flags) bytes; written on `stream`.
+ *  flags        : GPT2_PACK_F32 and/or GPT2_PACK_Q8.  The int8 form follows the
+ *                 marXiv 2609.00018 abstract: every block matrix and the tied head,
+ *                 per output row and per group of 64 inputs, scale = max|w|/127,
+ *                 code = clamp(round-half-even(w/scale), -127, 127).
+ *  out          : receives a host handle that refers to packed_dev (which must
+ *                 stay allocated while the handle is used).  The checkpoint is
+ *                 not referenced after the enqueued packing work completes.
+ */
+int gpt2_pack_weights(const void* ckpt_dev, size_t ckpt_nbytes, void* packed_dev, size_t packed_nbytes,
+                      int flags, void* stream, gpt2_model** out);
+
+/* Free the host handle (device memory is the caller's). */
+void gpt2_release(gpt2_model* model);
+
+/* cachedStep (LeanExe GPT-2 README, cachedStep paragraph): one token at `position`.
+ *  cache_dev    : caller's cache with room for (position+1)*18,432 words.  Its first
+ *                 cache_nwords words are the incoming cache, ordered by prior position,
+ *                 then layer, then 768 keys and 768 values: word
+ *                 (source*12 + layer)*1536 + offset.  The step appends the current
+ *                 position's 12 key/value rows in place (the returned cache is the
+ *                 first (position+1)*18,432 words) and reads the supplied contents.
+ *  cache_nwords : must equal position * 18,432 (GPT2_ECACHE otherwise).
+ *  token        : 0..50,256.  position: 0..127.
+ *  ws_dev       : gpt2_workspace_nbytes() bytes.
+ *  logits_dev   : receives the 50,257 binary32 logits.
+ * Needs a model packed with GPT2_PACK_F32. */
+int gpt2_cached_step(const gpt2_model* model, float* cache_dev, size_t cache_nwords, uint32_t token,
+                     int32_t position, void* ws_dev, float* logits_dev, void* stream);
+
+/* The int8 group-64 cached step (marXiv 2609.00018 abstract): signed int8 weights
+ * and projection inputs with one binary32 scale per 64 consecutive coordinates,
+ * 32-bit integer group sums, binary32 everywhere else (embeddings, LayerNorm,
+ * attention, GELU, residuals, the cache).  Each projection input is quantized per
+ * group (scale = max|x|/127, code = clamp(round-half-even(x/scale), -127, 127)),
+ * acc[j][g] = sum of 64 code products, and the output is
+ * y = 0; y = y + ((float)acc[j][g] * wscale[j][g]) * xscale[g] for g = 0..G-1; y = y + bias.
+ * Same arguments and errors as gpt2_cached_step; needs GPT2_PACK_Q8. */
+int gpt2_q8_cached_step(const gpt2_model* model, float* cache_dev, size_t cache_nwords, uint32_t token,
+                        int32_t position, void* ws_dev, float* logits_dev, void* stream);
+
+/* B independent sessions (1..64) advanced by one token each.
+ *  caches_dev         : session b's cache starts at caches_dev + b*cache_stride_words;
+ *                       same layout and in-place append as gpt2_cached_step.
+ *  cache_stride_words : >= (max_b position[b] + 1) * 18,432 and a multiple of 4.
+ *  cache_nwords_host, tokens_host, positions_host : host arrays of B entries, each
+ *                       validated like gpt2_cached_step's scalars.
+ *  logits_dev         : [B][50,257].
+ * Session b's logits and cache are bit-identical to gpt2_cached_step run on that
+ * session alone.  Needs GPT2_PACK_F32. */
+int gpt2_batched_cached_step(const gpt2_model* model, float* caches_dev, size_t cache_stride_words,
+                             const size_t* cache_nwords_host, const uint32_t* tokens_host,
+                             const int32_t* positions_host, int B, void* ws_dev, float* logits_dev,
+                             void* stream);
+
+/* infer (LeanExe GPT-2 README, infer paragraph): recompute a prefix of n = 1..128
+ * tokens (host array; GPT2_ETOKEN for n outside 1..128 or any id >= 50,257) and
+ * write the final row's 50,257 logits.  Needs GPT2_PACK_F32. */
+int gpt2_infer(const gpt2_model* model, const uint32_t* tokens_host, int n, void* ws_dev, float* logits_dev,
+               void* stream);
+
+/* ---- test hooks (not needed by applications) -------------------------------- */
+
+/* Group-64 quantizer alone: n (a multiple of 64) values -> codes [n], scales [n/64]. */
+int gpt2_test_quantize(const float* x_dev, int n, int8_t* codes_dev, float* scales_dev, void* stream);
+
+/* C[M][N] = A[M][K] * W[N][K]^T with the prefill matrix-core kernel
+ * (M 1..128, N a multiple of 64, K a multiple of 32). */
+int gpt2_test_gemm(const float* A_dev, const float* W_dev, float* C_dev, int M, int N, int K, void* stream);
+
+/* Bytes of the capture buffer of gpt2_q8_cached_step_capture. */
+size_t gpt2_q8_capture_nbytes(void);
+
+/* Byte offset inside the capture buffer of projection `matrix` (0 qkv, 1 output
+ * projection, 2 fc, 3 mlp projection, 4 head) of `layer`, and of its parts:
+ * input binary32 [K], input codes int8 [K], input scales [K/64], accumulators
+ * int32 [N][K/64], output binary32 [N] (bias included, before residual/GELU). */
+int gpt2_q8_capture_offsets(int layer, int matrix, size_t* base, size_t* in, size_t* codes, size_t* scales,
+                            size_t* acc, size_t* out);
+
+/* gpt2_q8_cached_step that also records every projection's operands (above). */
+int gpt2_q8_cached_step_capture(const gpt2_model* model, float* cache_dev, size_t cache_nwords, uint32_t token,
+                                int32_t position, void* ws_dev, float* logits_dev, void* capture_dev,
+                                void* stream);
+
+/* Device addresses of a packed matrix: matrix 0 qkv [2304][768], 1 output
+ * projection [768][768], 2 fc [3072][768], 3 mlp projection [768][3072], 4 head
+ * [50257][768] (layer ignored).  fp32 rows for GPT2_PACK_F32 (the head is the
+ * token-embedding table), int8 codes and [rows][cols/64] scales for GPT2_PACK_Q8;
+ * a pointer is null when that form was not packed. */
+int gpt2_weight_view(const gpt2_model* model, int layer, int matrix, const float** f32_rows,
+                     const int8_t** q8_codes, const float** q8_scales, int* rows, int* cols);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

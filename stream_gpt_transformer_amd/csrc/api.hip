@@ -1,0 +1,197 @@
+// C-ABI of the library: host-side validation, the model handle and dispatch to the
+// kernel launchers.  Entry points and their input rules follow the LeanExe GPT-2
+// README (infer and cachedStep paragraphs) and the marXiv 2609.00018 abstract.
+#include <new>
+
+#include "../../include/gpt2.h"
+#include "internal.hpp"
+
+using namespace g2;
+
+struct gpt2_model {
+  Weights w;
+  int flags;
+  const void* packed;
+};
+
+namespace g2 {
+Work work_ptrs(void* ws, int max_batch) {
+  const WsLayout l = ws_layout(max_batch);
+  char* b = (char*)ws;
+  Work k{};
+  k.header = (uint32_t*)(b + l.header);
+  k.x = (float*)(b + l.x);
+  k.qkv = (float*)(b + l.qkv);
+  k.att = (float*)(b + l.att);
+  k.g = (float*)(b + l.g);
+  k.ll = (unsigned long long*)(b + l.ll);
+  k.pf_x = (float*)(b + l.pf_x);
+  k.pf_h = (float*)(b + l.pf_h);
+  k.pf_qkv = (float*)(b + l.pf_qkv);
+  k.pf_att = (float*)(b + l.pf_att);
+  k.pf_u = (float*)(b + l.pf_u);
+  k.pf_part = (float*)(b + l.pf_part);
+  return k;
+}
+}  // namespace g2
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+static bool aligned4(const void* p) { return ((uintptr_t)p & 3) == 0; }
+
+static int step_checks(const gpt2_model* m, int need_flag, const float* cache, size_t cache_nwords,
+                       uint32_t token, int32_t pos, const void* ws, const float* logits) {
+  if (!m) return GPT2_EARG;
+  if (!(m->flags & need_flag)) return GPT2_ENOTPACKED;
+  if (token >= (uint32_t)V) return GPT2_ETOKEN;
+  if (pos < 0 || pos >= PMAX) return GPT2_EPOSITION;
+  if (!cache || !aligned16(cache) || cache_nwords != (size_t)pos * CACHE_POS) return GPT2_ECACHE;
+  if (!ws || !aligned16(ws) || !logits || !aligned4(logits)) return GPT2_EARG;
+  return GPT2_OK;
+}
+
+extern "C" {
+
+size_t gpt2_packed_nbytes(int flags) {
+  if (flags < 1 || flags > 3) return 0;
+  return packed_layout(flags).total;
+}
+
+size_t gpt2_workspace_nbytes(void) { return ws_layout(MAX_BATCH).total; }
+
+int gpt2_pack_weights(const void* ckpt_dev, size_t ckpt_nbytes, void* packed_dev, size_t packed_nbytes,
+                      int flags, void* stream, gpt2_model** out) {
+  if (!out || flags < 1 || flags > 3) return GPT2_EARG;
+  if (!ckpt_dev || ckpt_nbytes != (size_t)ck::WORDS * 4) return GPT2_EWEIGHTS;
+  if (!aligned16(ckpt_dev)) return GPT2_EARG;
+  if (!packed_dev || !aligned16(packed_dev) || packed_nbytes < packed_layout(flags).total) return GPT2_EARG;
+  gpt2_model* m = new (std::nothrow) gpt2_model();
+  if (!m) return GPT2_EARG;
+  if (launch_pack((const float*)ckpt_dev, (char*)packed_dev, flags, (hipStream_t)stream) != hipSuccess) {
+    delete m;
+    return GPT2_EHIP;
+  }
+  const PackedLayout pl = packed_layout(flags);
+  const char* p = (const char*)packed_dev;
+  m->flags = flags;
+  m->packed = packed_dev;
+  m->w.wte = (const float*)(p + pl.wte);
+  m->w.wpe = (const float*)(p + pl.wpe);
+  m->w.small = (const float*)(p + pl.small);
+  m->w.f32 = (flags & 1) ? (const float*)(p + pl.f32) : nullptr;
+  m->w.q8c = (flags & 2) ? (const int8_t*)(p + pl.q8_codes) : nullptr;
+  m->w.q8s = (flags & 2) ? (const float*)(p + pl.q8_scales) : nullptr;
+  *out = m;
+  return GPT2_OK;
+}
+
+void gpt2_release(gpt2_model* model) { delete model; }
+
+int gpt2_cached_step(const gpt2_model* m, float* cache, size_t cache_nwords, uint32_t token, int32_t pos,
+                     void* ws, float* logits, void* stream) {
+  const int rc = step_checks(m, GPT2_PACK_F32, cache, cache_nwords, token, pos, ws, logits);
+  if (rc) return rc;
+  Sessions ss{};
+  ss.B = 1;
+  ss.tok[0] = token;
+  ss.pos[0] = pos;
+  const hipError_t e = launch_step_f32(m->w, work_ptrs(ws, MAX_BATCH), ss, cache, 0, logits, (hipStream_t)stream);
+  return e == hipSuccess ? GPT2_OK : GPT2_EHIP;
+}
+
+static int q8_step(const gpt2_model* m, float* cache, size_t cache_nwords, uint32_t token, int32_t pos, void* ws,
+                   float* logits, void* capture, void* stream) {
+  const int rc = step_checks(m, GPT2_PACK_Q8, cache, cache_nwords, token, pos, ws, logits);
+  if (rc) return rc;
+  if (capture && !aligned16(capture)) return GPT2_EARG;
+  Sessions ss{};
+  ss.B = 1;
+  ss.tok[0] = token;
+  ss.pos[0] = pos;
+  const hipError_t e =
+      launch_step_q8(m->w, work_ptrs(ws, MAX_BATCH), ss, cache, logits, (char*)capture, (hipStream_t)stream);
+  return e == hipSuccess ? GPT2_OK : GPT2_EHIP;
+}
+
+int gpt2_q8_cached_step(const gpt2_model* m, float* cache, size_t cache_nwords, uint32_t token, int32_t pos,
+                        void* ws, float* logits, void* stream) {
+  return q8_step(m, cache, cache_nwords, token, pos, ws, logits, nullptr, stream);
+}
+
+int gpt2_q8_cached_step_capture(const gpt2_model* m, float* cache, size_t cache_nwords, uint32_t token,
+                                int32_t pos, void* ws, float* logits, void* capture, void* stream) {
+  if (!capture) return GPT2_EARG;
+  return q8_step(m, cache, cache_nwords, token, pos, ws, logits, capture, stream);
+}
+
+int gpt2_batched_cached_step(const gpt2_model* m, float* caches, size_t stride, const size_t* cache_nwords,
+                             const uint32_t* tokens, const int32_t* positions, int B, void* ws, float* logits,
+                             void* stream) {
+  if (!m) return GPT2_EARG;
+  if (!(m->flags & GPT2_PACK_F32)) return GPT2_ENOTPACKED;
+  if (B < 1 || B > MAX_BATCH || !cache_nwords || !tokens || !positions) return GPT2_EARG;
+  if (!ws || !aligned16(ws) || !logits || !aligned4(logits)) return GPT2_EARG;
+  if (!caches || !aligned16(caches) || (stride & 3)) return GPT2_ECACHE;
+  Sessions ss{};
+  ss.B = B;
+  for (int b = 0; b < B; ++b) {
+    if (tokens[b] >= (uint32_t)V) return GPT2_ETOKEN;
+    if (positions[b] < 0 || positions[b] >= PMAX) return GPT2_EPOSITION;
+    if (cache_nwords[b] != (size_t)positions[b] * CACHE_POS) return GPT2_ECACHE;
+    if (stride < (size_t)(positions[b] + 1) * CACHE_POS) return GPT2_ECACHE;
+    ss.tok[b] = tokens[b];
+    ss.pos[b] = positions[b];
+  }
+  const hipError_t e =
+      launch_step_f32(m->w, work_ptrs(ws, MAX_BATCH), ss, caches, stride, logits, (hipStream_t)stream);
+  return e == hipSuccess ? GPT2_OK : GPT2_EHIP;
+}
+
+int gpt2_infer(const gpt2_model* m, const uint32_t* tokens, int n, void* ws, float* logits, void* stream) {
+  if (!m) return GPT2_EARG;
+  if (!(m->flags & GPT2_PACK_F32)) return GPT2_ENOTPACKED;
+  if (!tokens || n < 1 || n > PMAX) return GPT2_ETOKEN;
+  for (int t = 0; t < n; ++t)
+    if (tokens[t] >= (uint32_t)V) return GPT2_ETOKEN;
+  if (!ws || !aligned16(ws) || !logits || !aligned4(logits)) return GPT2_EARG;
+  const hipError_t e = launch_infer(m->w, work_ptrs(ws, MAX_BATCH), tokens, n, logits, (hipStream_t)stream);
+  return e == hipSuccess ? GPT2_OK : GPT2_EHIP;
+}
+
+int gpt2_test_quantize(const float* x, int n, int8_t* codes, float* scales, void* stream) {
+  if (n < 0 || n % 64 || (n && (!x || !codes || !scales))) return GPT2_EARG;
+  return launch_quantize(x, n, codes, scales, (hipStream_t)stream) == hipSuccess ? GPT2_OK : GPT2_EHIP;
+}
+
+int gpt2_test_gemm(const float* A, const float* W, float* C, int M, int N, int K, void* stream) {
+  if (!A || !W || !C || M < 1 || M > PMAX || N < 64 || N % 64 || K < 32 || K % 32) return GPT2_EARG;
+  return launch_gemm_test(A, W, C, M, N, K, (hipStream_t)stream) == hipSuccess ? GPT2_OK : GPT2_EHIP;
+}
+
+size_t gpt2_q8_capture_nbytes(void) { return cap_total(); }
+
+int gpt2_q8_capture_offsets(int layer, int matrix, size_t* base, size_t* in, size_t* codes, size_t* scales,
+                            size_t* acc, size_t* out) {
+  if (matrix < 0 || matrix > 4 || (matrix < 4 && (layer < 0 || layer >= L))) return GPT2_EARG;
+  const CapLayout c = cap_item(matrix);
+  const size_t b = cap_offset(matrix == 4 ? 0 : layer, matrix);
+  if (base) *base = b;
+  if (in) *in = b + c.in;
+  if (codes) *codes = b + c.codes;
+  if (scales) *scales = b + c.xs;
+  if (acc) *acc = b + c.acc;
+  if (out) *out = b + c.y;
+  return GPT2_OK;
+}
+
+int gpt2_weight_view(const gpt2_model* m, int layer, int matrix, const float** f32_rows, const int8_t** codes,
+                     const float** scales, int* rows, int* cols) {
+  if (!m || matrix < 0 || matrix > 4 || (matrix < 4 && (layer < 0 || layer >= L))) return GPT2_EARG;
+  if (rows) *rows = mat_rows(matrix);
+  if (cols) *cols = mat_cols(matrix);
+  if (f32_rows) *f32_rows = matrix == 4 ? m->w.wte : (m->w.f32 ? f32_mat(m->w, layer, matrix) : nullptr);
+  if (codes) *codes = m->w.q8c ? q8_codes(m->w, layer, matrix) : nullptr;
+  if (scales) *scales = m->w.q8s ? q8_scales(m->w, layer, matrix) : nullptr;
+  return GPT2_OK;
+}
+
+}  // extern "C"

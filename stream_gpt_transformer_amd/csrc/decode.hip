@@ -1,0 +1,344 @@
+// Decode-step kernels: one token per session through the 12 blocks and the tied
+// head (LeanExe GPT-2 README, cachedStep paragraph), binary32 and int8 group-64
+// (marXiv 2609.00018 abstract).
+//
+// Each phase of a block is one kernel here.  The projections stream weight rows
+// with 1 KB coalesced wave loads (lane fragments, device.hpp), keep them in
+// registers and apply them to every session of the launch, so a batch of B
+// sessions reads each weight once and every output keeps the batch-1 arithmetic.
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace g2 {
+
+enum Mode { MODE_QKV = M_QKV, MODE_O = M_O, MODE_FC = M_FC, MODE_PR = M_PR, MODE_HEAD = M_HEAD };
+
+struct ProjArgs {
+  Weights w;
+  Work k;
+  Sessions ss;
+  float* caches;        // session b's cache starts at caches + b*cache_stride
+  size_t cache_stride;  // words
+  float* logits;        // [B][V]
+  char* capture;        // int8 path capture buffer or null
+  int layer;
+};
+
+template <class T>
+__device__ __forceinline__ T nt_load(const T* p) {
+  return __builtin_nontemporal_load(p);
+}
+
+// x += wte[tok] + wpe[pos]: one block of 192 threads per session.
+__global__ __launch_bounds__(192) void k_embed(const Weights w, const Sessions ss, float* x) {
+  const int b = blockIdx.x, t = threadIdx.x;
+  const f4 e = *(const f4*)(w.wte + (size_t)ss.tok[b] * D + 4 * t);
+  const f4 p = *(const f4*)(w.wpe + (size_t)ss.pos[b] * D + 4 * t);
+  *(f4*)(x + (size_t)b * D + 4 * t) = e + p;
+}
+
+template <int MODE>
+__device__ __forceinline__ constexpr int mode_rows() {
+  return MODE == MODE_QKV ? D3 : MODE == MODE_FC ? F : MODE == MODE_HEAD ? V : D;
+}
+template <int MODE>
+__device__ __forceinline__ constexpr bool mode_ln() {
+  return MODE == MODE_QKV || MODE == MODE_FC || MODE == MODE_HEAD;
+}
+
+// Projection input of session b: LN1(x), attention output, LN2(x), GELU output,
+// LN_f(x) for QKV, O, FC, PR, HEAD.
+template <int MODE, int NI>
+__device__ __forceinline__ void proj_input(const ProjArgs& a, int b, f4 (&x)[NI]) {
+  const float* src = MODE == MODE_O ? a.k.att + (size_t)b * D
+                     : MODE == MODE_PR ? a.k.g + (size_t)b * F
+                                       : a.k.x + (size_t)b * D;
+  load_frag<NI>(x, src);
+  if constexpr (mode_ln<MODE>()) {
+    const float* gam = MODE == MODE_QKV ? small_p(a.w, a.layer, sp::LN1_G)
+                       : MODE == MODE_FC ? small_p(a.w, a.layer, sp::LN2_G)
+                                         : a.w.small + sp::LNF_G;
+    const float* bet = MODE == MODE_QKV ? small_p(a.w, a.layer, sp::LN1_B)
+                       : MODE == MODE_FC ? small_p(a.w, a.layer, sp::LN2_B)
+                                         : a.w.small + sp::LNF_B;
+    layernorm_frag(*reinterpret_cast<f4(*)[3]>(&x), gam, bet);
+  }
+}
+
+// Epilogue of output r of session b; y is the projection value including bias.
+template <int MODE>
+__device__ __forceinline__ void proj_store(const ProjArgs& a, int b, int r, float y) {
+  if constexpr (MODE == MODE_QKV) {
+    a.k.qkv[(size_t)b * D3 + r] = y;
+    if (r >= D) {
+      float* cache = a.caches + (size_t)b * a.cache_stride;
+      cache[((size_t)a.ss.pos[b] * L + a.layer) * KV_ROW + (r - D)] = y;
+    }
+  } else if constexpr (MODE == MODE_O || MODE == MODE_PR) {
+    float* x = a.k.x + (size_t)b * D + r;
+    *x = *x + y;
+  } else if constexpr (MODE == MODE_FC) {
+    a.k.g[(size_t)b * F + r] = gelu_tanh(y);
+  } else {
+    a.logits[(size_t)b * V + r] = y;
+  }
+}
+
+template <int MODE>
+__device__ __forceinline__ float proj_bias(const ProjArgs& a, int r) {
+  if constexpr (MODE == MODE_QKV) return small_p(a.w, a.layer, sp::B_QKV)[r];
+  else if constexpr (MODE == MODE_O) return small_p(a.w, a.layer, sp::B_O)[r];
+  else if constexpr (MODE == MODE_FC) return small_p(a.w, a.layer, sp::B_FC)[r];
+  else if constexpr (MODE == MODE_PR) return small_p(a.w, a.layer, sp::B_PR)[r];
+  else return 0.0f;
+}
+
+// fp32 projection over B sessions.  Block = 4 waves; wave w owns RPW consecutive
+// output rows, whose weights it loads once; sessions are staged BT at a time in
+// LDS as (normalised) input fragments.  Output r of session b is
+// dot_frag(W_r, x_b) + bias_r — the same value for any B, RPW or BT.
+template <int MODE, int RPW, int BT>
+__global__ __launch_bounds__(256) void k_proj(const ProjArgs a) {
+  constexpr int NI = MODE == MODE_PR ? F / 256 : D / 256;
+  constexpr int K = 256 * NI;
+  constexpr int NROWS = mode_rows<MODE>();
+  __shared__ __align__(16) float xs[BT][K];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row0 = (blockIdx.x * 4 + wave) * RPW;
+  const float* W = MODE == MODE_HEAD ? a.w.wte : f32_mat(a.w, a.layer, MODE);
+  f4 w[RPW][NI];
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    const int r = row0 + rr;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      w[rr][i] = r < NROWS ? nt_load((const f4*)(W + (size_t)r * K + 256 * i + 4 * lane)) : f4{0, 0, 0, 0};
+  }
+  float bias[RPW];
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) bias[rr] = row0 + rr < NROWS ? proj_bias<MODE>(a, row0 + rr) : 0.0f;
+  for (int b0 = 0; b0 < a.ss.B; b0 += BT) {
+    const int nb = min(BT, a.ss.B - b0);
+    __syncthreads();
+    for (int s = wave; s < nb; s += 4) {
+      f4 x[NI];
+      proj_input<MODE, NI>(a, b0 + s, x);
+      store_frag<NI>(&xs[s][0], x);
+    }
+    __syncthreads();
+    for (int s = 0; s < nb; ++s) {
+      f4 x[NI];
+      load_frag<NI>(x, &xs[s][0]);
+#pragma unroll
+      for (int rr = 0; rr < RPW; ++rr) {
+        const int r = row0 + rr;
+        if (r >= NROWS) break;
+        const float y = dot_frag<NI>(w[rr], x) + bias[rr];
+        if (lane == 0) proj_store<MODE>(a, b0 + s, r, y);
+      }
+    }
+  }
+}
+
+// Attention of head blockIdx.x for session blockIdx.y over its positions 0..pos,
+// reading every key/value row (the current one included) from the session's cache
+// at (source*12 + layer)*1536 + offset.
+__global__ __launch_bounds__(128) void k_attn(const ProjArgs a) {
+  __shared__ AttnSmem sm;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int npos = a.ss.pos[b] + 1;
+  const float* cache = a.caches + (size_t)b * a.cache_stride;
+  const int l = a.layer;
+  auto kv = [&](int j) { return cache + ((size_t)j * L + l) * KV_ROW + h * DH; };
+  attn_stage(sm, kv, npos, a.k.qkv + (size_t)b * D3 + h * DH);
+  __syncthreads();
+  const float o = attn_compute(sm, npos);
+  if (threadIdx.x < DH) a.k.att[(size_t)b * D + h * DH + threadIdx.x] = o;
+}
+
+// ---- int8 group-64 projections (batch 1) -------------------------------------
+// The block quantizes its fp32 input in LDS (every block does the same work and
+// gets the same codes), then each wave streams its rows' int8 codes: lane l takes
+// 16 codes at byte 1024*i + 16*l, so group 16*i + l/4; v_dot4 gives a lane partial
+// and two exact integer butterfly steps give the group accumulator.  The rescale
+// runs in one fixed order: y = 0; y = y + ((float)acc_g * sw_g) * sx_g for
+// g = 0..G-1; y = y + bias.
+template <int MODE, int RPW>
+__global__ __launch_bounds__(256) void k_q8proj(const ProjArgs a) {
+  constexpr int K = MODE == MODE_PR ? F : D;
+  constexpr int NI = K / 256;
+  constexpr int G = K / 64;
+  constexpr int NCH = (K + 1023) / 1024;
+  constexpr int NROWS = mode_rows<MODE>();
+  __shared__ __align__(16) float xf[K];
+  __shared__ __align__(16) int8_t xc[K];
+  __shared__ float xsc[G];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const CapLayout cl = cap_item(MODE);
+  char* cap = a.capture ? a.capture + cap_offset(a.layer, MODE) : nullptr;
+
+  if (wave == 0) {
+    f4 x[NI];
+    proj_input<MODE, NI>(a, 0, x);
+    store_frag<NI>(xf, x);
+  }
+  __syncthreads();
+  for (int g = wave; g < G; g += 4) {
+    float s;
+    const int c = quant_lane(xf[g * 64 + lane], s);
+    xc[g * 64 + lane] = (int8_t)c;
+    if (lane == 0) xsc[g] = s;
+  }
+  __syncthreads();
+  if (cap && blockIdx.x == 0) {
+    for (int i = threadIdx.x; i < K; i += 256) {
+      ((float*)(cap + cl.in))[i] = xf[i];
+      ((int8_t*)(cap + cl.codes))[i] = xc[i];
+    }
+    if (threadIdx.x < G) ((float*)(cap + cl.xs))[threadIdx.x] = xsc[threadIdx.x];
+  }
+
+  const int8_t* codes = q8_codes(a.w, a.layer, MODE);
+  const float* scales = q8_scales(a.w, a.layer, MODE);
+  const int row0 = (blockIdx.x * 4 + wave) * RPW;
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    const int r = row0 + rr;
+    if (r >= NROWS) break;
+    const int8_t* wr = codes + (size_t)r * K;
+    int acc[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int off = 1024 * i + 16 * lane;
+      int p = 0;
+      if (off < K) {
+        const i4 wv = nt_load((const i4*)(wr + off));
+        const i4 xv = *(const i4*)(xc + off);
+        p = __builtin_amdgcn_sdot4(wv.x, xv.x, p, false);
+        p = __builtin_amdgcn_sdot4(wv.y, xv.y, p, false);
+        p = __builtin_amdgcn_sdot4(wv.z, xv.z, p, false);
+        p = __builtin_amdgcn_sdot4(wv.w, xv.w, p, false);
+      }
+      p += __shfl_xor(p, 1);
+      p += __shfl_xor(p, 2);
+      acc[i] = p;
+    }
+    const float swl = lane < G ? scales[(size_t)r * G + lane] : 0.0f;
+    float y = 0.0f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int ag = __shfl(acc[g / 16], (g % 16) * 4);
+      const float sg = __shfl(swl, g);
+      y = y + ((float)ag * sg) * xsc[g];
+    }
+    y = y + proj_bias<MODE>(a, r);
+    if (cap) {
+      int32_t* ca = (int32_t*)(cap + cl.acc) + (size_t)r * G;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int g = 16 * i + lane / 4;
+        if ((lane & 3) == 0 && g < G) ca[g] = acc[i];
+      }
+      if (lane == 0) ((float*)(cap + cl.y))[r] = y;
+    }
+    if (lane == 0) proj_store<MODE>(a, 0, r, y);
+  }
+}
+
+// Stand-alone group-64 quantizer (test hook): block g quantizes x[64g .. 64g+63].
+__global__ __launch_bounds__(64) void k_quantize(const float* x, int8_t* codes, float* scales) {
+  const int g = blockIdx.x, lane = threadIdx.x;
+  float s;
+  const int c = quant_lane(x[(size_t)g * 64 + lane], s);
+  codes[(size_t)g * 64 + lane] = (int8_t)c;
+  if (lane == 0) scales[g] = s;
+}
+
+// ---- launchers ---------------------------------------------------------------
+
+template <int MODE, int RPW, int BT>
+static void launch_proj(const ProjArgs& a, hipStream_t s) {
+  const int rows = MODE == MODE_QKV ? D3 : MODE == MODE_FC ? F : MODE == MODE_HEAD ? V : D;
+  const int nblk = (rows + 4 * RPW - 1) / (4 * RPW);
+  hipLaunchKernelGGL((k_proj<MODE, RPW, BT>), dim3(nblk), dim3(256), 0, s, a);
+}
+
+template <int RPW, int BT768, int BT3072>
+static void launch_layers(ProjArgs& a, hipStream_t s) {
+  const int B = a.ss.B;
+  for (int l = 0; l < L; ++l) {
+    a.layer = l;
+    launch_proj<MODE_QKV, RPW, BT768>(a, s);
+    hipLaunchKernelGGL(k_attn, dim3(H, B), dim3(128), 0, s, a);
+    launch_proj<MODE_O, RPW, BT768>(a, s);
+    launch_proj<MODE_FC, RPW, BT768>(a, s);
+    launch_proj<MODE_PR, RPW, BT3072>(a, s);
+  }
+  launch_proj<MODE_HEAD, RPW, BT768>(a, s);
+}
+
+hipError_t launch_step_f32(const Weights& w, const Work& k, const Sessions& ss, float* caches,
+                           size_t cache_stride, float* logits, hipStream_t s) {
+  ProjArgs a{};
+  a.w = w;
+  a.k = k;
+  a.ss = ss;
+  a.caches = caches;
+  a.cache_stride = cache_stride;
+  a.logits = logits;
+  a.capture = nullptr;
+  hipLaunchKernelGGL(k_embed, dim3(ss.B), dim3(192), 0, s, w, ss, k.x);
+  if (ss.B == 1)
+    launch_layers<2, 1, 1>(a, s);
+  else
+    launch_layers<4, 16, 4>(a, s);
+  return hipGetLastError();
+}
+
+template <int MODE, int RPW>
+static void launch_q8(const ProjArgs& a, hipStream_t s) {
+  const int rows = MODE == MODE_QKV ? D3 : MODE == MODE_FC ? F : MODE == MODE_HEAD ? V : D;
+  const int nblk = (rows + 4 * RPW - 1) / (4 * RPW);
+  hipLaunchKernelGGL((k_q8proj<MODE, RPW>), dim3(nblk), dim3(256), 0, s, a);
+}
+
+hipError_t launch_step_q8(const Weights& w, const Work& k, const Sessions& ss, float* cache,
+                          float* logits, char* capture, hipStream_t s) {
+  ProjArgs a{};
+  a.w = w;
+  a.k = k;
+  a.ss = ss;
+  a.caches = cache;
+  a.cache_stride = 0;
+  a.logits = logits;
+  a.capture = capture;
+  hipLaunchKernelGGL(k_embed, dim3(1), dim3(192), 0, s, w, ss, k.x);
+  for (int l = 0; l < L; ++l) {
+    a.layer = l;
+    launch_q8<MODE_QKV, 2>(a, s);
+    hipLaunchKernelGGL(k_attn, dim3(H, 1), dim3(128), 0, s, a);
+    launch_q8<MODE_O, 2>(a, s);
+    launch_q8<MODE_FC, 2>(a, s);
+    launch_q8<MODE_PR, 2>(a, s);
+  }
+  launch_q8<MODE_HEAD, 4>(a, s);
+  return hipGetLastError();
+}
+
+// Final LayerNorm and tied head of one residual row (used by the full-prefix path).
+hipError_t launch_head_f32(const Weights& w, const float* x_row, float* logits, hipStream_t s) {
+  ProjArgs a{};
+  a.w = w;
+  a.k.x = const_cast<float*>(x_row);
+  a.ss.B = 1;
+  a.logits = logits;
+  launch_proj<MODE_HEAD, 2, 1>(a, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const float* x, int n, int8_t* codes, float* scales, hipStream_t s) {
+  if (n > 0) hipLaunchKernelGGL(k_quantize, dim3(n / 64), dim3(64), 0, s, x, codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace g2

@@ -1,0 +1,64 @@
+// Internal interface between the C-ABI layer and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "layout.hpp"
+
+namespace g2 {
+
+// Device pointers into a packed weight buffer.
+struct Weights {
+  const float* wte;    // [V][D] token embeddings = tied head matrix
+  const float* wpe;    // [PMAX][D]
+  const float* small;  // per-layer LayerNorm parameters and biases (sp:: offsets)
+  const float* f32;    // per-layer [out][in] fp32 matrices, or null
+  const int8_t* q8c;   // per-layer [out][in] int8 codes, then the head [V][D], or null
+  const float* q8s;    // per-layer [out][in/64] scales, then the head [V][D/64], or null
+};
+
+__host__ __device__ inline const float* f32_mat(const Weights& w, int layer, int m) {
+  return w.f32 + (size_t)layer * LAYER_ELEMS + mat_elem_off(m);
+}
+__host__ __device__ inline const int8_t* q8_codes(const Weights& w, int layer, int m) {
+  return m == M_HEAD ? w.q8c + (size_t)L * LAYER_ELEMS : w.q8c + (size_t)layer * LAYER_ELEMS + mat_elem_off(m);
+}
+__host__ __device__ inline const float* q8_scales(const Weights& w, int layer, int m) {
+  return m == M_HEAD ? w.q8s + (size_t)L * LAYER_SCALES : w.q8s + (size_t)layer * LAYER_SCALES + mat_scale_off(m);
+}
+__host__ __device__ inline const float* small_p(const Weights& w, int layer, int off) {
+  return w.small + (size_t)layer * sp::PER_LAYER + off;
+}
+
+// Sessions advanced by one decode launch (kernel argument, <= 4 KB).
+struct Sessions {
+  int B;
+  uint32_t tok[MAX_BATCH];
+  int32_t pos[MAX_BATCH];
+};
+
+// Workspace pointers.
+struct Work {
+  uint32_t* header;
+  float* x;    // [B][D] residual stream
+  float* qkv;  // [B][3D]
+  float* att;  // [B][D]
+  float* g;    // [B][F]
+  unsigned long long* ll;
+  float *pf_x, *pf_h, *pf_qkv, *pf_att, *pf_u, *pf_part;
+};
+
+Work work_ptrs(void* ws, int max_batch);
+
+hipError_t launch_pack(const float* ckpt, char* packed, int flags, hipStream_t s);
+hipError_t launch_step_f32(const Weights& w, const Work& k, const Sessions& ss, float* caches,
+                           size_t cache_stride, float* logits, hipStream_t s);
+hipError_t launch_step_q8(const Weights& w, const Work& k, const Sessions& ss, float* cache,
+                          float* logits, char* capture, hipStream_t s);
+hipError_t launch_infer(const Weights& w, const Work& k, const uint32_t* toks, int n, float* logits,
+                        hipStream_t s);
+hipError_t launch_quantize(const float* x, int n, int8_t* codes, float* scales, hipStream_t s);
+hipError_t launch_gemm_test(const float* A, const float* W, float* C, int M, int N, int K, hipStream_t s);
+
+}  // namespace g2
