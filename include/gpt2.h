@@ -152,6 +152,14 @@ int gpt2_infer(const gpt2_model* model, const uint32_t* tokens_host, int n, void
 /* Group-64 quantizer alone: n (a multiple of 64) values -> codes [n], scales [n/64]. */
 int gpt2_test_quantize(const float* x_dev, int n, int8_t* codes_dev, float* scales_dev, void* stream);
 
+/* The library's exponential (kind 0) or tanh (kind 1) of every binary32 value whose
+ * bit pattern is first_bits + i, i < n, into y[i].  The exponential is the ordered
+ * binary32 approximation the decode path uses (LeanExe GPT-2 README, numerical
+ * functions): k = rint(x*log2 e), Cody-Waite reduction r = (x - k*ln2_hi) - k*ln2_lo,
+ * a degree-7 Taylor polynomial of e^r by Horner, times 2^k; x < -87 gives 0 and
+ * x >= 88.72283935546875 gives +inf.  tanh(z) = 1 - 2/(exp(2|z|) + 1) with the sign of z. */
+int gpt2_test_special(int kind, uint32_t first_bits, size_t n, float* y, void* stream);
+
 /* C[M][N] = A[M][K] * W[N][K]^T with the prefill matrix-core kernel
  * (M 1..128, N a multiple of 64, K a multiple of 32). */
 int gpt2_test_gemm(const float* A_dev, const float* W_dev, float* C_dev, int M, int N, int K, void* stream);

@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         "oracle_layernorm": (None, [ctypes.c_int, _f32p, _f32p, _f32p, _f32p]),
         "oracle_linear": (None, [ctypes.c_int, ctypes.c_int, _f32p, _f32p, ctypes.c_void_p, _f32p]),
         "oracle_gelu": (None, [ctypes.c_int, _f32p, _f32p]),
+        "oracle_special": (None, [ctypes.c_int, ctypes.c_longlong, _f32p, _f32p]),
+        "oracle_special_bits": (None, [ctypes.c_int, ctypes.c_uint32, ctypes.c_longlong, _f32p]),
         "oracle_attention_head": (None, [ctypes.c_int, _f32p, _f32p, _f32p, ctypes.c_int,
                                          ctypes.c_int, _f32p, _f32p]),
         "oracle_quantize": (ctypes.c_int, [ctypes.c_int, _f32p, _i8p, _f32p]),
@@ -204,6 +206,27 @@ def linear(x, W_in_out, b=None) -> np.ndarray:
 def gelu(x) -> np.ndarray:
     y = np.zeros_like(x)
     lib().oracle_gelu(x.size, x, y)
+    return y
+
+
+def exp_spec(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.zeros_like(x)
+    lib().oracle_special(0, x.size, x, y)
+    return y
+
+
+def tanh_spec(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.zeros_like(x)
+    lib().oracle_special(1, x.size, x, y)
+    return y
+
+
+def special_bits(kind: int, first: int, n: int) -> np.ndarray:
+    """f(x) for every binary32 bit pattern first..first+n-1 (kind 0 exp, 1 tanh)."""
+    y = np.zeros(n, np.float32)
+    lib().oracle_special_bits(kind, first, n, y)
     return y
 
 

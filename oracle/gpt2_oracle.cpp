@@ -10,8 +10,9 @@
 // sequentially in ascending index order; every product is rounded before it is
 // added (built with -ffp-contract=off -fno-fast-math, the muInference page's "IEEE
 // ops" table rule that FMA is not used where the source rounds twice).  Division
-// and sqrtf are the correctly rounded IEEE operations.  expf and tanhf are the
-// C library's.
+// and sqrtf are the correctly rounded IEEE operations.  The exponential is not the
+// C library's: it is the ordered binary32 approximation defined below (exp_spec),
+// and tanh is derived from it, so the whole forward pass is specified to the bit.
 //
 // Parity pins (see tests/test_oracle_*.py): closed-form sizes, the full-prefix ==
 // cached recurrence identity, single-key attention == V exactly, softmax mass,
@@ -161,11 +162,56 @@ void linear(int K, int N, const float* x, const float* W, const float* b, float*
   }
 }
 
+// ---- ordered binary32 exponential -------------------------------------------
+// LeanExe GPT-2 README (source table, numerical functions) names an "ordered
+// binary32 exponential approximation"; the muInference page (IEEE-ops table)
+// builds exp from range reduction, a Taylor polynomial and 2^k assembled as a
+// bit pattern, using only correctly rounded operations.  Definition used here,
+// every step one rounded binary32 operation in this order:
+//   x NaN -> x;  x >= 88.72283935546875 -> +inf;  x < -87 -> 0 (no subnormal results);
+//   k = rint(x * log2(e));  r = (x - k*LN2_HI) - k*LN2_LO   (LN2_HI has 12 zero low bits,
+//       so k*LN2_HI is exact);
+//   p = 1/5040;  p = p*r + c for c = 1/720, 1/120, 1/24, 1/6, 1/2, 1, 1  (Horner, degree 7);
+//   result = p * 2^k  (k = 128 is taken as (p*2) * 2^127).
+float exp_spec(float x) {
+  if (x != x) return x;
+  if (x >= 88.72283935546875f) return INFINITY;
+  if (x < -87.0f) return 0.0f;
+  const float kf = std::rint(x * 1.44269502162933349609375f);
+  const float LN2_HI = 0.693145751953125f;      // 0x3f317200
+  const float LN2_LO = 1.428606765330187e-06f;  // ln 2 - LN2_HI
+  const float r = (x - kf * LN2_HI) - kf * LN2_LO;
+  float p = 1.0f / 5040.0f;
+  p = p * r + 1.0f / 720.0f;
+  p = p * r + 1.0f / 120.0f;
+  p = p * r + 1.0f / 24.0f;
+  p = p * r + 1.0f / 6.0f;
+  p = p * r + 0.5f;
+  p = p * r + 1.0f;
+  p = p * r + 1.0f;
+  int k = (int)kf;
+  if (k == 128) {
+    p = p * 2.0f;
+    k = 127;
+  }
+  uint32_t bits = (uint32_t)(k + 127) << 23;
+  float scale;
+  std::memcpy(&scale, &bits, 4);
+  return p * scale;
+}
+
+// tanh from the exponential: t = 1 - 2/(exp(2|z|) + 1), sign of z restored.
+float tanh_spec(float z) {
+  const float e = exp_spec(2.0f * std::fabs(z));
+  const float t = 1.0f - 2.0f / (e + 1.0f);
+  return z < 0.0f ? -t : t;
+}
+
 // tanh form of GELU: 0.5*u*(1 + tanh(sqrt(2/pi)*(u + 0.044715*u^3))).
 float gelu(float u) {
   const float c = 0.7978845608028654f;  // sqrt(2/pi) rounded to binary32
   const float inner = u + 0.044715f * (u * u * u);
-  const float t = std::tanh(c * inner);
+  const float t = tanh_spec(c * inner);
   return (0.5f * u) * (1.0f + t);
 }
 
@@ -188,7 +234,7 @@ void attend_head(int dh, const float* q, const float* kbase, const float* vbase,
     if (s[j] > m) m = s[j];
   float Z = 0.0f;
   for (int j = 0; j < npos; ++j) {
-    e[j] = std::exp(s[j] - m);
+    e[j] = exp_spec(s[j] - m);
     Z = Z + e[j];
   }
   for (int j = 0; j < npos; ++j) e[j] = e[j] / Z;  // now the weights w_j
@@ -566,6 +612,23 @@ void oracle_linear(int K, int N, const float* x, const float* W_in_out, const fl
 
 void oracle_gelu(int n, const float* x, float* y) {
   for (int i = 0; i < n; ++i) y[i] = gelu(x[i]);
+}
+
+// The specified exponential and tanh over n inputs (kind 0 = exp, 1 = tanh).
+void oracle_special(int kind, long long n, const float* x, float* y) {
+#pragma omp parallel for schedule(static)
+  for (long long i = 0; i < n; ++i) y[i] = kind == 0 ? exp_spec(x[i]) : tanh_spec(x[i]);
+}
+
+// Same over raw bit patterns [first, first + n): y[i] = f(bits_as_float(first + i)).
+void oracle_special_bits(int kind, uint32_t first, long long n, float* y) {
+#pragma omp parallel for schedule(static)
+  for (long long i = 0; i < n; ++i) {
+    const uint32_t b = first + (uint32_t)i;
+    float x;
+    std::memcpy(&x, &b, 4);
+    y[i] = kind == 0 ? exp_spec(x) : tanh_spec(x);
+  }
 }
 
 // q [dh]; K, V as [npos][stride] rows; a [dh]; w_out [npos] softmax weights.

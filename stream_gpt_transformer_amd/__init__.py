@@ -46,6 +46,7 @@ SIGNATURES = {
     "gpt2_infer": (_i, [_vp, _vp, _i, _vp, _vp, _vp]),
     "gpt2_test_quantize": (_i, [_vp, _i, _vp, _vp, _vp]),
     "gpt2_test_gemm": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
+    "gpt2_test_special": (_i, [_i, _u32, _sz, _vp, _vp]),
     "gpt2_q8_capture_nbytes": (_sz, []),
     "gpt2_q8_capture_offsets": (_i, [_i, _i] + [ctypes.POINTER(_sz)] * 6),
     "gpt2_q8_cached_step_capture": (_i, [_vp, _vp, _sz, _u32, ctypes.c_int32, _vp, _vp, _vp, _vp]),
@@ -139,6 +140,10 @@ def gpt2_infer(model, tokens: Sequence[int], ws_dev, logits_dev, stream=0) -> in
 
 def gpt2_test_quantize(x_dev, n, codes_dev, scales_dev, stream=0) -> int:
     return lib().gpt2_test_quantize(x_dev, n, codes_dev, scales_dev, stream)
+
+
+def gpt2_test_special(kind, first_bits, n, y_dev, stream=0) -> int:
+    return lib().gpt2_test_special(kind, first_bits, n, y_dev, stream)
 
 
 def gpt2_test_gemm(A_dev, W_dev, C_dev, M, N, K, stream=0) -> int:

@@ -162,6 +162,11 @@ int gpt2_test_quantize(const float* x, int n, int8_t* codes, float* scales, void
   return launch_quantize(x, n, codes, scales, (hipStream_t)stream) == hipSuccess ? GPT2_OK : GPT2_EHIP;
 }
 
+int gpt2_test_special(int kind, uint32_t first_bits, size_t n, float* y, void* stream) {
+  if ((kind != 0 && kind != 1) || n > ((size_t)1 << 32) - first_bits || (n && !y)) return GPT2_EARG;
+  return launch_special_bits(kind, first_bits, (long long)n, y, (hipStream_t)stream) == hipSuccess ? GPT2_OK : GPT2_EHIP;
+}
+
 int gpt2_test_gemm(const float* A, const float* W, float* C, int M, int N, int K, void* stream) {
   if (!A || !W || !C || M < 1 || M > PMAX || N < 64 || N % 64 || K < 32 || K % 32) return GPT2_EARG;
   return launch_gemm_test(A, W, C, M, N, K, (hipStream_t)stream) == hipSuccess ? GPT2_OK : GPT2_EHIP;

@@ -46,23 +46,29 @@ __device__ __forceinline__ constexpr bool mode_ln() {
   return MODE == MODE_QKV || MODE == MODE_FC || MODE == MODE_HEAD;
 }
 
-// Projection input of session b: LN1(x), attention output, LN2(x), GELU output,
-// LN_f(x) for QKV, O, FC, PR, HEAD.
+// Raw input vector of session b: the residual x (QKV, FC, HEAD take its
+// LayerNorm), the attention output (O) or the GELU output (PR).
+template <int MODE>
+__device__ __forceinline__ const float* proj_src(const ProjArgs& a, int b) {
+  return MODE == MODE_O ? a.k.att + (size_t)b * D : MODE == MODE_PR ? a.k.g + (size_t)b * F : a.k.x + (size_t)b * D;
+}
+template <int MODE>
+__device__ __forceinline__ const float* ln_gamma(const ProjArgs& a) {
+  return MODE == MODE_QKV ? small_p(a.w, a.layer, sp::LN1_G)
+         : MODE == MODE_FC ? small_p(a.w, a.layer, sp::LN2_G) : a.w.small + sp::LNF_G;
+}
+template <int MODE>
+__device__ __forceinline__ const float* ln_beta(const ProjArgs& a) {
+  return MODE == MODE_QKV ? small_p(a.w, a.layer, sp::LN1_B)
+         : MODE == MODE_FC ? small_p(a.w, a.layer, sp::LN2_B) : a.w.small + sp::LNF_B;
+}
+
+// fp32-path projection input of session b as a lane fragment: LN1(x), attention
+// output, LN2(x), GELU output, LN_f(x) for QKV, O, FC, PR, HEAD.
 template <int MODE, int NI>
 __device__ __forceinline__ void proj_input(const ProjArgs& a, int b, f4 (&x)[NI]) {
-  const float* src = MODE == MODE_O ? a.k.att + (size_t)b * D
-                     : MODE == MODE_PR ? a.k.g + (size_t)b * F
-                                       : a.k.x + (size_t)b * D;
-  load_frag<NI>(x, src);
-  if constexpr (mode_ln<MODE>()) {
-    const float* gam = MODE == MODE_QKV ? small_p(a.w, a.layer, sp::LN1_G)
-                       : MODE == MODE_FC ? small_p(a.w, a.layer, sp::LN2_G)
-                                         : a.w.small + sp::LNF_G;
-    const float* bet = MODE == MODE_QKV ? small_p(a.w, a.layer, sp::LN1_B)
-                       : MODE == MODE_FC ? small_p(a.w, a.layer, sp::LN2_B)
-                                         : a.w.small + sp::LNF_B;
-    layernorm_frag(*reinterpret_cast<f4(*)[3]>(&x), gam, bet);
-  }
+  load_frag<NI>(x, proj_src<MODE>(a, b));
+  if constexpr (mode_ln<MODE>()) layernorm_frag(*reinterpret_cast<f4(*)[3]>(&x), ln_gamma<MODE>(a), ln_beta<MODE>(a));
 }
 
 // Epilogue of output r of session b; y is the projection value including bias.
@@ -157,6 +163,8 @@ __global__ __launch_bounds__(128) void k_attn(const ProjArgs a) {
 }
 
 // ---- int8 group-64 projections (batch 1) -------------------------------------
+// LayerNorm inputs use the sequential-sum LayerNorm, so every fp32 value of the
+// int8 path follows the specification's operation order exactly.
 // The block quantizes its fp32 input in LDS (every block does the same work and
 // gets the same codes), then each wave streams its rows' int8 codes: lane l takes
 // 16 codes at byte 1024*i + 16*l, so group 16*i + l/4; v_dot4 gives a lane partial
@@ -179,10 +187,14 @@ __global__ __launch_bounds__(256) void k_q8proj(const ProjArgs a) {
 
   if (wave == 0) {
     f4 x[NI];
-    proj_input<MODE, NI>(a, 0, x);
+    load_frag<NI>(x, proj_src<MODE>(a, 0));
     store_frag<NI>(xf, x);
   }
   __syncthreads();
+  if constexpr (mode_ln<MODE>()) {
+    if (wave == 0) layernorm_seq(xf, ln_gamma<MODE>(a), ln_beta<MODE>(a), xf);
+    __syncthreads();
+  }
   for (int g = wave; g < G; g += 4) {
     float s;
     const int c = quant_lane(xf[g * 64 + lane], s);
@@ -252,6 +264,15 @@ __global__ __launch_bounds__(64) void k_quantize(const float* x, int8_t* codes, 
   const int c = quant_lane(x[(size_t)g * 64 + lane], s);
   codes[(size_t)g * 64 + lane] = (int8_t)c;
   if (lane == 0) scales[g] = s;
+}
+
+// The specified exponential (kind 0) or tanh (kind 1) of the binary32 value whose
+// bit pattern is first + i (test hook).
+__global__ __launch_bounds__(256) void k_special_bits(int kind, uint32_t first, long long n, float* y) {
+  const long long i = blockIdx.x * 256ll + threadIdx.x;
+  if (i >= n) return;
+  const float x = __uint_as_float(first + (uint32_t)i);
+  y[i] = kind == 0 ? exp_spec(x) : tanh_spec(x);
 }
 
 // ---- launchers ---------------------------------------------------------------
@@ -333,6 +354,11 @@ hipError_t launch_head_f32(const Weights& w, const float* x_row, float* logits, 
   a.ss.B = 1;
   a.logits = logits;
   launch_proj<MODE_HEAD, 2, 1>(a, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_special_bits(int kind, uint32_t first, long long n, float* y, hipStream_t s) {
+  if (n > 0) hipLaunchKernelGGL(k_special_bits, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, kind, first, n, y);
   return hipGetLastError();
 }
 

@@ -94,28 +94,92 @@ __device__ __forceinline__ float dot_frag(const f4 (&w)[NI], const f4 (&x)[NI]) 
   return wave_sum(acc);
 }
 
+// Ordered binary32 exponential (LeanExe GPT-2 README, numerical functions: an
+// ordered binary32 exponential approximation; muInference page, IEEE-ops table:
+// range reduction, Taylor polynomial, 2^k as a bit pattern, only correctly rounded
+// operations).  Each line is one rounded binary32 operation, in this order:
+// k = rint(x*log2 e); r = (x - k*ln2_hi) - k*ln2_lo with ln2_hi = 0x3f317200 (k*ln2_hi
+// exact); degree-7 Taylor polynomial of e^r by Horner from 1/5040 down to 1; times
+// 2^k from its bit pattern.  NaN passes through, x >= 88.72283935546875 gives +inf,
+// x < -87 gives 0 (so no result is subnormal).
+__device__ __forceinline__ float exp_spec(float x) {
+  if (x != x) return x;
+  if (x >= 88.72283935546875f) return INFINITY;
+  if (x < -87.0f) return 0.0f;
+  const float k = rintf(x * 1.44269502162933349609375f);
+  const float r = (x - k * 0.693145751953125f) - k * 1.428606765330187e-06f;
+  float p = 1.0f / 5040.0f;
+  p = p * r + 1.0f / 720.0f;
+  p = p * r + 1.0f / 120.0f;
+  p = p * r + 1.0f / 24.0f;
+  p = p * r + 1.0f / 6.0f;
+  p = p * r + 0.5f;
+  p = p * r + 1.0f;
+  p = p * r + 1.0f;
+  int ki = (int)k;
+  if (ki == 128) {
+    p = p * 2.0f;
+    ki = 127;
+  }
+  return p * __uint_as_float((unsigned)(ki + 127) << 23);
+}
+
+// tanh(z) = 1 - 2/(exp(2|z|) + 1), with the sign of z.
+__device__ __forceinline__ float tanh_spec(float z) {
+  const float e = exp_spec(2.0f * fabsf(z));
+  const float t = 1.0f - 2.0f / (e + 1.0f);
+  return z < 0.0f ? -t : t;
+}
+
 // tanh form of GELU: 0.5*u*(1 + tanh(sqrt(2/pi)*(u + 0.044715*u^3))).
 __device__ __forceinline__ float gelu_tanh(float u) {
   const float c = 0.7978845608028654f;  // sqrt(2/pi) rounded to binary32
   const float inner = u + 0.044715f * (u * u * u);
-  const float t = tanhf(c * inner);
+  const float t = tanh_spec(c * inner);
   return (0.5f * u) * (1.0f + t);
 }
 
+// LayerNorm of a 768-vector in LDS with every sum taken sequentially in index order
+// (mean, then the variance of the centred values), one rounding per operation:
+// the order the int8 path needs so that its activation codes are a function of the
+// specification alone.  Lane 0 runs the two sums; all 64 lanes write y to LDS.
+__device__ __forceinline__ void layernorm_seq(const float* xs, const float* __restrict__ gamma,
+                                              const float* __restrict__ beta, float* ys) {
+  const int lane = lane_id();
+  float mean = 0.0f, r = 0.0f;
+  if (lane == 0) {
+    float s = 0.0f;
+    for (int i = 0; i < 768; i += 4) {
+      const f4 v = *(const f4*)(xs + i);
+      s = s + v.x; s = s + v.y; s = s + v.z; s = s + v.w;
+    }
+    mean = s / 768.0f;
+    float q = 0.0f;
+    for (int i = 0; i < 768; i += 4) {
+      const f4 v = *(const f4*)(xs + i) - mean;
+      q = q + v.x * v.x; q = q + v.y * v.y; q = q + v.z * v.z; q = q + v.w * v.w;
+    }
+    const float var = q / 768.0f;
+    r = 1.0f / sqrtf(var + 1e-5f);
+  }
+  mean = __shfl(mean, 0);
+  r = __shfl(r, 0);
+  for (int i = lane; i < 768; i += 64) ys[i] = ((xs[i] - mean) * r) * gamma[i] + beta[i];
+}
+
 // ---- attention (one session, one head) --------------------------------------
-// 128 threads (two wavefronts); thread t owns key t.  With npos keys (1..128):
-//   s_t = fmaf-chain over d of q_d*K_t,d, times 0.125 (1/sqrt(64));
-//   m = max_t s_t;  e_t = exp(s_t - m) (0 for t >= npos);
-//   Z = wave-butterfly sum of each wave's e, then Z = Z_wave0 + Z_wave1;
-//   w_t = e_t / Z;
-//   a_d = (fmaf-chain over t < 64 of w_t*V_t,d) + (fmaf-chain over 64 <= t < npos).
+// 128 threads (two wavefronts); thread t owns key t, and with npos keys (1..128)
+// every value is the oracle's sequential definition, one rounding per operation:
+//   s_t = (sum over d ascending of q_d*K_t,d) * 0.125   (1/sqrt(64));
+//   m = max_t s_t;  e_t = exp_spec(s_t - m);
+//   Z = sum over t ascending of e_t;  w_t = e_t / Z;
+//   a_d = sum over t ascending of w_t*V_t,d.
 struct AttnSmem {
-  float k[PMAX][DH + 1];  // padded row: lanes reading K_t,d for consecutive t avoid bank clashes
+  float k[PMAX][DH + 4];  // padded rows, 16-byte aligned
   float v[PMAX][DH];
   float q[DH];
   float w[PMAX];
   float red[4];
-  float part[DH];
 };
 
 // Stage npos key/value rows of one head into LDS.  Row t of the keys is at
@@ -126,10 +190,8 @@ __device__ __forceinline__ void attn_stage(AttnSmem& sm, RowPtr kv, int npos, co
   for (int idx = t; idx < npos * 16; idx += 128) {
     const int j = idx >> 4, c = (idx & 15) * 4;
     const float* row = kv(j);
-    const f4 kk = *(const f4*)(row + c);
-    const f4 vv = *(const f4*)(row + D + c);
-    sm.k[j][c + 0] = kk.x; sm.k[j][c + 1] = kk.y; sm.k[j][c + 2] = kk.z; sm.k[j][c + 3] = kk.w;
-    *(f4*)&sm.v[j][c] = vv;
+    *(f4*)&sm.k[j][c] = *(const f4*)(row + c);
+    *(f4*)&sm.v[j][c] = *(const f4*)(row + D + c);
   }
   if (t < DH) sm.q[t] = q[t];
 }
@@ -139,28 +201,39 @@ __device__ __forceinline__ float attn_compute(AttnSmem& sm, int npos) {
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
   float s = -INFINITY;
   if (t < npos) {
+    f4 kr[DH / 4];
+#pragma unroll
+    for (int i = 0; i < DH / 4; ++i) kr[i] = *(const f4*)&sm.k[t][4 * i];
     float acc = 0.0f;
-#pragma unroll 16
-    for (int d = 0; d < DH; ++d) acc = fmaf(sm.q[d], sm.k[t][d], acc);
+#pragma unroll
+    for (int i = 0; i < DH / 4; ++i) {
+      const f4 qq = *(const f4*)&sm.q[4 * i];
+      acc = acc + qq.x * kr[i].x;
+      acc = acc + qq.y * kr[i].y;
+      acc = acc + qq.z * kr[i].z;
+      acc = acc + qq.w * kr[i].w;
+    }
     s = acc * 0.125f;
   }
   const float mw = wave_max(s);
   if (lane == 0) sm.red[wv] = mw;
   __syncthreads();
   const float m = fmaxf(sm.red[0], sm.red[1]);
-  const float e = t < npos ? expf(s - m) : 0.0f;
-  const float zw = wave_sum(e);
-  if (lane == 0) sm.red[2 + wv] = zw;
+  const float e = t < npos ? exp_spec(s - m) : 0.0f;
+  sm.w[t] = e;
   __syncthreads();
-  const float Z = sm.red[2] + sm.red[3];
-  sm.w[t] = e / Z;
+  if (t == 0) {
+    float Z = 0.0f;
+    for (int j = 0; j < npos; ++j) Z = Z + sm.w[j];
+    sm.red[2] = Z;
+  }
+  __syncthreads();
+  if (t < npos) sm.w[t] = e / sm.red[2];
   __syncthreads();
   float acc = 0.0f;
-  const int j1 = min(npos, 64 * wv + 64);
-  for (int j = 64 * wv; j < j1; ++j) acc = fmaf(sm.w[j], sm.v[j][lane], acc);
-  if (wv == 1) sm.part[lane] = acc;
-  __syncthreads();
-  return wv == 0 ? acc + sm.part[lane] : 0.0f;
+  if (wv == 0)
+    for (int j = 0; j < npos; ++j) acc = acc + sm.w[j] * sm.v[j][lane];
+  return acc;
 }
 
 // ---- int8 group-64 quantizer (marXiv 2609.00018 abstract) --------------------

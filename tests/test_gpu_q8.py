@@ -6,9 +6,11 @@
   accumulators and output.  The oracle quantizes the captured input and
   accumulates it with its own weight codes: codes, scales, accumulators and
   outputs must be bit-identical (the abstract's captured-operand identity).
-- Logits within 5e-3 of the oracle's int8 session, caches within 1e-3.
-- The number of end-to-end activation codes that differ between the two full
-  sessions (upstream fp32 differences crossing a rounding boundary) is reported.
+- Every fp32 operation of the int8 path (embedding, sequential-sum LayerNorm,
+  attention, the specified exponential and tanh, residual adds, the fixed-order
+  rescale) follows the oracle's operation order, so the 6,432,896 logits and the
+  cache of the session are bit-identical to the oracle's (which implies the
+  required max |diff| <= 5e-3).
 """
 import numpy as np
 import pytest
@@ -86,9 +88,13 @@ def test_q8_session_capture_bit_exact_and_logits():
     assert n_checked == 128 * 49
     got = lg.cpu().numpy()
     err = check_logits(got, ref, TOL_Q8, "int8 session")
-    assert np.abs(cache.cpu().numpy() - ref_cache).max() <= 1e-3
-    print(f"int8 session: max |logit diff| vs oracle {err:.2e}; vs fp32 oracle "
-          f"{np.abs(got - ref_f32).max():.3f}; 6,432,896 logits compared")
+    # Every fp32 step of the int8 path follows the specification's operation order,
+    # so the whole session is bit-identical to the oracle: 6,432,896 logits and the
+    # 128-position cache.
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    assert np.array_equal(cache.cpu().numpy().view(np.uint32), ref_cache.view(np.uint32))
+    print(f"int8 session: bit-identical to the oracle (max |diff| {err:.1e}); deviation from the "
+          f"fp32 oracle {np.abs(got - ref_f32).max():.3f}")
 
 
 def test_q8_plain_step_equals_capture_step():
