@@ -72,8 +72,10 @@ typedef struct gpt2_model gpt2_model; /* opaque host handle */
 size_t gpt2_packed_nbytes(int flags);
 
 /* Bytes of device workspace one stream needs (activations of up to 64 sessions,
- * the 128-row prefill buffers).  The workspace is scratch: its contents between
- * calls do not matter. */
+ * the 128-row prefill buffers, the exchange buffers of the single-launch decode
+ * step).  The caller zero-fills a workspace once before its first use; after that
+ * the library keeps it consistent (its header holds a per-launch epoch).  Calls on
+ * different streams need different workspaces. */
 size_t gpt2_workspace_nbytes(void);
 
 /* Re-lay the packed checkpoint for the device.
@@ -147,7 +149,17 @@ int gpt2_batched_cached_step(const gpt2_model* model, float* caches_dev, size_t 
 int gpt2_infer(const gpt2_model* model, const uint32_t* tokens_host, int n, void* ws_dev, float* logits_dev,
                void* stream);
 
+/* Error word of a workspace, given a host copy of at least its first 16 bytes:
+ * 0 = fine; nonzero = a wait inside the single-launch decode step gave up (after
+ * about 2^21 polls); that step's outputs are invalid and the word stays set until
+ * the caller zero-fills the workspace again. */
+int gpt2_workspace_status(const void* ws_host_copy);
+
 /* ---- test hooks (not needed by applications) -------------------------------- */
+
+/* on != 0: gpt2_cached_step / gpt2_q8_cached_step use one kernel per block phase
+ * instead of the single-launch step (same results; for testing both paths). */
+void gpt2_test_force_phase_kernels(int on);
 
 /* Group-64 quantizer alone: n (a multiple of 64) values -> codes [n], scales [n/64]. */
 int gpt2_test_quantize(const float* x_dev, int n, int8_t* codes_dev, float* scales_dev, void* stream);

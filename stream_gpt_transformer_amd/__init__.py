@@ -48,6 +48,8 @@ SIGNATURES = {
     "gpt2_test_gemm": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
     "gpt2_test_special": (_i, [_i, _u32, _sz, _vp, _vp]),
     "gpt2_q8_capture_nbytes": (_sz, []),
+    "gpt2_test_force_phase_kernels": (None, [_i]),
+    "gpt2_workspace_status": (_i, [_vp]),
     "gpt2_q8_capture_offsets": (_i, [_i, _i] + [ctypes.POINTER(_sz)] * 6),
     "gpt2_q8_cached_step_capture": (_i, [_vp, _vp, _sz, _u32, ctypes.c_int32, _vp, _vp, _vp, _vp]),
     "gpt2_weight_view": (_i, [_vp, _i, _i, ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp),
@@ -150,6 +152,15 @@ def gpt2_test_gemm(A_dev, W_dev, C_dev, M, N, K, stream=0) -> int:
     return lib().gpt2_test_gemm(A_dev, W_dev, C_dev, M, N, K, stream)
 
 
+def gpt2_test_force_phase_kernels(on: bool) -> None:
+    lib().gpt2_test_force_phase_kernels(1 if on else 0)
+
+
+def gpt2_workspace_status(ws_host_copy: bytes) -> int:
+    buf = ctypes.create_string_buffer(bytes(ws_host_copy[:16]), 16)
+    return lib().gpt2_workspace_status(ctypes.cast(buf, _vp))
+
+
 def gpt2_q8_capture_nbytes() -> int:
     return int(lib().gpt2_q8_capture_nbytes())
 
@@ -204,6 +215,10 @@ class Model:
             self.close()
         except Exception:
             pass
+
+    def status(self) -> int:
+        """Error word of this model's workspace (0 = fine)."""
+        return gpt2_workspace_status(self.ws[:16].cpu().numpy().tobytes())
 
     def new_cache(self, positions: int = GPT2_MAX_POS, batch: int = 0):
         import torch

@@ -35,6 +35,10 @@ Work work_ptrs(void* ws, int max_batch) {
 }
 }  // namespace g2
 
+namespace g2 {
+bool g_force_phase_kernels = false;
+}
+
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 static bool aligned4(const void* p) { return ((uintptr_t)p & 3) == 0; }
 
@@ -90,11 +94,17 @@ int gpt2_cached_step(const gpt2_model* m, float* cache, size_t cache_nwords, uin
                      void* ws, float* logits, void* stream) {
   const int rc = step_checks(m, GPT2_PACK_F32, cache, cache_nwords, token, pos, ws, logits);
   if (rc) return rc;
+  const Work k = work_ptrs(ws, MAX_BATCH);
+  bool used = false;
+  if (!g_force_phase_kernels &&
+      launch_fused(false, m->w, k, token, pos, cache, logits, nullptr, (hipStream_t)stream, &used) != hipSuccess)
+    return GPT2_EHIP;
+  if (used) return GPT2_OK;
   Sessions ss{};
   ss.B = 1;
   ss.tok[0] = token;
   ss.pos[0] = pos;
-  const hipError_t e = launch_step_f32(m->w, work_ptrs(ws, MAX_BATCH), ss, cache, 0, logits, (hipStream_t)stream);
+  const hipError_t e = launch_step_f32(m->w, k, ss, cache, 0, logits, (hipStream_t)stream);
   return e == hipSuccess ? GPT2_OK : GPT2_EHIP;
 }
 
@@ -103,12 +113,17 @@ static int q8_step(const gpt2_model* m, float* cache, size_t cache_nwords, uint3
   const int rc = step_checks(m, GPT2_PACK_Q8, cache, cache_nwords, token, pos, ws, logits);
   if (rc) return rc;
   if (capture && !aligned16(capture)) return GPT2_EARG;
+  const Work k = work_ptrs(ws, MAX_BATCH);
+  bool used = false;
+  if (!g_force_phase_kernels &&
+      launch_fused(true, m->w, k, token, pos, cache, logits, (char*)capture, (hipStream_t)stream, &used) != hipSuccess)
+    return GPT2_EHIP;
+  if (used) return GPT2_OK;
   Sessions ss{};
   ss.B = 1;
   ss.tok[0] = token;
   ss.pos[0] = pos;
-  const hipError_t e =
-      launch_step_q8(m->w, work_ptrs(ws, MAX_BATCH), ss, cache, logits, (char*)capture, (hipStream_t)stream);
+  const hipError_t e = launch_step_q8(m->w, k, ss, cache, logits, (char*)capture, (hipStream_t)stream);
   return e == hipSuccess ? GPT2_OK : GPT2_EHIP;
 }
 
@@ -170,6 +185,12 @@ int gpt2_test_special(int kind, uint32_t first_bits, size_t n, float* y, void* s
 int gpt2_test_gemm(const float* A, const float* W, float* C, int M, int N, int K, void* stream) {
   if (!A || !W || !C || M < 1 || M > PMAX || N < 64 || N % 64 || K < 32 || K % 32) return GPT2_EARG;
   return launch_gemm_test(A, W, C, M, N, K, (hipStream_t)stream) == hipSuccess ? GPT2_OK : GPT2_EHIP;
+}
+
+void gpt2_test_force_phase_kernels(int on) { g_force_phase_kernels = on != 0; }
+
+int gpt2_workspace_status(const void* ws_host_copy) {
+  return ws_host_copy ? (int)((const uint32_t*)ws_host_copy)[2] : 0;
 }
 
 size_t gpt2_q8_capture_nbytes(void) { return cap_total(); }

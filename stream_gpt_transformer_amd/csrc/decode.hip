@@ -217,42 +217,13 @@ __global__ __launch_bounds__(256) void k_q8proj(const ProjArgs a) {
   for (int rr = 0; rr < RPW; ++rr) {
     const int r = row0 + rr;
     if (r >= NROWS) break;
-    const int8_t* wr = codes + (size_t)r * K;
-    int acc[NCH];
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int off = 1024 * i + 16 * lane;
-      int p = 0;
-      if (off < K) {
-        const i4 wv = nt_load((const i4*)(wr + off));
-        const i4 xv = *(const i4*)(xc + off);
-        p = __builtin_amdgcn_sdot4(wv.x, xv.x, p, false);
-        p = __builtin_amdgcn_sdot4(wv.y, xv.y, p, false);
-        p = __builtin_amdgcn_sdot4(wv.z, xv.z, p, false);
-        p = __builtin_amdgcn_sdot4(wv.w, xv.w, p, false);
-      }
-      p += __shfl_xor(p, 1);
-      p += __shfl_xor(p, 2);
-      acc[i] = p;
-    }
-    const float swl = lane < G ? scales[(size_t)r * G + lane] : 0.0f;
-    float y = 0.0f;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int ag = __shfl(acc[g / 16], (g % 16) * 4);
-      const float sg = __shfl(swl, g);
-      y = y + ((float)ag * sg) * xsc[g];
-    }
+    i4 wc[NCH];
+    float swl;
+    q8_load_row<K>(wc, swl, codes, scales, r);
+    int32_t* ca = cap ? (int32_t*)(cap + cl.acc) + (size_t)r * G : nullptr;
+    float y = q8_dot<K>(wc, swl, xc, xsc, ca);
     y = y + proj_bias<MODE>(a, r);
-    if (cap) {
-      int32_t* ca = (int32_t*)(cap + cl.acc) + (size_t)r * G;
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const int g = 16 * i + lane / 4;
-        if ((lane & 3) == 0 && g < G) ca[g] = acc[i];
-      }
-      if (lane == 0) ((float*)(cap + cl.y))[r] = y;
-    }
+    if (cap && lane == 0) ((float*)(cap + cl.y))[r] = y;
     if (lane == 0) proj_store<MODE>(a, 0, r, y);
   }
 }

@@ -131,6 +131,23 @@ __device__ __forceinline__ float tanh_spec(float z) {
   return z < 0.0f ? -t : t;
 }
 
+// dot_frag with the input fragment read from LDS one float4 at a time (same fmaf
+// chain and butterfly, so the same value; fewer live registers).
+template <int NI>
+__device__ __forceinline__ float dot_lds(const f4 (&w)[NI], const float* xs) {
+  const int l = lane_id();
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const f4 x = *(const f4*)(xs + 256 * i + 4 * l);
+    acc = fmaf(w[i].x, x.x, acc);
+    acc = fmaf(w[i].y, x.y, acc);
+    acc = fmaf(w[i].z, x.z, acc);
+    acc = fmaf(w[i].w, x.w, acc);
+  }
+  return wave_sum(acc);
+}
+
 // tanh form of GELU: 0.5*u*(1 + tanh(sqrt(2/pi)*(u + 0.044715*u^3))).
 __device__ __forceinline__ float gelu_tanh(float u) {
   const float c = 0.7978845608028654f;  // sqrt(2/pi) rounded to binary32
@@ -182,25 +199,35 @@ struct AttnSmem {
   float red[4];
 };
 
-// Stage npos key/value rows of one head into LDS.  Row t of the keys is at
-// kv(t) (64 keys), its values at kv(t) + D.  Called by all 128 threads.
+// Stage key/value rows j0..j1-1 of one head into LDS with threads tid0..tid0+nthr-1
+// of the block.  Row j of the keys is at kv(j) (64 keys), its values at kv(j) + D.
 template <class RowPtr>
-__device__ __forceinline__ void attn_stage(AttnSmem& sm, RowPtr kv, int npos, const float* q) {
-  const int t = threadIdx.x;
-  for (int idx = t; idx < npos * 16; idx += 128) {
-    const int j = idx >> 4, c = (idx & 15) * 4;
+__device__ __forceinline__ void attn_stage_rows(AttnSmem& sm, RowPtr kv, int j0, int j1, int tid0, int nthr) {
+  const int t = (int)threadIdx.x - tid0;
+  if (t < 0 || t >= nthr) return;
+  for (int idx = t; idx < (j1 - j0) * 16; idx += nthr) {
+    const int j = j0 + (idx >> 4), c = (idx & 15) * 4;
     const float* row = kv(j);
     *(f4*)&sm.k[j][c] = *(const f4*)(row + c);
     *(f4*)&sm.v[j][c] = *(const f4*)(row + D + c);
   }
-  if (t < DH) sm.q[t] = q[t];
 }
 
-// Returns a_d in threads 0..63 (d = thread index); other threads return 0.
+// Stage all npos rows and the query with the first 128 threads.
+template <class RowPtr>
+__device__ __forceinline__ void attn_stage(AttnSmem& sm, RowPtr kv, int npos, const float* q) {
+  attn_stage_rows(sm, kv, 0, npos, 0, 128);
+  if (threadIdx.x < DH) sm.q[threadIdx.x] = q[threadIdx.x];
+}
+
+// Returns a_d in threads 0..63 (d = thread index); other threads return 0.  Every
+// thread of the block must call it (it synchronises the block); threads 128 and up
+// only take part in the barriers.
 __device__ __forceinline__ float attn_compute(AttnSmem& sm, int npos) {
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
+  const bool act = t < 128;
   float s = -INFINITY;
-  if (t < npos) {
+  if (act && t < npos) {
     f4 kr[DH / 4];
 #pragma unroll
     for (int i = 0; i < DH / 4; ++i) kr[i] = *(const f4*)&sm.k[t][4 * i];
@@ -216,11 +243,11 @@ __device__ __forceinline__ float attn_compute(AttnSmem& sm, int npos) {
     s = acc * 0.125f;
   }
   const float mw = wave_max(s);
-  if (lane == 0) sm.red[wv] = mw;
+  if (act && lane == 0) sm.red[wv] = mw;
   __syncthreads();
   const float m = fmaxf(sm.red[0], sm.red[1]);
-  const float e = t < npos ? exp_spec(s - m) : 0.0f;
-  sm.w[t] = e;
+  const float e = (act && t < npos) ? exp_spec(s - m) : 0.0f;
+  if (act) sm.w[t] = e;
   __syncthreads();
   if (t == 0) {
     float Z = 0.0f;
@@ -228,7 +255,7 @@ __device__ __forceinline__ float attn_compute(AttnSmem& sm, int npos) {
     sm.red[2] = Z;
   }
   __syncthreads();
-  if (t < npos) sm.w[t] = e / sm.red[2];
+  if (act && t < npos) sm.w[t] = e / sm.red[2];
   __syncthreads();
   float acc = 0.0f;
   if (wv == 0)
@@ -249,6 +276,59 @@ __device__ __forceinline__ int quant_lane(float x, float& s_out) {
   if (q != q) q = 0.0f;
   q = fminf(fmaxf(q, -127.0f), 127.0f);
   return (int)q;
+}
+
+// One output of an int8 group-64 projection with K inputs.  Lane l holds the row's
+// codes at bytes 1024*i + 16*l (i < NCH), i.e. group 16*i + l/4; swl is lane g's
+// weight scale for group g (g < K/64).  xc/xsc are the input codes and scales.
+//   acc[g] = sum of the 64 code products of group g (v_dot4, then two exact integer
+//   butterfly steps inside each 4-lane quad), moved to lane g;
+//   t[g] = ((float)acc[g] * sw[g]) * sx[g] in lane g;
+//   y = 0; y = y + t[g] for g = 0..K/64-1  (fixed order, through readlane).
+// cap_acc (may be null) receives acc[0..K/64-1].  Bias excluded.
+template <int K>
+__device__ __forceinline__ float q8_dot(const i4 (&wc)[(K + 1023) / 1024], float swl, const int8_t* xc,
+                                        const float* xsc, int32_t* cap_acc) {
+  constexpr int NCH = (K + 1023) / 1024, G = K / 64;
+  const int lane = lane_id();
+  int accg = 0;  // acc[lane] for lane < G
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int off = 1024 * i + 16 * lane;
+    int p = 0;
+    if (off < K) {
+      const i4 xv = *(const i4*)(xc + off);
+      p = __builtin_amdgcn_sdot4(wc[i].x, xv.x, p, false);
+      p = __builtin_amdgcn_sdot4(wc[i].y, xv.y, p, false);
+      p = __builtin_amdgcn_sdot4(wc[i].z, xv.z, p, false);
+      p = __builtin_amdgcn_sdot4(wc[i].w, xv.w, p, false);
+    }
+    p += __shfl_xor(p, 1);
+    p += __shfl_xor(p, 2);
+    const int gi = __shfl(p, 4 * (lane & 15));  // group 16*i + (lane & 15)
+    if ((lane >> 4) == i) accg = gi;
+  }
+  if (cap_acc && lane < G) cap_acc[lane] = accg;
+  const float t = lane < G ? ((float)accg * swl) * xsc[lane] : 0.0f;
+  float y = 0.0f;
+#pragma unroll
+  for (int g = 0; g < G; ++g) y = y + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), g));
+  return y;
+}
+
+// Load the codes and lane-g scale of int8 row r of a [rows][K] matrix (nontemporal).
+template <int K>
+__device__ __forceinline__ void q8_load_row(i4 (&wc)[(K + 1023) / 1024], float& swl, const int8_t* codes,
+                                            const float* scales, int r) {
+  constexpr int NCH = (K + 1023) / 1024, G = K / 64;
+  const int lane = lane_id();
+  const int8_t* row = codes + (size_t)r * K;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int off = 1024 * i + 16 * lane;
+    wc[i] = off < K ? __builtin_nontemporal_load((const i4*)(row + off)) : i4{0, 0, 0, 0};
+  }
+  swl = lane < G ? scales[(size_t)r * G + lane] : 0.0f;
 }
 
 }  // namespace g2

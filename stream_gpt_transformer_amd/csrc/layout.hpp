@@ -90,12 +90,16 @@ inline PackedLayout packed_layout(int flags) {
 }
 
 // ---- workspace layout, in bytes --------------------------------------------
-// header: [0] launch epoch, [1] finished-block counter, [2] error flag.
+// header (uint32 words): [0] launch epoch of the fused step, [1] finished-workgroup
+// counter, [2] error code (nonzero: a fused-step wait gave up), [8..39] per-XCD relay
+// tickets (uint64).  A fresh workspace must be zero-filled.
 struct WsLayout {
   size_t header, x, qkv, att, g, ll, pf_x, pf_h, pf_qkv, pf_att, pf_u, pf_part, total;
 };
 
-constexpr int LL_PER_LAYER = D3 + D + D + F + D;  // (value, epoch) words per layer of the fused step
+constexpr int LL_PER_LAYER = D3 + D + D + F + D;  // (value, epoch) words per block exchanged by the fused step
+constexpr int L2_PER_LAYER = D + D + F + D;       // of which relayed to every XCD
+constexpr int MAX_XCC = 16;                       // XCD ids 0..15
 constexpr int PF_SPLIT = 4;                       // split-K factor of the 3072-input prefill GEMM
 
 inline WsLayout ws_layout(int max_batch) {
@@ -107,7 +111,7 @@ inline WsLayout ws_layout(int max_batch) {
   w.qkv = off; off = align256(off + B * D3 * 4);
   w.att = off; off = align256(off + B * D * 4);
   w.g = off; off = align256(off + B * F * 4);
-  w.ll = off; off = align256(off + ((size_t)L * LL_PER_LAYER + D) * 8);
+  w.ll = off; off = align256(off + ((size_t)L * LL_PER_LAYER + (size_t)MAX_XCC * L * L2_PER_LAYER) * 8);
   w.pf_x = off; off = align256(off + (size_t)PMAX * D * 4);
   w.pf_h = off; off = align256(off + (size_t)PMAX * D * 4);
   w.pf_qkv = off; off = align256(off + (size_t)PMAX * D3 * 4);

@@ -62,6 +62,7 @@ def gpu_session(m: g.Model, toks, q8: bool = False):
     for p in range(T):
         m.step(cache, p, int(toks[p]), out[p], q8=q8)
     torch.cuda.synchronize()
+    assert m.status() == 0, f"workspace error {m.status()}"
     return out.cpu().numpy(), cache.cpu().numpy()
 
 

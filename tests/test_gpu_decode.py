@@ -58,6 +58,24 @@ def test_robust_weights_session():
     assert np.abs(cache[:24 * PER] - ref_cache).max() <= 1e-4
 
 
+@pytest.mark.parametrize("q8", [False, True], ids=["fp32", "int8"])
+def test_fused_step_equals_phase_kernels(q8):
+    """The single-launch step and the one-kernel-per-phase path compute the same bits
+    (logits and caches) over a 40-position session; the workspace reports no error."""
+    need_gpu()
+    m = model()
+    toks = synth.make_tokens(21, 40)
+    fused, cf = gpu_session(m, toks, q8=q8)
+    assert m.status() == 0
+    g.gpt2_test_force_phase_kernels(True)
+    try:
+        phase, cp = gpu_session(m, toks, q8=q8)
+    finally:
+        g.gpt2_test_force_phase_kernels(False)
+    assert np.array_equal(fused.view(np.uint32), phase.view(np.uint32))
+    assert np.array_equal(cf.view(np.uint32), cp.view(np.uint32))
+
+
 def test_deterministic_bits():
     need_gpu()
     toks = synth.make_tokens(5, 16)
