@@ -161,6 +161,17 @@ int gpt2_workspace_status(const void* ws_host_copy);
  * instead of the single-launch step (same results; for testing both paths). */
 void gpt2_test_force_phase_kernels(int on);
 
+/* Timeline of the single-launch step: with trace_dev non-null (device buffer of
+ * grid x 64 uint64), later steps write a 100 MHz timestamp per workgroup at each
+ * phase boundary (slot 0 start; 1+4l+{0..3} inputs of the QKV/O/FC/MLP-projection
+ * phases of block l received; 49 head input received; 50 head rows done; 51 end).
+ * NULL turns it off. */
+void gpt2_test_fused_trace(void* trace_dev);
+
+/* on != 0: launch the single-launch step with an ordinary launch instead of a
+ * cooperative one (its waits are bounded either way). */
+void gpt2_test_fused_plain_launch(int on);
+
 /* Group-64 quantizer alone: n (a multiple of 64) values -> codes [n], scales [n/64]. */
 int gpt2_test_quantize(const float* x_dev, int n, int8_t* codes_dev, float* scales_dev, void* stream);
 

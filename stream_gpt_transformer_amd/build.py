@@ -25,7 +25,7 @@ def hipcc() -> str:
 # off for the device code.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}", "-ffp-contract=off",
          "-fno-fast-math", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-Wno-unused-command-line-argument"]
+         "-Wno-unused-command-line-argument", "-Wl,--no-undefined"]
 
 
 def build(verbose: bool = False) -> str:

@@ -166,12 +166,14 @@ __device__ __forceinline__ void layernorm_seq(const float* xs, const float* __re
   float mean = 0.0f, r = 0.0f;
   if (lane == 0) {
     float s = 0.0f;
+#pragma unroll 16
     for (int i = 0; i < 768; i += 4) {
       const f4 v = *(const f4*)(xs + i);
       s = s + v.x; s = s + v.y; s = s + v.z; s = s + v.w;
     }
     mean = s / 768.0f;
     float q = 0.0f;
+#pragma unroll 16
     for (int i = 0; i < 768; i += 4) {
       const f4 v = *(const f4*)(xs + i) - mean;
       q = q + v.x * v.x; q = q + v.y * v.y; q = q + v.z * v.z; q = q + v.w * v.w;
@@ -251,6 +253,7 @@ __device__ __forceinline__ float attn_compute(AttnSmem& sm, int npos) {
   __syncthreads();
   if (t == 0) {
     float Z = 0.0f;
+#pragma unroll 16
     for (int j = 0; j < npos; ++j) Z = Z + sm.w[j];
     sm.red[2] = Z;
   }
@@ -258,8 +261,10 @@ __device__ __forceinline__ float attn_compute(AttnSmem& sm, int npos) {
   if (act && t < npos) sm.w[t] = e / sm.red[2];
   __syncthreads();
   float acc = 0.0f;
-  if (wv == 0)
+  if (wv == 0) {
+#pragma unroll 16
     for (int j = 0; j < npos; ++j) acc = acc + sm.w[j] * sm.v[j][lane];
+  }
   return acc;
 }
 

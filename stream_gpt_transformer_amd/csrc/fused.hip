@@ -17,17 +17,19 @@
 //    1 PR rows per block), and every workgroup takes rows of the tied head at the end;
 //  - wave 0 of each workgroup receives the phase input and hands it to the
 //    compute waves through LDS and s_barrier (no vmcnt drain, so register
-//    prefetches stay in flight);
-//  - wave 1 of the first projection workgroup on each XCD relays: it polls the
-//    global copy of each all-to-all vector and rewrites it into a per-XCD buffer
-//    that the XCD's other workgroups read from their shared L2.
+//    prefetches stay in flight); wave 1 stages the next block's LayerNorm
+//    parameters in LDS.
 //
 // Exchanges carry (value, epoch) 64-bit words: a producer stores value and epoch
 // in one agent-scope store, a consumer polls until every word has this launch's
-// epoch, so no fence or flag is needed.  The epoch advances once per launch
-// (header word 0), written by the last workgroup to finish.  Every wait is
-// bounded: past SPIN_LIMIT polls a workgroup records an error code in header
-// word 2, every other wait then returns at once, and the launch runs to its end.
+// epoch, so no fence or flag is needed.  Vectors every workgroup needs (attention
+// output, x1, GELU output, x2) are written by their producers into one copy per
+// XCD (eight lanes store the eight copies in one instruction), and each
+// workgroup's input wave polls its own XCD's copy: this spreads the polling over
+// eight sets of memory lines.  The epoch advances once per launch (header word 0),
+// written by the last workgroup to finish.  Every wait is bounded: past
+// SPIN_LIMIT polls a workgroup records an error code in header word 2, every
+// other wait then returns at once, and the launch runs to its end.
 //
 // Every output value is computed by the same device functions as the per-phase
 // kernels (layernorm_frag / dot_frag / attn_compute / gelu_tanh for fp32;
@@ -42,7 +44,7 @@ namespace g2 {
 
 typedef unsigned long long u64;
 
-constexpr int FT = 512;           // threads per workgroup (8 waves: 2 input/relay, 6 compute)
+constexpr int FT = 512;           // threads per workgroup (8 waves: input, parameters, 6 compute)
 constexpr int NCW = FT / 64 - 2;  // compute waves per workgroup
 constexpr int MIN_GRID = 204;     // smallest grid for which the row bounds below hold
 // Rows of each projection per compute wave (rows r = c + k * compute_waves).
@@ -54,9 +56,10 @@ constexpr unsigned SPIN_LIMIT = 1u << 21;
 // Global exchange words per block: qkv | att | x1 | g | x2.
 constexpr int LO_QKV = 0, LO_ATT = D3, LO_X1 = D3 + D, LO_G = D3 + 2 * D, LO_X2 = D3 + 2 * D + F;
 static_assert(LO_X2 + D == LL_PER_LAYER, "exchange layout");
-// Per-XCD relayed words per block: att | x1 | g | x2.
+// Per-XCD copies per block: att | x1 | g | x2.
 constexpr int RO_ATT = 0, RO_X1 = D, RO_G = 2 * D, RO_X2 = 2 * D + F;
-static_assert(RO_X2 + D == L2_PER_LAYER, "relay layout");
+static_assert(RO_X2 + D == L2_PER_LAYER, "copy layout");
+constexpr int NXCC = 8;  // XCDs of an MI355X in single-partition mode
 
 enum { HDR_EPOCH = 0, HDR_DONE = 1, HDR_ERROR = 2, HDR_TICKETS = 8 };
 enum { ERR_SPIN = 1, ERR_XCC = 2 };
@@ -65,13 +68,21 @@ struct FusedArgs {
   Weights w;
   float* cache;
   float* logits;
-  u64* ll;           // [L][LL_PER_LAYER]
-  u64* l2;           // [MAX_XCC][L][L2_PER_LAYER]
+  u64* ll;           // [L][LL_PER_LAYER]: qkv words (one copy, read by attention)
+  u64* l2;           // [NXCC][L][L2_PER_LAYER]: per-XCD copies of att, x1, g, x2
   uint32_t* header;
   char* capture;     // int8 test capture or null
+  uint64_t* trace;   // timeline test hook or null: [grid][64] timestamps
   uint32_t token;
   int32_t pos;
 };
+
+// Timeline test hook: slot 0 kernel start; 1+4l+{0..3} inputs of QKV/O/FC/PR of block l
+// received (projection workgroups) or 1+4l+{0,1} qkv received / attention done
+// (attention workgroups); 49 head input received; 50 head rows done; 51 end.
+__device__ __forceinline__ void stamp(const uint64_t* trace, int slot) {
+  if (trace) ((uint64_t*)trace)[blockIdx.x * 64 + slot] = __builtin_amdgcn_s_memrealtime();
+}
 
 __device__ __forceinline__ u64 ld_sc1(const u64* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ __forceinline__ void st_sc1(u64* p, u64 v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
@@ -102,20 +113,6 @@ __device__ __forceinline__ bool give_up(uint32_t& spins, uint32_t* header) {
   return ld32(&header[HDR_ERROR]) != 0;
 }
 
-// First projection workgroup of this launch on XCD x becomes its relay.  The
-// per-XCD ticket word holds (epoch << 32 | count).
-__device__ bool elect_relay(uint32_t* header, uint32_t x, uint32_t E) {
-  u64* t = (u64*)(header + HDR_TICKETS) + x;
-  u64 old = ld_sc1(t);
-  while (true) {
-    const bool first = epoch_of(old) != E;
-    const u64 nw = first ? (((u64)E << 32) | 1ull) : old + 1;
-    const u64 seen = atomicCAS(t, old, nw);
-    if (seen == old) return first;
-    old = seen;
-  }
-}
-
 // One wave polls PL*64 global words at src[lane + 64j] until all carry epoch E.
 template <int PL>
 __device__ __forceinline__ bool poll_global(const u64* src, uint32_t E, u64 (&w)[PL], uint32_t* header) {
@@ -132,40 +129,26 @@ __device__ __forceinline__ bool poll_global(const u64* src, uint32_t E, u64 (&w)
   }
 }
 
-// Relay: global vector -> this XCD's copy (plain stores land in the XCD's L2).
-template <int PL>
-__device__ __forceinline__ void relay(const u64* src, u64* dst, uint32_t E, uint32_t* header) {
-  u64 w[PL];
-  if (poll_global<PL>(src, E, w, header)) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int j = 0; j < PL; ++j) dst[lane + 64 * j] = w[j];
-  }
-}
-
-// Input wave: poll this XCD's copy (nontemporal loads read the XCD's L2 and skip
-// the CU's L1) and write the values to LDS (and optionally a second LDS copy).
+// Input wave: poll this XCD's copy of a PL*64-word vector until every word has
+// epoch E, then write the values to LDS (and optionally a second LDS copy).
 template <int PL>
 __device__ __forceinline__ void receive(const u64* src, uint32_t E, float* out, float* out2, uint32_t* header) {
   const int lane = lane_id();
   u64 w[PL];
-  uint32_t spins = 0;
-  while (true) {
-    asm volatile("" ::: "memory");  // reload every round
-#pragma unroll
-    for (int j = 0; j < PL; ++j) w[j] = __builtin_nontemporal_load(src + lane + 64 * j);
-    bool ok = true;
-#pragma unroll
-    for (int j = 0; j < PL; ++j) ok &= epoch_of(w[j]) == E;
-    if (__all(ok)) break;
-    if (give_up(spins, header)) break;
-  }
+  poll_global<PL>(src, E, w, header);
 #pragma unroll
   for (int j = 0; j < PL; ++j) {
     const float v = __uint_as_float((uint32_t)w[j]);
     out[lane + 64 * j] = v;
     if (out2) out2[lane + 64 * j] = v;
   }
+}
+
+// Producer side of a per-XCD vector: lanes 0..NXCC-1 of the producing wave store
+// word idx of block l's slice `off` into every XCD's copy.
+__device__ __forceinline__ void publish(u64* l2, int l, int off, int idx, float v, uint32_t E) {
+  const int lane = lane_id();
+  if (lane < NXCC) st_sc1(l2 + ((size_t)lane * L + l) * L2_PER_LAYER + off + idx, pack(v, E));
 }
 
 // ---- per-wave weight registers ----------------------------------------------
@@ -261,9 +244,10 @@ struct FusedSmem {
   float xg[F];      // input of PR (GELU output)
   float xres[D];    // residual of the current sub-block
   float xn[D];      // int8 path: LayerNorm output
+  float lnp[2][4][D];  // LayerNorm parameters by block parity: ln1 gamma, beta, ln2 gamma, beta
+  float lnf[2][D];     // final LayerNorm gamma, beta
   int8_t xc[F];     // int8 path: input codes
   float xsc[64];    // int8 path: input scales
-  uint32_t misc[16];
   AttnSmem att;     // attention workgroups
 };
 
@@ -271,25 +255,40 @@ struct FusedSmem {
 struct Ctx {
   uint32_t E;          // this launch's epoch
   int xcc;             // XCD of this workgroup
-  bool leader;         // this workgroup relays for its XCD
-  u64* l2x;            // this XCD's relayed copies
+  u64* cp;             // this XCD's copies
   int G;               // workgroups in the grid
 };
 
-__device__ __forceinline__ const u64* relayed(const Ctx& c, int l, int off) {
-  return c.l2x + (size_t)l * L2_PER_LAYER + off;
+__device__ __forceinline__ const u64* copy_of(const Ctx& c, int l, int off) {
+  return c.cp + (size_t)l * L2_PER_LAYER + off;
 }
 
-// ---- projection workgroups: waves 0 and 1 (input and relay) -------------------
-// Per phase: wave 0 puts the phase input in LDS (and, on the int8 path, the
-// sequential LayerNorm of it), wave 1 of the XCD's relay workgroup copies the
-// input vector from global memory into the XCD's buffer; then barrier B1.  On the
-// int8 path the compute waves quantize between B1 and B2; these waves write the
-// capture of the input side (test hook) after B2.
+// Wave 1: copy a 768-vector from global memory into LDS.
+__device__ __forceinline__ void stage_vec(float* dst, const float* src) {
+  const int lane = lane_id();
+  f4 v[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) v[i] = *(const f4*)(src + 256 * i + 4 * lane);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) *(f4*)(dst + 256 * i + 4 * lane) = v[i];
+}
+__device__ __forceinline__ void stage_ln(FusedSmem& S, const Weights& w, int l) {
+  float (*p)[D] = S.lnp[l & 1];
+  stage_vec(p[0], small_p(w, l, sp::LN1_G));
+  stage_vec(p[1], small_p(w, l, sp::LN1_B));
+  stage_vec(p[2], small_p(w, l, sp::LN2_G));
+  stage_vec(p[3], small_p(w, l, sp::LN2_B));
+}
+
+// ---- projection workgroups: waves 0 and 1 --------------------------------------
+// Per phase: wave 0 polls its XCD's copy of the phase input and puts it in LDS (on
+// the int8 path also the sequential LayerNorm of it); then barrier B1.  Wave 1
+// stages block l+1's LayerNorm parameters during block l.  On the int8 path the
+// compute waves quantize between B1 and B2; waves 0-1 write the capture of the
+// input side (test hook) after B2.
 template <bool Q8>
 __device__ void io_waves(const FusedArgs a, FusedSmem& S, const Ctx c) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const bool relay_wave = c.leader && wave == 1;
   uint32_t* hdr = a.header;
   char* cap = (Q8 && a.capture && (int)blockIdx.x == NATT) ? a.capture : nullptr;
   auto after_b1 = [&](int l, int m, const float* x) {
@@ -307,9 +306,15 @@ __device__ void io_waves(const FusedArgs a, FusedSmem& S, const Ctx c) {
       }
     }
   };
+  if (wave == 1) {
+    stage_ln(S, a.w, 0);
+    stage_vec(S.lnf[0], a.w.small + sp::LNF_G);
+    stage_vec(S.lnf[1], a.w.small + sp::LNF_B);
+  }
+  wg_barrier();  // B0: block 0's LayerNorm parameters are in LDS
   for (int l = 0; l < L; ++l) {
-    const u64* gl = a.ll + (size_t)l * LL_PER_LAYER;
-    // QKV input
+    const float(*lp)[D] = S.lnp[l & 1];
+    // QKV input: the embedding at block 0, else the previous block's x2
     if (wave == 0) {
       if (l == 0) {
 #pragma unroll
@@ -320,45 +325,42 @@ __device__ void io_waves(const FusedArgs a, FusedSmem& S, const Ctx c) {
           S.xres[i] = v;
         }
       } else {
-        receive<12>(relayed(c, l - 1, RO_X2), c.E, S.xs, S.xres, hdr);
+        receive<12>(copy_of(c, l - 1, RO_X2), c.E, S.xs, S.xres, hdr);
       }
-      if constexpr (Q8) layernorm_seq(S.xs, small_p(a.w, l, sp::LN1_G), small_p(a.w, l, sp::LN1_B), S.xn);
-    } else if (relay_wave && l > 0) {
-      relay<12>(a.ll + (size_t)(l - 1) * LL_PER_LAYER + LO_X2, (u64*)relayed(c, l - 1, RO_X2), c.E, hdr);
+      if (lane == 0) stamp(a.trace, 1 + 4 * l);
+      if constexpr (Q8) layernorm_seq(S.xs, lp[0], lp[1], S.xn);
     }
-    wg_barrier();
+    wg_barrier();  // B1
     after_b1(l, M_QKV, S.xn);
+    if (wave == 1 && l + 1 < L) stage_ln(S, a.w, l + 1);
     // O input: attention output
-    if (wave == 0) receive<12>(relayed(c, l, RO_ATT), c.E, S.xs, nullptr, hdr);
-    else if (relay_wave) relay<12>(gl + LO_ATT, (u64*)relayed(c, l, RO_ATT), c.E, hdr);
+    if (wave == 0) {
+      receive<12>(copy_of(c, l, RO_ATT), c.E, S.xs, nullptr, hdr);
+      if (lane == 0) stamp(a.trace, 2 + 4 * l);
+    }
     wg_barrier();
     after_b1(l, M_O, S.xs);
     // FC input: x1
     if (wave == 0) {
-      receive<12>(relayed(c, l, RO_X1), c.E, S.xs, S.xres, hdr);
-      if constexpr (Q8) layernorm_seq(S.xs, small_p(a.w, l, sp::LN2_G), small_p(a.w, l, sp::LN2_B), S.xn);
-    } else if (relay_wave) {
-      relay<12>(gl + LO_X1, (u64*)relayed(c, l, RO_X1), c.E, hdr);
+      receive<12>(copy_of(c, l, RO_X1), c.E, S.xs, S.xres, hdr);
+      if (lane == 0) stamp(a.trace, 3 + 4 * l);
+      if constexpr (Q8) layernorm_seq(S.xs, lp[2], lp[3], S.xn);
     }
     wg_barrier();
     after_b1(l, M_FC, S.xn);
-    // PR input: GELU output, 3072 words in four 768-word pieces
+    // PR input: GELU output
     if (wave == 0) {
-#pragma unroll 1
-      for (int q = 0; q < 4; ++q) receive<12>(relayed(c, l, RO_G) + q * D, c.E, S.xg + q * D, nullptr, hdr);
-    } else if (relay_wave) {
-#pragma unroll 1
-      for (int q = 0; q < 4; ++q) relay<12>(gl + LO_G + q * D, (u64*)relayed(c, l, RO_G) + q * D, c.E, hdr);
+      receive<48>(copy_of(c, l, RO_G), c.E, S.xg, nullptr, hdr);
+      if (lane == 0) stamp(a.trace, 4 + 4 * l);
     }
     wg_barrier();
     after_b1(l, M_PR, S.xg);
   }
   // head input
   if (wave == 0) {
-    receive<12>(relayed(c, L - 1, RO_X2), c.E, S.xs, nullptr, hdr);
-    if constexpr (Q8) layernorm_seq(S.xs, a.w.small + sp::LNF_G, a.w.small + sp::LNF_B, S.xn);
-  } else if (relay_wave) {
-    relay<12>(a.ll + (size_t)(L - 1) * LL_PER_LAYER + LO_X2, (u64*)relayed(c, L - 1, RO_X2), c.E, hdr);
+    receive<12>(copy_of(c, L - 1, RO_X2), c.E, S.xs, nullptr, hdr);
+    if (lane == 0) stamp(a.trace, 49);
+    if constexpr (Q8) layernorm_seq(S.xs, S.lnf[0], S.lnf[1], S.xn);
   }
   wg_barrier();
   after_b1(0, M_HEAD, S.xn);
@@ -373,7 +375,7 @@ __device__ __forceinline__ void head_rows(const FusedArgs a, FusedSmem& S, WRegs
   f4 x[3];
   if constexpr (!Q8) {
     load_frag<3>(x, S.xs);
-    layernorm_frag(x, a.w.small + sp::LNF_G, a.w.small + sp::LNF_B);
+    layernorm_frag(x, S.lnf[0], S.lnf[1]);
   }
   constexpr int NS = head_slots<Q8>();
   const int nrows = (V - hw + hstride - 1) / hstride;
@@ -425,8 +427,8 @@ __device__ void compute_waves(const FusedArgs a, FusedSmem& S, const Ctx c) {
       } else {
         f4 x[3];
         load_frag<3>(x, S.xs);
-        if constexpr (m == M_QKV) layernorm_frag(x, small_p(a.w, l, sp::LN1_G), small_p(a.w, l, sp::LN1_B));
-        if constexpr (m == M_FC) layernorm_frag(x, small_p(a.w, l, sp::LN2_G), small_p(a.w, l, sp::LN2_B));
+        if constexpr (m == M_QKV) layernorm_frag(x, S.lnp[l & 1][0], S.lnp[l & 1][1]);
+        if constexpr (m == M_FC) layernorm_frag(x, S.lnp[l & 1][2], S.lnp[l & 1][3]);
         y = dot_frag<3>(*reinterpret_cast<f4(*)[3]>(&R.r[s0]), x);
       }
     } else {
@@ -455,6 +457,7 @@ __device__ void compute_waves(const FusedArgs a, FusedSmem& S, const Ctx c) {
   load_row<Q8, M_FC, 1>(R, a.w, 0, cw, C);
   load_row<Q8, M_FC, 2>(R, a.w, 0, cw, C);
   load_row<Q8, M_PR, 0>(R, a.w, 0, cw, C);
+  wg_barrier();  // B0
 
   for (int l = 0; l < L; ++l) {
     u64* gl = a.ll + (size_t)l * LL_PER_LAYER;
@@ -482,8 +485,7 @@ __device__ void compute_waves(const FusedArgs a, FusedSmem& S, const Ctx c) {
       const int r = cw;
       if (r < D) {
         const float y = project(R, l, Om{}, K0{}, r);
-        const float x1 = S.xres[r] + y;
-        if (lane == 0) st_sc1(gl + LO_X1 + r, pack(x1, E));
+        publish(a.l2, l, RO_X1, r, S.xres[r] + y, E);
       }
       if (!last) load_row<Q8, M_O, 0>(R, a.w, l + 1, cw, C);
     }
@@ -494,7 +496,7 @@ __device__ void compute_waves(const FusedArgs a, FusedSmem& S, const Ctx c) {
       const int r = cw + decltype(kc)::value * C;
       if (r < F) {
         const float y = project(R, l, FCm{}, kc, r);
-        if (lane == 0) st_sc1(gl + LO_G + r, pack(gelu_tanh(y), E));
+        publish(a.l2, l, RO_G, r, gelu_tanh(y), E);
       }
       if (!last) load_row<Q8, M_FC, decltype(kc)::value>(R, a.w, l + 1, cw, C);
     };
@@ -508,8 +510,7 @@ __device__ void compute_waves(const FusedArgs a, FusedSmem& S, const Ctx c) {
       const int r = cw;
       if (r < D) {
         const float y = project(R, l, PRm{}, K0{}, r);
-        const float x2 = S.xres[r] + y;
-        if (lane == 0) st_sc1(gl + LO_X2 + r, pack(x2, E));
+        publish(a.l2, l, RO_X2, r, S.xres[r] + y, E);
       }
       if (!last) load_row<Q8, M_PR, 0>(R, a.w, l + 1, cw, C);
     }
@@ -520,6 +521,7 @@ __device__ void compute_waves(const FusedArgs a, FusedSmem& S, const Ctx c) {
   wg_barrier();
   quantize(S.xn, D);
   head_rows<Q8>(a, S, R, hw, hstride);
+  if (wave == 2 && lane == 0) stamp(a.trace, 50);
 }
 
 // ---- attention workgroups (head h = blockIdx.x) --------------------------------
@@ -529,6 +531,10 @@ __device__ void attention_wg(const FusedArgs a, FusedSmem& S, const Ctx c) {
   const int h = blockIdx.x, pos = a.pos;
   uint32_t* hdr = a.header;
   AttnSmem& sm = S.att;
+  if (wave == 1) {
+    stage_vec(S.lnf[0], a.w.small + sp::LNF_G);
+    stage_vec(S.lnf[1], a.w.small + sp::LNF_B);
+  }
   for (int l = 0; l < L; ++l) {
     const u64* gl = a.ll + (size_t)l * LL_PER_LAYER;
     const float* cl = a.cache + (size_t)l * KV_ROW + h * DH;
@@ -544,21 +550,27 @@ __device__ void attention_wg(const FusedArgs a, FusedSmem& S, const Ctx c) {
         if (__all(epoch_of(w0) == c.E && epoch_of(w1) == c.E && epoch_of(w2) == c.E)) break;
         if (give_up(spins, hdr)) break;
       }
+      if (lane == 0) stamp(a.trace, 1 + 4 * l);
       sm.q[lane] = __uint_as_float((uint32_t)w0);
       sm.k[pos][lane] = __uint_as_float((uint32_t)w1);
       sm.v[pos][lane] = __uint_as_float((uint32_t)w2);
     }
     __syncthreads();
     const float o = attn_compute(sm, pos + 1);
-    if (wave == 0) st_sc1((u64*)gl + LO_ATT + h * DH + lane, pack(o, c.E));
+    if (wave == 0) {
+#pragma unroll
+      for (int x = 0; x < NXCC; ++x)
+        st_sc1(a.l2 + ((size_t)x * L + l) * L2_PER_LAYER + RO_ATT + h * DH + lane, pack(o, c.E));
+      if (lane == 0) stamp(a.trace, 2 + 4 * l);
+    }
     __syncthreads();
   }
   // the tied head: these workgroups take head rows too
   const int hw = (wave - 2) * c.G + (int)blockIdx.x;
   const int hstride = NCW * c.G;
   if (wave == 0) {
-    receive<12>(relayed(c, L - 1, RO_X2), c.E, S.xs, nullptr, hdr);
-    if constexpr (Q8) layernorm_seq(S.xs, a.w.small + sp::LNF_G, a.w.small + sp::LNF_B, S.xn);
+    receive<12>(copy_of(c, L - 1, RO_X2), c.E, S.xs, nullptr, hdr);
+    if constexpr (Q8) layernorm_seq(S.xs, S.lnf[0], S.lnf[1], S.xn);
     wg_barrier();
     if constexpr (Q8) wg_barrier();
   } else if (wave == 1) {
@@ -582,32 +594,24 @@ __global__ __launch_bounds__(FT, 1) void k_fused(const FusedArgs a) {
   extern __shared__ __align__(16) char smem_raw[];
   FusedSmem& S = *(FusedSmem*)smem_raw;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const bool att_wg = blockIdx.x < NATT;
   uint32_t* hdr = a.header;
-  if (threadIdx.x == 0) {
-    const uint32_t E = ld32(&hdr[HDR_EPOCH]) + 1u;
-    uint32_t x = xcc_id();
-    if (x >= MAX_XCC) {
-      set_error(hdr, ERR_XCC);
-      x = 0;
-    }
-    S.misc[0] = E;
-    S.misc[1] = x;
-    S.misc[2] = att_wg ? 0u : (uint32_t)elect_relay(hdr, x, E);
-  }
-  __syncthreads();
+  if (threadIdx.x == 0) stamp(a.trace, 0);
   Ctx c;
-  c.E = S.misc[0];
-  c.xcc = (int)S.misc[1];
-  c.leader = S.misc[2] != 0;
-  c.l2x = a.l2 + (size_t)c.xcc * L * L2_PER_LAYER;
+  c.E = ld32(&hdr[HDR_EPOCH]) + 1u;
+  c.xcc = (int)xcc_id();
+  if (c.xcc >= NXCC) {
+    if (threadIdx.x == 0) set_error(hdr, ERR_XCC);
+    c.xcc = 0;
+  }
+  c.cp = a.l2 + (size_t)c.xcc * L * L2_PER_LAYER;
   c.G = gridDim.x;
-  if (att_wg) attention_wg<Q8>(a, S, c);
+  if ((int)blockIdx.x < NATT) attention_wg<Q8>(a, S, c);
   else if (wave < 2) io_waves<Q8>(a, S, c);
   else compute_waves<Q8>(a, S, c);
 
   __syncthreads();
   if (threadIdx.x == 0) {
+    stamp(a.trace, 51);
     const uint32_t done = atomicAdd(&hdr[HDR_DONE], 1u);
     if (done == (uint32_t)c.G - 1) {
       hdr[HDR_DONE] = 0;
@@ -623,6 +627,8 @@ struct FusedConfig {
   int grid;
 };
 static FusedConfig g_cfg[2][64];
+uint64_t* g_fused_trace = nullptr;  // timeline test hook
+int g_fused_plain_launch = 1;       // 1: ordinary launch (default), 0: cooperative launch
 
 template <bool Q8>
 static hipError_t fused_config(FusedConfig& c) {
@@ -662,10 +668,14 @@ static hipError_t launch_fused_t(const Weights& w, const Work& k, uint32_t token
   a.l2 = k.ll + (size_t)L * LL_PER_LAYER;
   a.header = k.header;
   a.capture = capture;
+  a.trace = g_fused_trace;
   a.token = token;
   a.pos = pos;
   void* args[] = {&a};
-  e = hipLaunchCooperativeKernel((const void*)k_fused<Q8>, dim3(c.grid), dim3(FT), args, sizeof(FusedSmem), s);
+  if (g_fused_plain_launch)
+    e = hipLaunchKernel((const void*)k_fused<Q8>, dim3(c.grid), dim3(FT), args, sizeof(FusedSmem), s);
+  else
+    e = hipLaunchCooperativeKernel((const void*)k_fused<Q8>, dim3(c.grid), dim3(FT), args, sizeof(FusedSmem), s);
   if (e == hipSuccess) *used = true;
   return e;
 }

@@ -61,6 +61,8 @@ hipError_t launch_infer(const Weights& w, const Work& k, const uint32_t* toks, i
 hipError_t launch_fused(bool q8, const Weights& w, const Work& k, uint32_t token, int32_t pos, float* cache,
                         float* logits, char* capture, hipStream_t s, bool* used);
 extern bool g_force_phase_kernels;
+extern uint64_t* g_fused_trace;
+extern int g_fused_plain_launch;
 hipError_t launch_special_bits(int kind, uint32_t first, long long n, float* y, hipStream_t s);
 hipError_t launch_quantize(const float* x, int n, int8_t* codes, float* scales, hipStream_t s);
 hipError_t launch_gemm_test(const float* A, const float* W, float* C, int M, int N, int K, hipStream_t s);
