@@ -61,7 +61,7 @@ constexpr int RO_ATT = 0, RO_X1 = D, RO_G = 2 * D, RO_X2 = 2 * D + F;
 static_assert(RO_X2 + D == L2_PER_LAYER, "copy layout");
 constexpr int NXCC = 8;  // XCDs of an MI355X in single-partition mode
 
-enum { HDR_EPOCH = 0, HDR_DONE = 1, HDR_ERROR = 2, HDR_TICKETS = 8 };
+enum { HDR_EPOCH = 0, HDR_DONE = 1, HDR_ERROR = 2 };
 enum { ERR_SPIN = 1, ERR_XCC = 2 };
 
 struct FusedArgs {

@@ -91,8 +91,8 @@ inline PackedLayout packed_layout(int flags) {
 
 // ---- workspace layout, in bytes --------------------------------------------
 // header (uint32 words): [0] launch epoch of the fused step, [1] finished-workgroup
-// counter, [2] error code (nonzero: a fused-step wait gave up), [8..39] per-XCD relay
-// tickets (uint64).  A fresh workspace must be zero-filled.
+// counter, [2] error code (nonzero: a fused-step wait gave up).  A fresh workspace
+// must be zero-filled.
 struct WsLayout {
   size_t header, x, qkv, att, g, ll, pf_x, pf_h, pf_qkv, pf_att, pf_u, pf_part, total;
 };
