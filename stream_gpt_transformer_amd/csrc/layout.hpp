@@ -100,7 +100,9 @@ struct WsLayout {
 constexpr int LL_PER_LAYER = D3 + D + D + F + D;  // (value, epoch) words per block exchanged by the fused step
 constexpr int L2_PER_LAYER = D + D + F + D;       // of which relayed to every XCD
 constexpr int MAX_XCC = 16;                       // XCD ids 0..15
-constexpr int PF_SPLIT = 4;                       // split-K factor of the 3072-input prefill GEMM
+// Split-K partial sums of one prefill projection: at most S x 128 rows x N with
+// S*N <= 12 * 768 (QKV 4 x 2304, FC 3 x 3072, O and PR 12 x 768).
+constexpr size_t PF_PART_WORDS = (size_t)12 * PMAX * D;
 
 inline WsLayout ws_layout(int max_batch) {
   WsLayout w{};
@@ -117,7 +119,7 @@ inline WsLayout ws_layout(int max_batch) {
   w.pf_qkv = off; off = align256(off + (size_t)PMAX * D3 * 4);
   w.pf_att = off; off = align256(off + (size_t)PMAX * D * 4);
   w.pf_u = off; off = align256(off + (size_t)PMAX * F * 4);
-  w.pf_part = off; off = align256(off + (size_t)PF_SPLIT * PMAX * D * 4);
+  w.pf_part = off; off = align256(off + PF_PART_WORDS * 4);
   w.total = off;
   return w;
 }
