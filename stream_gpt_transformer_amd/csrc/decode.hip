@@ -99,10 +99,20 @@ __device__ __forceinline__ float proj_bias(const ProjArgs& a, int r) {
   else return 0.0f;
 }
 
+// One fp32 projection output without bias: the output projection sums its 12 head
+// groups and the MLP projection its 8 slices in fixed order (o_row, pr_row); the
+// others are one 64-lane dot (dot_frag).
+template <int MODE, int NI>
+__device__ __forceinline__ float proj_dot(const f4 (&w)[NI], const f4 (&x)[NI]) {
+  if constexpr (MODE == MODE_O) return o_row(w, x);
+  else if constexpr (MODE == MODE_PR) return pr_row(w, x);
+  else return dot_frag<NI>(w, x);
+}
+
 // fp32 projection over B sessions.  Block = 4 waves; wave w owns RPW consecutive
 // output rows, whose weights it loads once; sessions are staged BT at a time in
 // LDS as (normalised) input fragments.  Output r of session b is
-// dot_frag(W_r, x_b) + bias_r — the same value for any B, RPW or BT.
+// proj_dot(W_r, x_b) + bias_r — the same value for any B, RPW or BT.
 template <int MODE, int RPW, int BT>
 __global__ __launch_bounds__(256) void k_proj(const ProjArgs a) {
   constexpr int NI = MODE == MODE_PR ? F / 256 : D / 256;
@@ -139,7 +149,7 @@ __global__ __launch_bounds__(256) void k_proj(const ProjArgs a) {
       for (int rr = 0; rr < RPW; ++rr) {
         const int r = row0 + rr;
         if (r >= NROWS) break;
-        const float y = dot_frag<NI>(w[rr], x) + bias[rr];
+        const float y = proj_dot<MODE, NI>(w[rr], x) + bias[rr];
         if (lane == 0) proj_store<MODE>(a, b0 + s, r, y);
       }
     }

@@ -94,6 +94,58 @@ __device__ __forceinline__ float dot_frag(const f4 (&w)[NI], const f4 (&x)[NI]) 
   return wave_sum(acc);
 }
 
+// One 64-input group dot on a quarter wave: lane j of the quarter holds inputs
+// 4j..4j+3 of the group, runs an fmaf chain over them, and a butterfly over the 16
+// lanes of the quarter sums the partials (all 16 lanes end with the value).
+__device__ __forceinline__ float dot_q16(const f4 w, const f4 x) {
+  float acc = 0.0f;
+  acc = fmaf(w.x, x.x, acc);
+  acc = fmaf(w.y, x.y, acc);
+  acc = fmaf(w.z, x.z, acc);
+  acc = fmaf(w.w, x.w, acc);
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) acc = acc + __shfl_xor(acc, m);
+  return acc;
+}
+__device__ __forceinline__ float lane_val(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// The fp32 output projection as a sum over heads.  In the lane-fragment layout the
+// 64 inputs of head h = 4i + q sit in quarter q of fragment i, so p_h = dot_q16 of
+// that quarter; then y = 0, y = y + p_h for h = 0..11 (bias excluded).
+__device__ __forceinline__ float o_row(const f4 (&w)[3], const f4 (&x)[3]) {
+  float p[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) p[i] = dot_q16(w[i], x[i]);
+  float y = 0.0f;
+#pragma unroll
+  for (int h = 0; h < H; ++h) y = y + lane_val(p[h / 4], 16 * (h % 4));
+  return y;
+}
+
+// The fp32 MLP projection (3072 inputs) as a sum over eight slices of 384 inputs
+// (six 64-input groups each): q_g = dot_q16 of group g (quarter g%4 of fragment
+// g/4); p_s = q_6s + q_6s+1 + ... + q_6s+5 in order; y = 0, y = y + p_s for
+// s = 0..7 (bias excluded).
+constexpr int PR_SLICES = 8;
+constexpr int PR_SLICE_GROUPS = F / 64 / PR_SLICES;  // 6
+__device__ __forceinline__ float pr_row(const f4 (&w)[12], const f4 (&x)[12]) {
+  float q[12];
+#pragma unroll
+  for (int f = 0; f < 12; ++f) q[f] = dot_q16(w[f], x[f]);
+  float y = 0.0f;
+#pragma unroll
+  for (int s = 0; s < PR_SLICES; ++s) {
+    const int g0 = PR_SLICE_GROUPS * s;
+    float p = lane_val(q[g0 / 4], 16 * (g0 % 4));
+#pragma unroll
+    for (int k = 1; k < PR_SLICE_GROUPS; ++k) p = p + lane_val(q[(g0 + k) / 4], 16 * ((g0 + k) % 4));
+    y = y + p;
+  }
+  return y;
+}
+
 // Ordered binary32 exponential (LeanExe GPT-2 README, numerical functions: an
 // ordered binary32 exponential approximation; muInference page, IEEE-ops table:
 // range reduction, Taylor polynomial, 2^k as a bit pattern, only correctly rounded
@@ -328,12 +380,16 @@ __device__ __forceinline__ void q8_load_row(i4 (&wc)[(K + 1023) / 1024], float& 
   constexpr int NCH = (K + 1023) / 1024, G = K / 64;
   const int lane = lane_id();
   const int8_t* row = codes + (size_t)r * K;
+  // every lane loads (lanes past the row re-read its last 16 bytes), so callers can
+  // keep an identical memory-instruction stream on every path
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
     const int off = 1024 * i + 16 * lane;
-    wc[i] = off < K ? __builtin_nontemporal_load((const i4*)(row + off)) : i4{0, 0, 0, 0};
+    const i4 v = __builtin_nontemporal_load((const i4*)(row + min(off, K - 16)));
+    wc[i] = off < K ? v : i4{0, 0, 0, 0};
   }
-  swl = lane < G ? scales[(size_t)r * G + lane] : 0.0f;
+  const float sv = scales[(size_t)r * G + min(lane, G - 1)];
+  swl = lane < G ? sv : 0.0f;
 }
 
 }  // namespace g2

@@ -97,9 +97,16 @@ struct WsLayout {
   size_t header, x, qkv, att, g, ll, pf_x, pf_h, pf_qkv, pf_att, pf_u, pf_part, total;
 };
 
-constexpr int LL_PER_LAYER = D3 + D + D + F + D;  // (value, epoch) words per block exchanged by the fused step
-constexpr int L2_PER_LAYER = D + D + F + D;       // of which relayed to every XCD
-constexpr int MAX_XCC = 16;                       // XCD ids 0..15
+// Exchange area of the fused step, in 64-bit (epoch, value) words: per XCD and
+// block the vectors exchanged inside the XCD (qkv of its heads 384 | attention
+// output 128 | x1 768 | GELU slice 384 | x2 768), per block the partial terms of the
+// two cross-XCD reductions (output projection 12 x 768 | MLP projection up to
+// 48 x 768), one word per workgroup for the placement check, and one 128-byte line
+// per wave (256 workgroups x 8 waves) that absorbs the stores of units it does not own.
+constexpr int FX_NXCC = 8;
+constexpr int FX_LOC_PER_LAYER = 384 + 128 + D + 384 + D;
+constexpr int FX_GLB_PER_LAYER = (H + F / 64) * D;
+constexpr size_t FX_WORDS = (size_t)FX_NXCC * L * FX_LOC_PER_LAYER + (size_t)L * FX_GLB_PER_LAYER + 256 + 256 * 8 * 16;
 // Split-K partial sums of one prefill projection: at most S x 128 rows x N with
 // S*N <= 12 * 768 (QKV 4 x 2304, FC 3 x 3072, O and PR 12 x 768).
 constexpr size_t PF_PART_WORDS = (size_t)12 * PMAX * D;
@@ -113,7 +120,7 @@ inline WsLayout ws_layout(int max_batch) {
   w.qkv = off; off = align256(off + B * D3 * 4);
   w.att = off; off = align256(off + B * D * 4);
   w.g = off; off = align256(off + B * F * 4);
-  w.ll = off; off = align256(off + ((size_t)L * LL_PER_LAYER + (size_t)MAX_XCC * L * L2_PER_LAYER) * 8);
+  w.ll = off; off = align256(off + FX_WORDS * 8);
   w.pf_x = off; off = align256(off + (size_t)PMAX * D * 4);
   w.pf_h = off; off = align256(off + (size_t)PMAX * D * 4);
   w.pf_qkv = off; off = align256(off + (size_t)PMAX * D3 * 4);
