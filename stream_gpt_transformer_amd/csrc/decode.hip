@@ -159,6 +159,7 @@ __global__ __launch_bounds__(256) void k_proj(const ProjArgs a) {
 // Attention of head blockIdx.x for session blockIdx.y over its positions 0..pos,
 // reading every key/value row (the current one included) from the session's cache
 // at (source*12 + layer)*1536 + offset.
+template <bool SEQ>
 __global__ __launch_bounds__(128) void k_attn(const ProjArgs a) {
   __shared__ AttnSmem sm;
   const int h = blockIdx.x, b = blockIdx.y;
@@ -168,13 +169,13 @@ __global__ __launch_bounds__(128) void k_attn(const ProjArgs a) {
   auto kv = [&](int j) { return cache + ((size_t)j * L + l) * KV_ROW + h * DH; };
   attn_stage(sm, kv, npos, a.k.qkv + (size_t)b * D3 + h * DH);
   __syncthreads();
-  const float o = attn_compute(sm, npos);
+  const float o = SEQ ? attn_compute_seq(sm, npos) : attn_compute(sm, npos, 2);
   if (threadIdx.x < DH) a.k.att[(size_t)b * D + h * DH + threadIdx.x] = o;
 }
 
 // ---- int8 group-64 projections (batch 1) -------------------------------------
-// LayerNorm inputs use the sequential-sum LayerNorm, so every fp32 value of the
-// int8 path follows the specification's operation order exactly.
+// LayerNorm inputs use the sequential-order LayerNorm (layernorm_seq), and the
+// attention the sequential-order attn_compute_seq, as the fused int8 step does.
 // The block quantizes its fp32 input in LDS (every block does the same work and
 // gets the same codes), then each wave streams its rows' int8 codes: lane l takes
 // 16 codes at byte 1024*i + 16*l, so group 16*i + l/4; v_dot4 gives a lane partial
@@ -189,6 +190,7 @@ __global__ __launch_bounds__(256) void k_q8proj(const ProjArgs a) {
   constexpr int NCH = (K + 1023) / 1024;
   constexpr int NROWS = mode_rows<MODE>();
   __shared__ __align__(16) float xf[K];
+  __shared__ __align__(16) float lntmp[mode_ln<MODE>() ? D : 1];
   __shared__ __align__(16) int8_t xc[K];
   __shared__ float xsc[G];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -202,7 +204,7 @@ __global__ __launch_bounds__(256) void k_q8proj(const ProjArgs a) {
   }
   __syncthreads();
   if constexpr (mode_ln<MODE>()) {
-    if (wave == 0) layernorm_seq(xf, ln_gamma<MODE>(a), ln_beta<MODE>(a), xf);
+    if (wave == 0) layernorm_seq(xf, ln_gamma<MODE>(a), ln_beta<MODE>(a), xf, lntmp);
     __syncthreads();
   }
   for (int g = wave; g < G; g += 4) {
@@ -271,7 +273,7 @@ static void launch_layers(ProjArgs& a, hipStream_t s) {
   for (int l = 0; l < L; ++l) {
     a.layer = l;
     launch_proj<MODE_QKV, RPW, BT768>(a, s);
-    hipLaunchKernelGGL(k_attn, dim3(H, B), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(k_attn<false>, dim3(H, B), dim3(128), 0, s, a);
     launch_proj<MODE_O, RPW, BT768>(a, s);
     launch_proj<MODE_FC, RPW, BT768>(a, s);
     launch_proj<MODE_PR, RPW, BT3072>(a, s);
@@ -318,7 +320,7 @@ hipError_t launch_step_q8(const Weights& w, const Work& k, const Sessions& ss, f
   for (int l = 0; l < L; ++l) {
     a.layer = l;
     launch_q8<MODE_QKV, 2>(a, s);
-    hipLaunchKernelGGL(k_attn, dim3(H, 1), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(k_attn<true>, dim3(H, 1), dim3(128), 0, s, a);
     launch_q8<MODE_O, 2>(a, s);
     launch_q8<MODE_FC, 2>(a, s);
     launch_q8<MODE_PR, 2>(a, s);

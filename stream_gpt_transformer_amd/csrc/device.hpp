@@ -20,17 +20,66 @@ namespace g2 {
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef int i4 __attribute__((ext_vector_type(4)));
 
-// All 64 lanes end with the same value: at each butterfly step lanes l and l^m add
-// the same two operands (in swapped order; addition commutes exactly).
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = v + __shfl_xor(v, m);
+// ---- cross-lane reductions on DPP ---------------------------------------------
+// Lane moves inside one VALU instruction (GFX9 data-parallel primitives), with no
+// trip through the LDS crossbar.  quad_perm [1,0,3,2] and [2,3,0,1] swap lanes at
+// distance 1 and 2; row_half_mirror and row_mirror reverse 8- and 16-lane groups,
+// which acts as a swap at distance 4 and 8 once the quads (then the 8-lane halves)
+// hold equal values; row_bcast:15 adds row r-1's last lane into row r (rows 1, 3),
+// row_bcast:31 adds lane 31 into rows 2 and 3.
+enum : int {
+  DPP_QUAD_1032 = 0xB1,
+  DPP_QUAD_2301 = 0x4E,
+  DPP_ROW_MIRROR = 0x140,
+  DPP_ROW_HALF_MIRROR = 0x141,
+  DPP_ROW_BCAST15 = 0x142,
+  DPP_ROW_BCAST31 = 0x143,
+};
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp_f(float v) {
+  const int i = __float_as_int(v);
+  return __int_as_float(__builtin_amdgcn_update_dpp(i, i, CTRL, ROWS, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ float bcast_lane(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Sum over each 16-lane row; every lane of the row ends with the row's value
+// (the two operands of each step are equal in every lane of a pair, in swapped
+// order, and addition commutes exactly).
+__device__ __forceinline__ float row16_sum(float v) {
+  v = v + dpp_f<DPP_QUAD_1032>(v);
+  v = v + dpp_f<DPP_QUAD_2301>(v);
+  v = v + dpp_f<DPP_ROW_HALF_MIRROR>(v);
+  v = v + dpp_f<DPP_ROW_MIRROR>(v);
   return v;
 }
+// Sum of the 64 lanes: row sums r0..r3 as above, then (r3 + r2) + (r1 + r0) in
+// lane 63, read back as a wave-uniform value.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  v = v + dpp_f<DPP_ROW_BCAST15, 0xa>(v);
+  v = v + dpp_f<DPP_ROW_BCAST31, 0xc>(v);
+  return bcast_lane(v, 63);
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
+  v = fmaxf(v, dpp_f<DPP_QUAD_1032>(v));
+  v = fmaxf(v, dpp_f<DPP_QUAD_2301>(v));
+  v = fmaxf(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp_f<DPP_ROW_MIRROR>(v));
+  v = fmaxf(v, dpp_f<DPP_ROW_BCAST15, 0xa>(v));
+  v = fmaxf(v, dpp_f<DPP_ROW_BCAST31, 0xc>(v));
+  return bcast_lane(v, 63);
+}
+// Exact integer sum over each 4-lane quad (every lane of the quad gets it).
+__device__ __forceinline__ int quad_sum(int p) {
+  p += dpp_i<DPP_QUAD_1032>(p);
+  p += dpp_i<DPP_QUAD_2301>(p);
+  return p;
 }
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
@@ -54,7 +103,7 @@ __device__ __forceinline__ void store_frag(float* __restrict__ dst, const f4 (&x
 // LayerNorm of a 768-vector held as a fragment (one wave):
 // mean = (sum x)/768, d = x - mean, var = (sum d*d)/768, r = 1/sqrt(var + 1e-5),
 // y = (d*r)*gamma + beta.  Each lane sums its 12 values in (i, e) order, then the
-// butterfly combines lanes.
+// wave_sum combines lanes.
 __device__ __forceinline__ void layernorm_frag(f4 (&x)[3], const float* __restrict__ gamma,
                                                const float* __restrict__ beta) {
   float s = 0.0f;
@@ -79,7 +128,7 @@ __device__ __forceinline__ void layernorm_frag(f4 (&x)[3], const float* __restri
 }
 
 // One output of an fp32 projection: lane l accumulates its 4*NI products with an
-// explicit fmaf chain in (i, e) order, then the butterfly sums the 64 lane partials.
+// explicit fmaf chain in (i, e) order, then wave_sum adds the 64 lane partials.
 // The returned value (identical in every lane) excludes the bias.
 template <int NI>
 __device__ __forceinline__ float dot_frag(const f4 (&w)[NI], const f4 (&x)[NI]) {
@@ -95,7 +144,7 @@ __device__ __forceinline__ float dot_frag(const f4 (&w)[NI], const f4 (&x)[NI]) 
 }
 
 // One 64-input group dot on a quarter wave: lane j of the quarter holds inputs
-// 4j..4j+3 of the group, runs an fmaf chain over them, and a butterfly over the 16
+// 4j..4j+3 of the group, runs an fmaf chain over them, and row16_sum over the 16
 // lanes of the quarter sums the partials (all 16 lanes end with the value).
 __device__ __forceinline__ float dot_q16(const f4 w, const f4 x) {
   float acc = 0.0f;
@@ -103,13 +152,9 @@ __device__ __forceinline__ float dot_q16(const f4 w, const f4 x) {
   acc = fmaf(w.y, x.y, acc);
   acc = fmaf(w.z, x.z, acc);
   acc = fmaf(w.w, x.w, acc);
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) acc = acc + __shfl_xor(acc, m);
-  return acc;
+  return row16_sum(acc);
 }
-__device__ __forceinline__ float lane_val(float v, int lane) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
-}
+__device__ __forceinline__ float lane_val(float v, int lane) { return bcast_lane(v, lane); }
 
 // The fp32 output projection as a sum over heads.  In the lane-fragment layout the
 // 64 inputs of head h = 4i + q sit in quarter q of fragment i, so p_h = dot_q16 of
@@ -184,7 +229,7 @@ __device__ __forceinline__ float tanh_spec(float z) {
 }
 
 // dot_frag with the input fragment read from LDS one float4 at a time (same fmaf
-// chain and butterfly, so the same value; fewer live registers).
+// chain and wave_sum, so the same value; fewer live registers).
 template <int NI>
 __device__ __forceinline__ float dot_lds(const f4 (&w)[NI], const float* xs) {
   const int l = lane_id();
@@ -208,49 +253,98 @@ __device__ __forceinline__ float gelu_tanh(float u) {
   return (0.5f * u) * (1.0f + t);
 }
 
-// LayerNorm of a 768-vector in LDS with every sum taken sequentially in index order
-// (mean, then the variance of the centred values), one rounding per operation:
-// the order the int8 path needs so that its activation codes are a function of the
-// specification alone.  Lane 0 runs the two sums; all 64 lanes write y to LDS.
-__device__ __forceinline__ void layernorm_seq(const float* xs, const float* __restrict__ gamma,
-                                              const float* __restrict__ beta, float* ys) {
-  const int lane = lane_id();
-  float mean = 0.0f, r = 0.0f;
-  if (lane == 0) {
-    float s = 0.0f;
-#pragma unroll 16
-    for (int i = 0; i < 768; i += 4) {
-      const f4 v = *(const f4*)(xs + i);
-      s = s + v.x; s = s + v.y; s = s + v.z; s = s + v.w;
-    }
-    mean = s / 768.0f;
-    float q = 0.0f;
-#pragma unroll 16
-    for (int i = 0; i < 768; i += 4) {
-      const f4 v = *(const f4*)(xs + i) - mean;
-      q = q + v.x * v.x; q = q + v.y * v.y; q = q + v.z * v.z; q = q + v.w * v.w;
-    }
-    const float var = q / 768.0f;
-    r = 1.0f / sqrtf(var + 1e-5f);
+// ---- sequential-order LayerNorm (the int8 path) -----------------------------
+// The int8 path quantizes LayerNorm outputs, so a one-ulp difference in an output
+// can move a code across a rounding boundary; its LayerNorm therefore takes every
+// sum sequentially in index order, one rounding per operation, as the oracle does:
+//   mean = (((0 + x_0) + x_1) + ... + x_767) / 768;  d_i = x_i - mean;
+//   var = (((0 + d_0*d_0) + d_1*d_1) + ...) / 768;  r = 1/sqrt(var + 1e-5);
+//   y_i = (d_i*r)*gamma_i + beta_i.
+// The chain of 768 dependent adds is the cost: the wave reads the next 32 values
+// from LDS (broadcast reads) while it adds the current 32, so the chain never
+// waits for LDS.
+__device__ __forceinline__ void lds_load32(f4 (&v)[8], const float* p) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = *(const f4*)(p + 4 * i);
+}
+__device__ __forceinline__ void seq_add32(float& s, const f4 (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    s = s + v[i].x;
+    s = s + v[i].y;
+    s = s + v[i].z;
+    s = s + v[i].w;
   }
-  mean = __shfl(mean, 0);
-  r = __shfl(r, 0);
-  for (int i = lane; i < 768; i += 64) ys[i] = ((xs[i] - mean) * r) * gamma[i] + beta[i];
+}
+// s = 0 + t_0 + t_1 + ... + t_767 in order, t in LDS.
+__device__ __forceinline__ float seq_sum768(const float* t) {
+  f4 a[8], b[8];
+  lds_load32(a, t);
+  float s = 0.0f;
+#pragma unroll 1
+  for (int c = 0; c < 24; c += 2) {
+    lds_load32(b, t + 32 * (c + 1));
+    __builtin_amdgcn_sched_barrier(0);
+    seq_add32(s, a);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_load32(a, t + 32 * min(c + 2, 23));
+    __builtin_amdgcn_sched_barrier(0);
+    seq_add32(s, b);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return s;
+}
+// One wave: xs (LDS) -> ys (LDS, may be xs); tmp is 768 floats of LDS scratch.
+__device__ __forceinline__ void layernorm_seq(const float* xs, const float* __restrict__ gamma,
+                                              const float* __restrict__ beta, float* ys, float* tmp) {
+  const int lane = lane_id();
+  const float mean = seq_sum768(xs) / 768.0f;
+  f4 d[3];
+  load_frag<3>(d, xs);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    d[i] = d[i] - mean;
+    *(f4*)(tmp + 256 * i + 4 * lane) = d[i] * d[i];
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the squares are in LDS
+  __builtin_amdgcn_wave_barrier();
+  const float var = seq_sum768(tmp) / 768.0f;
+  const float r = 1.0f / sqrtf(var + 1e-5f);
+  f4 g[3], b[3];
+  load_frag<3>(g, gamma);
+  load_frag<3>(b, beta);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) d[i] = (d[i] * r) * g[i] + b[i];
+  store_frag<3>(ys, d);
+}
+
+// LayerNorm of a 768-vector in LDS by one wave (layernorm_frag), written to ys
+// (which may be xs).
+__device__ __forceinline__ void layernorm_lds(const float* xs, const float* __restrict__ gamma,
+                                              const float* __restrict__ beta, float* ys) {
+  f4 x[3];
+  load_frag<3>(x, xs);
+  layernorm_frag(x, gamma, beta);
+  store_frag<3>(ys, x);
 }
 
 // ---- attention (one session, one head) --------------------------------------
-// 128 threads (two wavefronts); thread t owns key t, and with npos keys (1..128)
-// every value is the oracle's sequential definition, one rounding per operation:
+// npos keys (1..128), thread t < 128 owns key t:
 //   s_t = (sum over d ascending of q_d*K_t,d) * 0.125   (1/sqrt(64));
 //   m = max_t s_t;  e_t = exp_spec(s_t - m);
-//   Z = sum over t ascending of e_t;  w_t = e_t / Z;
-//   a_d = sum over t ascending of w_t*V_t,d.
+//   Z = Z_0 + Z_1 with Z_w = wave_sum of e_t over t in [64w, 64w+64);
+//   w_t = e_t / Z;
+//   a_d = p_0 + p_1 + ... + p_7 with p_b = sum over t in [16b, 16b+16), t < npos,
+//   ascending, of w_t*V_t,d.
+// The key blocks b are spread over waves 0..nwav-1 of the block (every value is the
+// same for any nwav).
 struct AttnSmem {
   float k[PMAX][DH + 4];  // padded rows, 16-byte aligned
   float v[PMAX][DH];
   float q[DH];
   float w[PMAX];
   float red[4];
+  float part[8][DH];  // per key-block partial outputs
 };
 
 // Stage key/value rows j0..j1-1 of one head into LDS with threads tid0..tid0+nthr-1
@@ -275,24 +369,74 @@ __device__ __forceinline__ void attn_stage(AttnSmem& sm, RowPtr kv, int npos, co
 }
 
 // Returns a_d in threads 0..63 (d = thread index); other threads return 0.  Every
-// thread of the block must call it (it synchronises the block); threads 128 and up
-// only take part in the barriers.
-__device__ __forceinline__ float attn_compute(AttnSmem& sm, int npos) {
+// thread of the block must call it (it synchronises the block); the block needs at
+// least 128 threads and nwav waves.
+__device__ __forceinline__ float attn_compute(AttnSmem& sm, int npos, int nwav) {
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
   const bool act = t < 128;
   float s = -INFINITY;
   if (act && t < npos) {
-    f4 kr[DH / 4];
-#pragma unroll
-    for (int i = 0; i < DH / 4; ++i) kr[i] = *(const f4*)&sm.k[t][4 * i];
     float acc = 0.0f;
-#pragma unroll
+#pragma unroll 4
     for (int i = 0; i < DH / 4; ++i) {
+      const f4 kr = *(const f4*)&sm.k[t][4 * i];
       const f4 qq = *(const f4*)&sm.q[4 * i];
-      acc = acc + qq.x * kr[i].x;
-      acc = acc + qq.y * kr[i].y;
-      acc = acc + qq.z * kr[i].z;
-      acc = acc + qq.w * kr[i].w;
+      acc = acc + qq.x * kr.x;
+      acc = acc + qq.y * kr.y;
+      acc = acc + qq.z * kr.z;
+      acc = acc + qq.w * kr.w;
+    }
+    s = acc * 0.125f;
+  }
+  const float mw = wave_max(s);
+  if (act && lane == 0) sm.red[wv] = mw;
+  __syncthreads();
+  const float m = fmaxf(sm.red[0], sm.red[1]);
+  const float e = (act && t < npos) ? exp_spec(s - m) : 0.0f;
+  const float zw = wave_sum(e);
+  __syncthreads();  // everyone has read red[0..1]
+  if (act && lane == 0) sm.red[2 + wv] = zw;
+  __syncthreads();
+  const float Z = sm.red[2] + sm.red[3];
+  if (act) sm.w[t] = e / Z;
+  __syncthreads();
+  if (wv < nwav) {
+    for (int b = wv; b < 8; b += nwav) {
+      float p = 0.0f;
+      const int j1 = min(16 * b + 16, npos);
+      for (int j = 16 * b; j < j1; ++j) p = p + sm.w[j] * sm.v[j][lane];
+      sm.part[b][lane] = p;
+    }
+  }
+  __syncthreads();
+  float acc = 0.0f;
+  if (wv == 0) {
+    acc = sm.part[0][lane];
+#pragma unroll
+    for (int b = 1; b < 8; ++b) acc = acc + sm.part[b][lane];
+  }
+  return acc;
+}
+
+// The int8 path's attention, in the oracle's order (its output is quantized, so
+// it must not depend on a reduction tree): s_t as above; m = max_t s_t;
+// e_t = exp_spec(s_t - m); Z = ((0 + e_0) + e_1) + ... ; w_t = e_t / Z;
+// a_d = ((0 + w_0*V_0,d) + w_1*V_1,d) + ... .  Wave 0 runs the two ordered sums.
+// Same calling rules as attn_compute.
+__device__ __forceinline__ float attn_compute_seq(AttnSmem& sm, int npos) {
+  const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
+  const bool act = t < 128;
+  float s = -INFINITY;
+  if (act && t < npos) {
+    float acc = 0.0f;
+#pragma unroll 4
+    for (int i = 0; i < DH / 4; ++i) {
+      const f4 kr = *(const f4*)&sm.k[t][4 * i];
+      const f4 qq = *(const f4*)&sm.q[4 * i];
+      acc = acc + qq.x * kr.x;
+      acc = acc + qq.y * kr.y;
+      acc = acc + qq.z * kr.z;
+      acc = acc + qq.w * kr.w;
     }
     s = acc * 0.125f;
   }
@@ -303,11 +447,11 @@ __device__ __forceinline__ float attn_compute(AttnSmem& sm, int npos) {
   const float e = (act && t < npos) ? exp_spec(s - m) : 0.0f;
   if (act) sm.w[t] = e;
   __syncthreads();
-  if (t == 0) {
+  if (wv == 0) {
     float Z = 0.0f;
 #pragma unroll 16
     for (int j = 0; j < npos; ++j) Z = Z + sm.w[j];
-    sm.red[2] = Z;
+    if (lane == 0) sm.red[2] = Z;
   }
   __syncthreads();
   if (act && t < npos) sm.w[t] = e / sm.red[2];
@@ -339,7 +483,7 @@ __device__ __forceinline__ int quant_lane(float x, float& s_out) {
 // codes at bytes 1024*i + 16*l (i < NCH), i.e. group 16*i + l/4; swl is lane g's
 // weight scale for group g (g < K/64).  xc/xsc are the input codes and scales.
 //   acc[g] = sum of the 64 code products of group g (v_dot4, then two exact integer
-//   butterfly steps inside each 4-lane quad), moved to lane g;
+//   quad_sum steps inside each 4-lane quad), moved to lane g;
 //   t[g] = ((float)acc[g] * sw[g]) * sx[g] in lane g;
 //   y = 0; y = y + t[g] for g = 0..K/64-1  (fixed order, through readlane).
 // cap_acc (may be null) receives acc[0..K/64-1].  Bias excluded.
@@ -360,8 +504,7 @@ __device__ __forceinline__ float q8_dot(const i4 (&wc)[(K + 1023) / 1024], float
       p = __builtin_amdgcn_sdot4(wc[i].z, xv.z, p, false);
       p = __builtin_amdgcn_sdot4(wc[i].w, xv.w, p, false);
     }
-    p += __shfl_xor(p, 1);
-    p += __shfl_xor(p, 2);
+    p = quad_sum(p);
     const int gi = __shfl(p, 4 * (lane & 15));  // group 16*i + (lane & 15)
     if ((lane >> 4) == i) accg = gi;
   }

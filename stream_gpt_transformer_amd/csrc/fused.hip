@@ -377,14 +377,13 @@ __device__ __forceinline__ int quad_acc(const i4 wc, const i4 xc) {
   p = __builtin_amdgcn_sdot4(wc.y, xc.y, p, false);
   p = __builtin_amdgcn_sdot4(wc.z, xc.z, p, false);
   p = __builtin_amdgcn_sdot4(wc.w, xc.w, p, false);
-  p += __shfl_xor(p, 1);
-  p += __shfl_xor(p, 2);
-  return p;
+  return quad_sum(p);
 }
 
 struct FusedSmem {
   float xs[D];         // block input x, then x1 (all-gathers)
   float xn[D];         // int8 path: LayerNorm output
+  float lntmp[D];      // int8 path: LayerNorm scratch
   float att[2 * DH];   // attention output of the XCD's heads
   float xg[GS];        // the XCD's GELU slice
   float rs[NG_PR * RSN];  // reduce-scatter terms
@@ -514,7 +513,7 @@ __device__ void io_wave(const FusedArgs a, FusedSmem& S, const Ctx c) {
     const float(*lp)[D] = S.lnp[l & 1];
     u64* loc = loc_of(c, l);
     if (lane == 0) stamp(a.trace, 1 + 4 * l);
-    if constexpr (Q8) layernorm_seq(S.xs, lp[0], lp[1], S.xn);
+    if constexpr (Q8) layernorm_seq(S.xs, lp[0], lp[1], S.xn, S.lntmp);
     if (l == 5 && lane == 0) stamp(a.trace, 52);
     wg_barrier();  // B1: QKV
     qbar(l, M_QKV, cap0);
@@ -533,7 +532,7 @@ __device__ void io_wave(const FusedArgs a, FusedSmem& S, const Ctx c) {
     if (l == 5 && lane == 0) stamp(a.trace, 55);
     gather<12>(loc + LO_X1, c.E, S.xs, hdr);
     if (lane == 0) stamp(a.trace, 3 + 4 * l);
-    if constexpr (Q8) layernorm_seq(S.xs, lp[2], lp[3], S.xn);
+    if constexpr (Q8) layernorm_seq(S.xs, lp[2], lp[3], S.xn, S.lntmp);
     wg_barrier();  // B3: FC
     qbar(l, M_FC, cap0);
     gather<GS / 64>(loc + LO_G, c.E, S.xg, hdr);
@@ -545,7 +544,7 @@ __device__ void io_wave(const FusedArgs a, FusedSmem& S, const Ctx c) {
     gather<12>(loc + LO_X2, c.E, S.xs, hdr);
   }
   if (lane == 0) stamp(a.trace, 49);
-  if constexpr (Q8) layernorm_seq(S.xs, S.lnf[0], S.lnf[1], S.xn);
+  if constexpr (Q8) layernorm_seq(S.xs, S.lnf[0], S.lnf[1], S.xn, S.lntmp);
   wg_barrier();  // B5: head
   qbar(0, M_HEAD, cap0);
 }
@@ -823,7 +822,7 @@ __device__ void attention_wg(const FusedArgs a, FusedSmem& S, const Ctx c) {
         sm.v[pos][lane] = v[2];
       }
       __syncthreads();
-      const float o = attn_compute(sm, pos + 1);
+      const float o = Q8 ? attn_compute_seq(sm, pos + 1) : attn_compute(sm, pos + 1, FT / 64);
       if (wave == 0) {
         st_loc(loc + LO_ATT + DH * c.rank + lane, pack(o, c.E));
         if (lane == 0) stamp(a.trace, 2 + 4 * l);
@@ -854,7 +853,7 @@ __device__ void attention_wg(const FusedArgs a, FusedSmem& S, const Ctx c) {
   }
   if (wave == 0) {
     gather<12>(loc_of(c, L - 1) + LO_X2, c.E, S.xs, hdr);
-    if constexpr (Q8) layernorm_seq(S.xs, S.lnf[0], S.lnf[1], S.xn);
+    if constexpr (Q8) layernorm_seq(S.xs, S.lnf[0], S.lnf[1], S.xn, S.lntmp);
   }
   wg_barrier();
   if (wave >= 1) {
