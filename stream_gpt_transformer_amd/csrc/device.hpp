@@ -82,6 +82,14 @@ __device__ __forceinline__ int quad_sum(int p) {
   return p;
 }
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+// The lane index through an empty asm: address arithmetic derived from it is redone
+// where it is used, instead of being hoisted out of a loop and kept live in
+// registers (the weight-load helpers call it).
+__device__ __forceinline__ int lane_id_fresh() {
+  int l = (int)(threadIdx.x & 63);
+  asm volatile("" : "+v"(l));
+  return l;
+}
 
 // ---- lane fragments ---------------------------------------------------------
 // A K-vector (K = 256*NI) is spread over one wavefront as NI float4 per lane:
@@ -328,9 +336,15 @@ __device__ __forceinline__ void layernorm_lds(const float* xs, const float* __re
   store_frag<3>(ys, x);
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not
+// for its outstanding global loads and stores (a __syncthreads would also wait for
+// every store of the wave to be acknowledged).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // ---- attention (one session, one head) --------------------------------------
 // npos keys (1..128), thread t < 128 owns key t:
-//   s_t = (sum over d ascending of q_d*K_t,d) * 0.125   (1/sqrt(64));
+//   s_t = ((c_0 + c_1) + (c_2 + c_3)) * 0.125 (1/sqrt(64)), where c_e is the sum over
+//   i ascending of q_{4i+e}*K_t,4i+e;
 //   m = max_t s_t;  e_t = exp_spec(s_t - m);
 //   Z = Z_0 + Z_1 with Z_w = wave_sum of e_t over t in [64w, 64w+64);
 //   w_t = e_t / Z;
@@ -376,39 +390,41 @@ __device__ __forceinline__ float attn_compute(AttnSmem& sm, int npos, int nwav) 
   const bool act = t < 128;
   float s = -INFINITY;
   if (act && t < npos) {
-    float acc = 0.0f;
-#pragma unroll 4
+    f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
     for (int i = 0; i < DH / 4; ++i) {
       const f4 kr = *(const f4*)&sm.k[t][4 * i];
       const f4 qq = *(const f4*)&sm.q[4 * i];
-      acc = acc + qq.x * kr.x;
-      acc = acc + qq.y * kr.y;
-      acc = acc + qq.z * kr.z;
-      acc = acc + qq.w * kr.w;
+      acc = acc + qq * kr;
     }
-    s = acc * 0.125f;
+    s = ((acc.x + acc.y) + (acc.z + acc.w)) * 0.125f;
   }
   const float mw = wave_max(s);
   if (act && lane == 0) sm.red[wv] = mw;
-  __syncthreads();
+  lds_barrier();
   const float m = fmaxf(sm.red[0], sm.red[1]);
   const float e = (act && t < npos) ? exp_spec(s - m) : 0.0f;
   const float zw = wave_sum(e);
-  __syncthreads();  // everyone has read red[0..1]
+  lds_barrier();  // everyone has read red[0..1]
   if (act && lane == 0) sm.red[2 + wv] = zw;
-  __syncthreads();
+  lds_barrier();
   const float Z = sm.red[2] + sm.red[3];
   if (act) sm.w[t] = e / Z;
-  __syncthreads();
+  lds_barrier();
   if (wv < nwav) {
     for (int b = wv; b < 8; b += nwav) {
       float p = 0.0f;
-      const int j1 = min(16 * b + 16, npos);
-      for (int j = 16 * b; j < j1; ++j) p = p + sm.w[j] * sm.v[j][lane];
+      const int j0 = 16 * b, j1 = min(j0 + 16, npos);
+      if (j1 - j0 == 16) {
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) p = p + sm.w[j0 + jj] * sm.v[j0 + jj][lane];
+      } else {
+        for (int j = j0; j < j1; ++j) p = p + sm.w[j] * sm.v[j][lane];
+      }
       sm.part[b][lane] = p;
     }
   }
-  __syncthreads();
+  lds_barrier();
   float acc = 0.0f;
   if (wv == 0) {
     acc = sm.part[0][lane];
@@ -442,20 +458,20 @@ __device__ __forceinline__ float attn_compute_seq(AttnSmem& sm, int npos) {
   }
   const float mw = wave_max(s);
   if (act && lane == 0) sm.red[wv] = mw;
-  __syncthreads();
+  lds_barrier();
   const float m = fmaxf(sm.red[0], sm.red[1]);
   const float e = (act && t < npos) ? exp_spec(s - m) : 0.0f;
   if (act) sm.w[t] = e;
-  __syncthreads();
+  lds_barrier();
   if (wv == 0) {
     float Z = 0.0f;
 #pragma unroll 16
     for (int j = 0; j < npos; ++j) Z = Z + sm.w[j];
     if (lane == 0) sm.red[2] = Z;
   }
-  __syncthreads();
+  lds_barrier();
   if (act && t < npos) sm.w[t] = e / sm.red[2];
-  __syncthreads();
+  lds_barrier();
   float acc = 0.0f;
   if (wv == 0) {
 #pragma unroll 16
@@ -521,7 +537,7 @@ template <int K>
 __device__ __forceinline__ void q8_load_row(i4 (&wc)[(K + 1023) / 1024], float& swl, const int8_t* codes,
                                             const float* scales, int r) {
   constexpr int NCH = (K + 1023) / 1024, G = K / 64;
-  const int lane = lane_id();
+  const int lane = lane_id_fresh();
   const int8_t* row = codes + (size_t)r * K;
   // every lane loads (lanes past the row re-read its last 16 bytes), so callers can
   // keep an identical memory-instruction stream on every path

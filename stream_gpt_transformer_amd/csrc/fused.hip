@@ -4,32 +4,34 @@
 //
 // Why one launch: a step is a chain of ~60 dependent phases over ~495 MB (fp32) or
 // ~137 MB (int8) of weights; a kernel launch per phase costs ~1.7-2.5 us on MI355X,
-// more than most phases' own HBM time.  Here every compute wave holds the weights
-// of its share of block l+1 in registers while block l runs, so the weight stream
-// is decoupled from the chain of exchanges between workgroups.
+// more than most phases' own HBM time.
 //
-// Placement: the eight XCDs are used like eight tensor-parallel devices, each with
-// its own L2.  Workgroup b runs on XCD b % 8 (the dispatcher deals workgroups
-// round-robin over the XCDs; every launch checks it) with rank b / 8 in it.  XCD X
-// owns heads X and X + 8 (when below 12), the FC rows 384X..384X+383 and the
-// matching 384-input slice of the MLP projection.  Ranks 0 and 1 run the
-// attention of the XCD's heads (K/V rows staged in LDS); ranks 2..31 compute:
-//  - inside the XCD (through its L2: plain stores, non-temporal polls) travel the
-//    q/k/v and attention outputs of its heads, its GELU slice, and the
-//    all-gathers of x1 and x2;
-//  - the two sums over all XCDs of a block are reduce-scatters through device
-//    memory: the XCDs publish terms (output projection: one per head; MLP
-//    projection: one per slice for fp32, one per 64-group for int8), every
-//    workgroup polls the terms of its 24 outputs, adds them in fixed order plus
-//    bias and residual, and writes the 24 values into its XCD's copy of x1/x2.
-// Each block thus has two exchanges across XCDs and five inside one.
+// Why two sets of compute units: an exchange between workgroups is a store and a
+// poll.  On MI355X a poll from a compute unit that also has HBM loads in flight
+// queues behind them (an XCD-local exchange goes from ~0.65 us to ~2.2 us), while
+// streaming on other compute units of the same XCD does not slow it.  So the 32
+// compute units of each XCD form two sets that alternate by block: set s = rank & 1
+// computes blocks s, s+2, ..., and while it computes block l (polls, dot products,
+// publishes: no HBM traffic but the key/value row of the new token) the other set
+// loads the weights of block l+1 into its registers (and the head's key/value rows
+// into LDS).  A unit loads the weights of its next block only after its last
+// exchange of the current one.
 //
-// Waves of a compute workgroup: wave 0 receives (polls, reduce-scatters,
-// all-gathers, the int8 LayerNorm) and stages the next block's LayerNorm
-// parameters while it waits; waves 1..7 compute.  Compute wave c of an XCD's 210
-// owns at most two units of every phase (QKV rows, head-group dots of the output
-// projection, FC rows, slice dots of the MLP projection) and holds their weights
-// in registers.
+// Placement (Megatron-style over the XCDs, inside each set): workgroup b runs on
+// XCD X = b % 8 (the dispatcher deals workgroups round-robin over the XCDs; every
+// launch checks it) with rank b / 8; set rank q = rank / 2.  XCD X owns heads X and
+// X + 8 (when below 12), FC rows 384X..384X+383 and the matching 384-input slice of
+// the MLP projection.  In each set, units q < (heads of X) are head units: the
+// attention of head X + 8q with its keys/values in LDS and that head's
+// output-projection terms (weights in registers); the others are regular units:
+// QKV rows of the XCD's heads, FC rows of the slice and the slice's MLP-projection
+// partials (weights in registers of waves 1..7).  Every unit of the set owns 48
+// outputs of the two reductions over XCDs (reduce-scatters through device memory).
+// Per block: x (all-gather in the XCD) -> LayerNorm, QKV rows -> head unit (XCD
+// local) -> attention, output-projection terms (global) -> reduce-scatter x1 ->
+// all-gather x1 -> LayerNorm, FC rows, GELU -> all-gather of the GELU slice -> MLP
+// partials (global) -> reduce-scatter by the other set, which computes the next
+// block: two exchanges across XCDs and four inside one per block.
 //
 // Exchange words are (epoch << 32 | value bits), stored with one 64-bit store, so
 // a poll that sees this launch's epoch sees the value: no flags, no fences.  The
@@ -54,28 +56,49 @@ namespace g2 {
 
 typedef unsigned long long u64;
 
-constexpr int FT = 512;               // threads per workgroup
-constexpr int NX = FX_NXCC;           // XCDs
-constexpr int NR = 32;                // workgroups per XCD
-constexpr int GRID = NX * NR;         // 256 = compute units of an MI355X
-constexpr int NCW = 7;                // compute waves per workgroup (waves 1..7)
-constexpr int CR0 = 2;                // first compute rank
-constexpr int CW = (NR - CR0) * NCW;  // compute waves per XCD (210: at most two units per phase)
-constexpr int RSN = D / NR;           // outputs per workgroup in a reduce-scatter
-constexpr int GS = F / NX;            // GELU slice of an XCD
-constexpr int GPS = GS / 64;          // groups per slice
-constexpr int NG_PR = F / 64;         // int8 MLP-projection groups
-constexpr int HEAD_MAX_ROWS = (V + NCW * GRID - 1) / (NCW * GRID);
+constexpr int FT = 512;                  // threads per workgroup
+constexpr int NWV = FT / 64;             // waves per workgroup
+constexpr int NX = FX_NXCC;              // XCDs
+constexpr int NR = 32;                   // workgroups per XCD
+constexpr int GRID = NX * NR;            // 256 = compute units of an MI355X
+constexpr int NQ = NR / 2;               // units of one set in one XCD
+constexpr int RSN = D / NQ;              // reduce-scatter outputs per unit (48)
+constexpr int GS = F / NX;               // FC slice of an XCD (384)
+constexpr int GPS = GS / 64;             // groups per slice (6)
+constexpr int NG_PR = F / 64;            // int8 MLP-projection groups (48)
+constexpr int NCW = NWV - 1;             // compute waves of a regular unit (waves 1..7)
+constexpr int UPW = 4;                   // units per compute wave per phase
+template <bool Q8>
+constexpr int nhs() { return Q8 ? 12 : 8; }  // head-row slots per wave
+constexpr int HEAD_STRIDE = NWV * GRID;  // head rows hw, hw + 2048, ...
+constexpr int HEAD_MAX_ROWS = (V + HEAD_STRIDE - 1) / HEAD_STRIDE;
+#ifndef FUSED_DELAY
+#define FUSED_DELAY 0
+#endif
+#ifndef FUSED_MASKED
+#define FUSED_MASKED 0
+#endif
+// lanes that store a value every lane of the group holds: one per group, or all
+__device__ __forceinline__ bool store_lane(int group) { return !FUSED_MASKED || (lane_id() % group) == 0; }
+// Output projection of a head unit: 768 outputs x 64 inputs as 1536 half dots of
+// 32 inputs, three per thread.
+constexpr int O_HALF_PER_THREAD = 2 * D / FT;
+static_assert(O_HALF_PER_THREAD * FT == 2 * D, "half dots per thread");
 constexpr unsigned SPIN_LIMIT = 1u << 21;
-static_assert(RSN * NR == D && GS * NX == F && GPS == PR_SLICE_GROUPS && NX == PR_SLICES, "slices");
+static_assert(RSN * NQ == D && GS * NX == F && GPS == PR_SLICE_GROUPS && NX == PR_SLICES, "slices");
 static_assert(H > NX && H <= 2 * NX, "one or two heads per XCD");
+// compute waves of a set in one XCD: 7 * (16 - heads) >= 98
+static_assert(UPW * NCW * (NQ - 2) >= 2 * 192 && UPW * NCW * (NQ - 2) >= GS && UPW * NCW * (NQ - 2) >= D / 2 &&
+                  UPW * NCW * (NQ - 2) >= GPS * D / 16,
+              "units per phase");
+static_assert(HEAD_MAX_ROWS > nhs<true>() && HEAD_MAX_ROWS > nhs<false>(), "head ring");
 
 __device__ __forceinline__ int heads_of(int X) { return X + NX < H ? 2 : 1; }
 
 // Exchange area (64-bit words): local [NX][L][FX_LOC_PER_LAYER], global
-// [L][FX_GLB_PER_LAYER], placement [GRID].
-constexpr int LO_QKV = 0, LO_ATT = 384, LO_X1 = 512, LO_G = 512 + D, LO_X2 = 512 + D + GS;
-static_assert(LO_X2 + D == FX_LOC_PER_LAYER, "local layout");
+// [L][FX_GLB_PER_LAYER], placement [GRID], sink lines [GRID*8][16].
+constexpr int LO_QKV = 0, LO_X1 = 384, LO_G = LO_X1 + D, LO_X2 = LO_G + GS;
+static_assert(LO_X2 + D <= FX_LOC_PER_LAYER, "local layout");
 constexpr int GL_O = 0, GL_P = H * D;  // output-projection terms [12][768]; MLP terms [8 or 48][768]
 static_assert(GL_P + NG_PR * D == FX_GLB_PER_LAYER, "global layout");
 constexpr size_t LOC_WORDS = (size_t)NX * L * FX_LOC_PER_LAYER;
@@ -98,15 +121,23 @@ struct FusedArgs {
   int32_t pos;
 };
 
-// Timeline test hook.  Compute workgroups: 0 start; 1+4l block l input ready;
-// 2+4l attention output received; 3+4l x1 gathered; 4+4l GELU slice gathered;
-// 49 head input ready; 50 head rows done; 51 end; block 5 only: 52 LayerNorm 1
-// done, 53/54/56/57 QKV/O/FC/MLP units published (wave 1), 55/58 the two
-// reduce-scatters done.  Attention workgroups: 1+4l
-// q/k/v received; 2+4l attention output published; 3+4l and 4+4l the two
-// reduce-scatters done.
+// Timeline test hook (100 MHz wall clock), per workgroup: 0 start; for block l
+// computed by the workgroup's set, 1+4l block input ready (head units: after their
+// reduce-scatter), 2+4l QKV rows published (regular, wave 1) / attention output
+// ready (head units), 3+4l x1 ready (after the all-gather; head units: their
+// reduce-scatter), 4+4l GELU slice gathered; 49 head input ready; 50 head rows
+// done; 51 end.
 __device__ __forceinline__ void stamp(const uint64_t* trace, int slot) {
   if (trace) ((uint64_t*)trace)[blockIdx.x * 64 + slot] = __builtin_amdgcn_s_memrealtime();
+}
+// Detail stamps 52..63 inside block 6 (set 0): regular wave 0: 52 own share of the
+// reduce-scatter polled, 53 terms of all waves in LDS, 54 x published, 56 x1
+// published; regular wave 1: 59 after the QKV barrier, 60 LayerNorm done, 62 MLP
+// phase start, 63 MLP partials published; head wave 0: 52 terms in LDS, 53 x
+// published, 54 q/k/v received, 56 output-projection terms published.
+constexpr int DETAIL_L = 6;
+__device__ __forceinline__ void dstamp(const uint64_t* trace, int l, int slot) {
+  if (l == DETAIL_L && lane_id() == 0) stamp(trace, slot);
 }
 
 __device__ __forceinline__ u64 ld_sc1(const u64* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
@@ -178,16 +209,15 @@ __device__ __forceinline__ void gather(const u64* src, uint32_t E, float* dst, u
   for (int j = 0; j < PL; ++j) dst[lane_id() + 64 * j] = v[j];
 }
 
-// Reduce-scatter: the workgroup's outputs o = RSN*rank + i (i < RSN) of a sum of
-// NT terms stored term-major at terms[t*D + o].  Lanes i < RSN return
+// Reduce-scatter: the unit's outputs o = RSN*q + i (i < RSN) of a sum of NT terms
+// stored term-major at terms[t*D + o].  Lanes i < RSN return
 // y = 0 + term_0 + ... + term_{NT-1} (fixed order).
 template <int NT>
-__device__ __forceinline__ float reduce_scatter(const u64* terms, int rank, uint32_t E, float* scratch,
-                                                uint32_t* hdr) {
+__device__ __forceinline__ float reduce_scatter(const u64* terms, int q, uint32_t E, float* scratch, uint32_t* hdr) {
   constexpr int N = NT * RSN, PL = (N + 63) / 64;
   const int lane = lane_id();
   float v[PL];
-  poll<PL, false>(terms, N, [&](int k) { return (k / RSN) * D + RSN * rank + k % RSN; }, E, v, hdr);
+  poll<PL, false>(terms, N, [&](int k) { return (k / RSN) * D + RSN * q + k % RSN; }, E, v, hdr);
 #pragma unroll
   for (int j = 0; j < PL; ++j)
     if (lane + 64 * j < N) scratch[lane + 64 * j] = v[j];
@@ -200,33 +230,57 @@ __device__ __forceinline__ float reduce_scatter(const u64* terms, int rank, uint
   return y;
 }
 
+// Cooperative poll of a reduce-scatter's NT*RSN terms (NT terms of the unit's RSN
+// outputs, term-major at terms[t*D + o]): wave w polls its share into
+// scratch[t*RSN + i]; after a workgroup barrier rs_sum adds them.
+template <int NT>
+__device__ __forceinline__ void rs_poll_part(const u64* terms, int q, uint32_t E, float* scratch, uint32_t* hdr,
+                                             int wave) {
+  constexpr int N = NT * RSN, PER = (N + NWV - 1) / NWV, PL = (PER + 63) / 64;
+  const int lane = lane_id();
+  const int k0 = wave * PER, n = min(PER, N - k0);
+  float v[PL];
+  poll<PL, false>(terms, n, [&](int k) { k += k0; return (k / RSN) * D + RSN * q + k % RSN; }, E, v, hdr);
+#pragma unroll
+  for (int j = 0; j < PL; ++j)
+    if (lane + 64 * j < n) scratch[k0 + lane + 64 * j] = v[j];
+}
+template <int NT>
+__device__ __forceinline__ float rs_sum(const float* scratch) {
+  const int lane = lane_id();
+  float y = 0.0f;
+  if (lane < RSN) {
+#pragma unroll 8
+    for (int t = 0; t < NT; ++t) y = y + scratch[t * RSN + lane];
+  }
+  return y;
+}
+
 // ---- per-wave weight registers ----------------------------------------------
-// fp32 (float4 slots): QKV rows k=0,1 -> 3k..3k+2; output-projection quad units
-// k=0,1 -> 6+k; FC rows k=0,1 -> 8+3k..; MLP row pairs k=0,1 -> 14+3k..16+3k.
-// The head uses the six row triples: head slot s at hbase(s) = 0,3,8,11,14,17.
-// int8 (int4 slots): QKV rows 0,1; output-projection units 2; FC rows 3,4; MLP
-// units 5,6; head slot s = slot s (7 rows in flight).  sc[] is the lane's weight
-// scale for its slot.
+// Regular units, fp32 (float4 slots): QKV rows k < 4 -> 3k..3k+2; FC rows k < 4 ->
+// 12+3k..; the MLP row pairs are in LDS (PrLds).  Head units: output-projection
+// half dot k < 3 -> slots 8k..8k+7.  Head rows (after the last block): slot triple
+// s -> 3s.
+// int8 (int4 slots): QKV rows 0..3, FC rows 4..7, MLP units 8..11; head units:
+// output-projection half dot k -> slots 2k, 2k+1 and scale sc[k]; head rows: slot s.  sc[] is the lane's weight scale
+// for its slot.
 //
-// Every compute wave issues the same sequence of memory instructions on every
-// path: units a wave does not own load a valid row in their place and store to a
-// sink word, and the last block loads the first head rows into the slots it frees
-// (instead of the next block's weights).  So the compiler's wait counts stay exact
-// and a wait for one phase's weights never drains the loads behind it.
+// Units a wave does not own load a valid row in their place and store to a sink
+// word, so every wave of a role issues the same memory-instruction stream and the
+// compiler's wait counts stay exact.
 template <bool Q8>
 struct WRegs;
 template <>
 struct WRegs<false> {
-  f4 r[20];
-  float b[4];  // bias of QKV rows 0,1, FC rows 0,1
+  f4 r[24];
+  float b[8];  // bias of QKV rows 0..3, FC rows 0..3
 };
 template <>
 struct WRegs<true> {
-  i4 c[7];
-  float sc[7];
-  float b[4];
+  i4 c[12];
+  float sc[12];
+  float b[8];
 };
-__device__ __host__ constexpr int hbase(int s) { return s < 2 ? 3 * s : 8 + 3 * (s - 2); }
 
 // QKV row n of XCD X (n < 192 per head): head hh = n/192, part (q,k,v) = n%192/64,
 // coordinate n%64.
@@ -235,139 +289,141 @@ __device__ __forceinline__ int qkv_row(int X, int n) {
   return part * D + DH * (X + NX * hh) + d;
 }
 
-// Where a wave's units and head rows are; unit indexes are clamped to valid units.
+// Where a regular compute wave's units are; unit indexes are clamped to valid units.
 struct Units {
-  int X, cw, nh;  // XCD, compute wave of the XCD, heads of the XCD
-  int hw, hstride;
-  __device__ int head_row(int s) const { return min(hw + s * hstride, V - 1); }
+  int X, cw, cwn, nh;  // XCD, compute wave of the XCD's set, compute waves of the set, heads of the XCD
+  __device__ int qkv(int k) const { return cw + cwn * k; }
 };
 
 __device__ __forceinline__ void ld_row3(f4* dst, const float* row) {
-  const int lane = lane_id();
+  const int lane = lane_id_fresh();
 #pragma unroll
   for (int i = 0; i < 3; ++i) dst[i] = __builtin_nontemporal_load((const f4*)(row + 256 * i + 4 * lane));
 }
 
-// Block l's QKV row k into its slots, or (head) head slot k.
-template <bool Q8, int k>
-__device__ __forceinline__ void load_qkv(WRegs<Q8>& R, const Weights& w, int l, const Units& U, bool head) {
-  const int r = qkv_row(U.X, min(U.cw + CW * k, 192 * U.nh - 1));
-  const int hr = U.head_row(k);
-  if constexpr (!Q8) {
-    ld_row3(&R.r[hbase(k)], head ? w.wte + (size_t)hr * D : f32_mat(w, l, M_QKV) + (size_t)r * D);
-  } else {
-    i4 t[1];
-    q8_load_row<D>(t, R.sc[k], head ? q8_codes(w, 0, M_HEAD) : q8_codes(w, l, M_QKV),
-                   head ? q8_scales(w, 0, M_HEAD) : q8_scales(w, l, M_QKV), head ? hr : r);
-    R.c[k] = t[0];
-  }
-  R.b[k] = small_p(w, l, sp::B_QKV)[r];
-}
-
-// Output projection.  fp32: quad unit u (< 192 per head) = outputs 4(u%192)+q of
-// head hh = u/192 in quarter q; lane 16q+j holds inputs 4j..4j+3 of the head.
-// int8: unit n = 16u + lane/4 (< 768 per head): output n%768 of head n/768; quad
-// member s holds codes 16s..16s+15 of the head group.  (fp32 at the last block
-// reloads its units; int8 loads head slot 2.)
-__device__ __forceinline__ void o_unit_f32(const Units& U, int k, int& u, int& hh, int& i, int& h) {
-  u = min(U.cw + CW * k, 192 * U.nh - 1);
-  hh = u / 192;
-  i = 4 * (u % 192) + lane_id() / 16;
-  h = U.X + NX * hh;
-}
-__device__ __forceinline__ void o_unit_q8(const Units& U, int& n, int& i, int& h) {
-  const int u = min(U.cw, 48 * U.nh - 1);
-  n = 16 * u + lane_id() / 4;
-  i = n % D;
-  h = U.X + NX * (n / D);
-}
-template <bool Q8, int k>
-__device__ __forceinline__ void load_o(WRegs<Q8>& R, const Weights& w, int l, const Units& U, bool head) {
-  const int lane = lane_id();
-  if constexpr (!Q8) {
-    int u, hh, i, h;
-    o_unit_f32(U, k, u, hh, i, h);
-    R.r[6 + k] = __builtin_nontemporal_load(
-        (const f4*)(f32_mat(w, l, M_O) + (size_t)i * D + DH * h + 4 * (lane % 16)));
-  } else {
-    const int hr = U.head_row(2);
-    int n, i, h;
-    o_unit_q8(U, n, i, h);
-    const int8_t* p = head ? q8_codes(w, 0, M_HEAD) + (size_t)hr * D + 16 * min(lane, D / 16 - 1)
-                           : q8_codes(w, l, M_O) + (size_t)i * D + DH * h + 16 * (lane % 4);
-    const float* sp_ = head ? q8_scales(w, 0, M_HEAD) + (size_t)hr * H + min(lane, H - 1)
-                            : q8_scales(w, l, M_O) + (size_t)i * H + h;
-    const i4 c = __builtin_nontemporal_load((const i4*)p);
-    const float sc = *sp_;
-    R.c[2] = (!head || lane < D / 16) ? c : i4{0, 0, 0, 0};
-    R.sc[2] = (!head || lane < H) ? sc : 0.0f;
-  }
-}
-
-// FC row k of the XCD's slice, or head slot 2+k (fp32) / 3+k (int8).
-template <bool Q8, int k>
-__device__ __forceinline__ void load_fc(WRegs<Q8>& R, const Weights& w, int l, const Units& U, bool head) {
-  const int r = GS * U.X + min(U.cw + CW * k, GS - 1);
-  if constexpr (!Q8) {
-    const int hr = U.head_row(2 + k);
-    ld_row3(&R.r[hbase(2 + k)], head ? w.wte + (size_t)hr * D : f32_mat(w, l, M_FC) + (size_t)r * D);
-  } else {
-    const int hr = U.head_row(3 + k);
-    i4 t[1];
-    q8_load_row<D>(t, R.sc[3 + k], head ? q8_codes(w, 0, M_HEAD) : q8_codes(w, l, M_FC),
-                   head ? q8_scales(w, 0, M_HEAD) : q8_scales(w, l, M_FC), head ? hr : r);
-    R.c[3 + k] = t[0];
-  }
-  R.b[2 + k] = small_p(w, l, sp::B_FC)[r];
-}
-
-// MLP projection.  fp32: row pair u (< 384) = rows 2u, 2u+1 over the XCD's slice;
-// pass p, quarter q takes group dot kk = 4p+q: row 2u + kk/6, slice group kk%6.
-// int8: unit n = 16u + lane/4 (< 6*768): output n/6, group 6X + n%6.  Head
-// alternative: fp32 head slot 4+k, int8 head slot 5+k.
-template <bool Q8, int k>
-__device__ __forceinline__ void load_pr(WRegs<Q8>& R, const Weights& w, int l, const Units& U, bool head) {
-  const int lane = lane_id();
-  if constexpr (!Q8) {
-    const int hr = U.head_row(4 + k);
-    const int u = min(U.cw + CW * k, D / 2 - 1);
-    const float* W = f32_mat(w, l, M_PR);
-    const int q = lane / 16, j = lane % 16;
-#pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      const int kk = 4 * p + q, row = 2 * u + kk / GPS, g = GPS * U.X + kk % GPS;
-      const float* src = head ? w.wte + (size_t)hr * D + 256 * p + 4 * lane : W + (size_t)row * F + 64 * g + 4 * j;
-      R.r[hbase(4 + k) + p] = __builtin_nontemporal_load((const f4*)src);
-    }
-  } else {
-    const int hr = U.head_row(5 + k);
-    const int u = min(U.cw + CW * k, GPS * D / 16 - 1);
-    const int n = 16 * u + lane / 4, i = n / GPS, g = GPS * U.X + n % GPS;
-    const int8_t* p = head ? q8_codes(w, 0, M_HEAD) + (size_t)hr * D + 16 * min(lane, D / 16 - 1)
-                           : q8_codes(w, l, M_PR) + (size_t)i * F + 64 * g + 16 * (lane % 4);
-    const float* sp_ = head ? q8_scales(w, 0, M_HEAD) + (size_t)hr * H + min(lane, H - 1)
-                            : q8_scales(w, l, M_PR) + (size_t)i * NG_PR + g;
-    const i4 c = __builtin_nontemporal_load((const i4*)p);
-    const float sc = *sp_;
-    R.c[5 + k] = (!head || lane < D / 16) ? c : i4{0, 0, 0, 0};
-    R.sc[5 + k] = (!head || lane < H) ? sc : 0.0f;
-  }
-}
-
 template <bool Q8>
-constexpr int head_slots() { return Q8 ? 7 : 6; }
+__device__ __forceinline__ void load_row768(WRegs<Q8>& R, int slot, const Weights& w, int l, int m, int r) {
+  if constexpr (!Q8) {
+    ld_row3(&R.r[3 * slot], f32_mat(w, l, m) + (size_t)r * D);
+  } else {
+    i4 t[1];
+    q8_load_row<D>(t, R.sc[slot], q8_codes(w, l, m), q8_scales(w, l, m), r);
+    R.c[slot] = t[0];
+  }
+}
+
+// fp32 MLP-projection weights of a regular unit in LDS: [wave 1..7][unit k < 4]
+// [pass p < 3] one float4 per lane, written by direct global-to-LDS loads.
+struct PrLds {
+  f4 w[NCW][UPW][3][64];
+};
+static_assert(sizeof(PrLds) >= (size_t)FT * 128, "head units stage their output-projection rows in this space");
+__device__ __forceinline__ const f4& pr_w(const PrLds& P, int wave, int k, int p) {
+  return P.w[wave - 1][k][p][lane_id()];
+}
+
+// All units of a regular compute wave for block l.
+template <bool Q8>
+__device__ __forceinline__ void load_block(WRegs<Q8>& R, PrLds& P, const Weights& w, int l, const Units& U,
+                                           int wave) {
+  const int lane = lane_id_fresh();
+#pragma unroll
+  for (int k = 0; k < UPW; ++k) {
+    const int r = qkv_row(U.X, min(U.qkv(k), 192 * U.nh - 1));
+    load_row768<Q8>(R, k, w, l, M_QKV, r);
+    R.b[k] = small_p(w, l, sp::B_QKV)[r];
+  }
+#pragma unroll
+  for (int k = 0; k < UPW; ++k) {
+    const int r = GS * U.X + min(U.cw + U.cwn * k, GS - 1);
+    load_row768<Q8>(R, UPW + k, w, l, M_FC, r);
+    R.b[UPW + k] = small_p(w, l, sp::B_FC)[r];
+  }
+  // MLP projection.  fp32: row pair u (< 384) = rows 2u, 2u+1 over the XCD's slice;
+  // pass p, quarter qq takes group dot kk = 4p+qq: row 2u + kk/6, slice group kk%6.
+  // int8: unit n = 16u + lane/4 (< 6*768): output n/6, group 6X + n%6.
+#pragma unroll
+  for (int k = 0; k < UPW; ++k) {
+    if constexpr (!Q8) {
+      const int u = min(U.cw + U.cwn * k, D / 2 - 1);
+      const float* W = f32_mat(w, l, M_PR);
+      const int qq = lane / 16, j = lane % 16;
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        const int kk = 4 * p + qq, row = 2 * u + kk / GPS, g = GPS * U.X + kk % GPS;
+        __builtin_amdgcn_global_load_lds((const void*)(W + (size_t)row * F + 64 * g + 4 * j),
+                                         (__attribute__((address_space(3))) void*)&P.w[wave - 1][k][p][0], 16, 0, 0);
+      }
+    } else {
+      const int u = min(U.cw + U.cwn * k, GPS * D / 16 - 1);
+      const int n = 16 * u + lane / 4, i = n / GPS, g = GPS * U.X + n % GPS;
+      R.c[2 * UPW + k] = __builtin_nontemporal_load((const i4*)(q8_codes(w, l, M_PR) + (size_t)i * F + 64 * g + 16 * (lane % 4)));
+      R.sc[2 * UPW + k] = q8_scales(w, l, M_PR)[(size_t)i * NG_PR + g];
+    }
+  }
+}
+
+// Output projection of head h on a head unit.  Thread t holds half dots
+// hd = t + 512k (k < 3): output i = hd/2, inputs 64h + 32(hd%2) + 0..31 of the
+// head, i.e. the two halves of an output sit in adjacent lanes.  fp32: f4 slots
+// 8k..8k+7; int8: i4 slots 2k, 2k+1 and the output's group scale sc[k].
+// Loading: for each k the 256 rows' 64 head columns are copied into LDS with
+// coalesced direct loads (rows are contiguous 256 / 64-byte segments), then each
+// thread reads its 128 / 32 contiguous bytes from there (a thread's half dot is
+// one row segment, which a per-lane global load would fetch as scattered 16-byte
+// pieces).  Uses `stage` (>= 64 KB of LDS) as scratch; every thread must call it.
+__device__ __forceinline__ int o_half(int k) { return (int)threadIdx.x + FT * k; }
+template <bool Q8>
+__device__ __forceinline__ void load_o_head(WRegs<Q8>& R, char* stage, const Weights& w, int l, int h) {
+  constexpr int SEG = Q8 ? 32 : 128;              // bytes of one half dot
+  constexpr int CHUNK = (FT / 2) * 2 * SEG;       // 256 rows x 64 columns
+  constexpr int ITERS = CHUNK / (FT * 16);
+  static_assert(ITERS * FT * 16 == CHUNK, "chunk");
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int lane = lane_id_fresh();
+  const char* base = Q8 ? (const char*)q8_codes(w, l, M_O) : (const char*)f32_mat(w, l, M_O);
+  constexpr int ELEM = Q8 ? 1 : 4;
+#pragma unroll
+  for (int k = 0; k < O_HALF_PER_THREAD; ++k) {
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int off0 = (it * FT + wave * 64) * 16;  // wave-uniform LDS byte offset
+      const int off = off0 + lane * 16;
+      const int row = (FT / 2) * k + off / (2 * SEG), colb = off % (2 * SEG);
+      __builtin_amdgcn_global_load_lds((const void*)(base + ((size_t)row * D + DH * h) * ELEM + colb),
+                                       (__attribute__((address_space(3))) void*)(stage + off0), 16, 0, 0);
+    }
+    __syncthreads();  // every wave's copies have landed
+    const char* mine = stage + (size_t)threadIdx.x * SEG;
+    if constexpr (!Q8) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) R.r[8 * k + j] = *(const f4*)(mine + 16 * j);
+    } else {
+      R.c[2 * k] = *(const i4*)mine;
+      R.c[2 * k + 1] = *(const i4*)(mine + 16);
+      const int i = o_half(k) >> 1;
+      R.sc[k] = q8_scales(w, l, M_O)[(size_t)i * H + h];
+    }
+    __syncthreads();  // the stage is free again
+  }
+}
 
 // Head row r (clamped to the last row) into head slot s.
 template <bool Q8>
 __device__ __forceinline__ void load_head(WRegs<Q8>& R, const Weights& w, int s, int r) {
   r = min(r, V - 1);
   if constexpr (!Q8) {
-    ld_row3(&R.r[hbase(s)], w.wte + (size_t)r * D);
+    ld_row3(&R.r[3 * s], w.wte + (size_t)r * D);
   } else {
     i4 t[1];
     q8_load_row<D>(t, R.sc[s], q8_codes(w, 0, M_HEAD), q8_scales(w, 0, M_HEAD), r);
     R.c[s] = t[0];
   }
+}
+template <bool Q8>
+__device__ __forceinline__ void load_head_slots(WRegs<Q8>& R, const Weights& w, int hw) {
+#pragma unroll
+  for (int s = 0; s < nhs<Q8>(); ++s) load_head<Q8>(R, w, s, hw + s * HEAD_STRIDE);
 }
 
 // int8 group accumulator of a quad: lanes 4k..4k+3 each hold 16 codes of one group.
@@ -381,24 +437,31 @@ __device__ __forceinline__ int quad_acc(const i4 wc, const i4 xc) {
 }
 
 struct FusedSmem {
-  float xs[D];         // block input x, then x1 (all-gathers)
-  float xn[D];         // int8 path: LayerNorm output
-  float lntmp[D];      // int8 path: LayerNorm scratch
-  float att[2 * DH];   // attention output of the XCD's heads
-  float xg[GS];        // the XCD's GELU slice
+  float xs[D];          // block input x (all-gather), x12 for the head
+  float x1s[D];         // x1 (all-gather; a buffer of its own: waves 1..7 may still read xs)
+  float xn[D];          // int8 path: LayerNorm output
+  float lntmp[D];       // int8 path: LayerNorm scratch
+  float att[DH];        // attention output of a head unit
+  float xg[GS];         // the XCD's GELU slice
   float rs[NG_PR * RSN];  // reduce-scatter terms
-  float lnp[2][4][D];  // LayerNorm parameters by block parity: ln1 gamma, beta, ln2 gamma, beta
-  float lnf[2][D];     // final LayerNorm gamma, beta
-  int8_t xc[F];        // int8 path: input codes (by input index)
-  float xsc[64];       // int8 path: input scales (by group)
-  AttnSmem at;         // attention workgroups
+  float lnp[4][D];      // LayerNorm parameters of the unit's next block: ln1 gamma, beta, ln2 gamma, beta
+  float lnf[2][D];      // final LayerNorm gamma, beta
+  int8_t xc[F];         // int8 path: input codes (by input index)
+  float xsc[64];        // int8 path: input scales (by group)
+  union {
+    AttnSmem at;        // head units
+    PrLds pr;           // regular units, fp32
+  };
 };
 
 // Per-workgroup constants.
 struct Ctx {
   uint32_t E;  // this launch's epoch
   int X;       // XCD
-  int rank;    // rank inside the XCD
+  int set;     // 0: blocks 0, 2, ...; 1: blocks 1, 3, ...
+  int q;       // rank inside the XCD's set
+  int nh;      // heads of the XCD
+  bool head;   // head unit (q < nh): head X + 8q
   u64* loc;    // this XCD's local words, block 0
   u64* glb;    // global words, block 0
 };
@@ -415,50 +478,64 @@ __device__ __forceinline__ void stage_vec(float* dst, const float* src) {
   for (int i = 0; i < 3; ++i) *(f4*)(dst + 256 * i + 4 * lane) = v[i];
 }
 __device__ __forceinline__ void stage_ln(FusedSmem& S, const Weights& w, int l) {
-  float(*p)[D] = S.lnp[l & 1];
-  stage_vec(p[0], small_p(w, l, sp::LN1_G));
-  stage_vec(p[1], small_p(w, l, sp::LN1_B));
-  stage_vec(p[2], small_p(w, l, sp::LN2_G));
-  stage_vec(p[3], small_p(w, l, sp::LN2_B));
+  stage_vec(S.lnp[0], small_p(w, l, sp::LN1_G));
+  stage_vec(S.lnp[1], small_p(w, l, sp::LN1_B));
+  stage_vec(S.lnp[2], small_p(w, l, sp::LN2_G));
+  stage_vec(S.lnp[3], small_p(w, l, sp::LN2_B));
 }
 
-// x = wte[token] + wpe[pos] into LDS; lanes < RSN return element RSN*rank + lane.
-__device__ __forceinline__ float embed(const FusedArgs& a, float* xs, int rank) {
+// x = wte[token] + wpe[pos] into LDS (if xs) ; lanes < RSN return element RSN*q + lane.
+__device__ __forceinline__ float embed(const FusedArgs& a, float* xs, int q) {
   const int lane = lane_id();
+  if (xs) {
 #pragma unroll
-  for (int j = 0; j < 12; ++j) {
-    const int i = lane + 64 * j;
-    xs[i] = a.w.wte[(size_t)a.token * D + i] + a.w.wpe[(size_t)a.pos * D + i];
+    for (int j = 0; j < 12; ++j) {
+      const int i = lane + 64 * j;
+      xs[i] = a.w.wte[(size_t)a.token * D + i] + a.w.wpe[(size_t)a.pos * D + i];
+    }
   }
-  const int o = RSN * rank + min(lane, RSN - 1);
+  const int o = RSN * q + min(lane, RSN - 1);
   return a.w.wte[(size_t)a.token * D + o] + a.w.wpe[(size_t)a.pos * D + o];
 }
 
-// The two reduce-scatters of block l (wave 0 of every workgroup).  xr holds the
-// residual of this workgroup's outputs (lanes < RSN) and is updated.
-template <bool Q8, bool CAP>
-__device__ __forceinline__ void rs_o(const FusedArgs& a, FusedSmem& S, const Ctx& c, int l, float& xr) {
-  const int lane = lane_id();
-  float y = reduce_scatter<H>(glb_of(c, l) + GL_O, c.rank, c.E, S.rs, a.header);
-  if (lane < RSN) {
-    const int o = RSN * c.rank + lane;
-    y = y + small_p(a.w, l, sp::B_O)[o];
-    if (CAP && c.X == 0) ((float*)(a.capture + cap_offset(l, M_O) + cap_item(M_O).y))[o] = y;
-    xr = xr + y;
-    st_loc(loc_of(c, l) + LO_X1 + o, pack(xr, c.E));
-  }
+// Reduce-scatter of block l's MLP projection by a unit of the set that computes
+// block l+1: every wave polls its share of the terms (rs_pr_poll), then after a
+// workgroup barrier wave 0 forms x_{l+1}[o] = x1_l[o] + (sum + bias) and publishes
+// it into the XCD's copy (rs_pr).  Lanes < RSN return it.
+template <bool Q8>
+__device__ __forceinline__ void rs_pr_poll(const FusedArgs& a, FusedSmem& S, const Ctx& c, int l, int wave) {
+  rs_poll_part<Q8 ? NG_PR : NX>(glb_of(c, l) + GL_P, c.q, c.E, S.rs, a.header, wave);
 }
 template <bool Q8, bool CAP>
-__device__ __forceinline__ void rs_pr(const FusedArgs& a, FusedSmem& S, const Ctx& c, int l, float& xr) {
+__device__ __forceinline__ float rs_pr(const FusedArgs& a, FusedSmem& S, const Ctx& c, int l, float bpr) {
   const int lane = lane_id();
-  float y = reduce_scatter<Q8 ? NG_PR : NX>(glb_of(c, l) + GL_P, c.rank, c.E, S.rs, a.header);
+  float y = rs_sum<Q8 ? NG_PR : NX>(S.rs);
+  float x1[1];
+  poll<1, true>(loc_of(c, l) + LO_X1 + RSN * c.q, RSN, [](int k) { return k; }, c.E, x1, a.header);
+  float xr = 0.0f;
   if (lane < RSN) {
-    const int o = RSN * c.rank + lane;
-    y = y + small_p(a.w, l, sp::B_PR)[o];
+    const int o = RSN * c.q + lane;
+    y = y + bpr;
     if (CAP && c.X == 0) ((float*)(a.capture + cap_offset(l, M_PR) + cap_item(M_PR).y))[o] = y;
-    xr = xr + y;
+    xr = x1[0] + y;
     st_loc(loc_of(c, l) + LO_X2 + o, pack(xr, c.E));
   }
+  return xr;
+}
+// Reduce-scatter of block l's output projection: x1[o] = x[o] + (sum + bias).
+template <bool Q8, bool CAP>
+__device__ __forceinline__ float rs_o(const FusedArgs& a, FusedSmem& S, const Ctx& c, int l, float xr, float bo) {
+  const int lane = lane_id();
+  float y = reduce_scatter<H>(glb_of(c, l) + GL_O, c.q, c.E, S.rs, a.header);
+  float x1 = 0.0f;
+  if (lane < RSN) {
+    const int o = RSN * c.q + lane;
+    y = y + bo;
+    if (CAP && c.X == 0) ((float*)(a.capture + cap_offset(l, M_O) + cap_item(M_O).y))[o] = y;
+    x1 = xr + y;
+    st_loc(loc_of(c, l) + LO_X1 + o, pack(x1, c.E));
+  }
+  return x1;
 }
 
 // int8: quantize groups g0, g0+gstep, ... (< g1) of src (LDS, indexed from group
@@ -467,8 +544,8 @@ __device__ __forceinline__ void quantize_groups(FusedSmem& S, const float* src, 
   const int lane = lane_id();
   for (int g = g0 + (wave - 1); g < g1; g += NCW) {
     float s;
-    const int q = quant_lane(src[(g - gsrc0) * 64 + lane], s);
-    S.xc[g * 64 + lane] = (int8_t)q;
+    const int qv = quant_lane(src[(g - gsrc0) * 64 + lane], s);
+    S.xc[g * 64 + lane] = (int8_t)qv;
     if (lane == 0) S.xsc[g] = s;
   }
 }
@@ -486,267 +563,221 @@ __device__ __forceinline__ void capture_input(const FusedArgs& a, FusedSmem& S, 
   }
 }
 
-// ---- compute workgroups: wave 0 ---------------------------------------------------
+// ---- the tied head -------------------------------------------------------------
+// Head rows of wave hw (rows hw + k*HEAD_STRIDE): the first NS slots were loaded
+// ahead; each slot is refilled with the row NS further on as soon as it has been
+// used.  Rows past the vocabulary compute on the last row and store to the sink.
 template <bool Q8, bool CAP>
-__device__ void io_wave(const FusedArgs a, FusedSmem& S, const Ctx c) {
+__device__ __forceinline__ void head_rows(const FusedArgs a, FusedSmem& S, WRegs<Q8>& R, int hw, float* sinkf) {
   const int lane = lane_id();
-  uint32_t* hdr = a.header;
-  // the capture of LayerNorm-output inputs is written by one workgroup, that of the
-  // XCD's GELU slice by one workgroup per XCD
-  const bool cap0 = CAP && c.X == 0 && c.rank == CR0;
-  const bool capx = CAP && c.rank == CR0;
-  auto qbar = [&](int l, int m, bool cap) {  // int8: barrier after the compute waves quantized
-    if constexpr (Q8) {
-      wg_barrier();
-      if (cap) {
-        if (m == M_PR) capture_input(a, S, l, m, S.xg, GS * c.X, GS * (c.X + 1), lane, 64);
-        else capture_input(a, S, l, m, S.xn, 0, D, lane, 64);
-      }
-    }
-  };
-  stage_ln(S, a.w, 0);
-  stage_vec(S.lnf[0], a.w.small + sp::LNF_G);
-  stage_vec(S.lnf[1], a.w.small + sp::LNF_B);
-  float xr = embed(a, S.xs, c.rank);  // lanes < RSN: residual of this workgroup's reduce-scatter outputs
-  wg_barrier();  // B0: block 0's input and LayerNorm parameters are in LDS
-  for (int l = 0; l < L; ++l) {
-    const float(*lp)[D] = S.lnp[l & 1];
-    u64* loc = loc_of(c, l);
-    if (lane == 0) stamp(a.trace, 1 + 4 * l);
-    if constexpr (Q8) layernorm_seq(S.xs, lp[0], lp[1], S.xn, S.lntmp);
-    if (l == 5 && lane == 0) stamp(a.trace, 52);
-    wg_barrier();  // B1: QKV
-    qbar(l, M_QKV, cap0);
-    // while the XCD's attention runs: next block's LayerNorm parameters
-    if (l + 1 < L) stage_ln(S, a.w, l + 1);
-    {
-      float v[2];
-      poll<2, true>(loc + LO_ATT, DH * heads_of(c.X), [](int k) { return k; }, c.E, v, hdr);
-      S.att[lane] = v[0];
-      S.att[lane + 64] = v[1];
-      if (lane == 0) stamp(a.trace, 2 + 4 * l);
-    }
-    wg_barrier();  // B2: output projection
-    qbar(l, M_O, false);
-    rs_o<Q8, CAP>(a, S, c, l, xr);
-    if (l == 5 && lane == 0) stamp(a.trace, 55);
-    gather<12>(loc + LO_X1, c.E, S.xs, hdr);
-    if (lane == 0) stamp(a.trace, 3 + 4 * l);
-    if constexpr (Q8) layernorm_seq(S.xs, lp[2], lp[3], S.xn, S.lntmp);
-    wg_barrier();  // B3: FC
-    qbar(l, M_FC, cap0);
-    gather<GS / 64>(loc + LO_G, c.E, S.xg, hdr);
-    if (lane == 0) stamp(a.trace, 4 + 4 * l);
-    wg_barrier();  // B4: MLP projection
-    qbar(l, M_PR, capx);
-    rs_pr<Q8, CAP>(a, S, c, l, xr);
-    if (l == 5 && lane == 0) stamp(a.trace, 58);
-    gather<12>(loc + LO_X2, c.E, S.xs, hdr);
-  }
-  if (lane == 0) stamp(a.trace, 49);
-  if constexpr (Q8) layernorm_seq(S.xs, S.lnf[0], S.lnf[1], S.xn, S.lntmp);
-  wg_barrier();  // B5: head
-  qbar(0, M_HEAD, cap0);
-}
-
-// Head rows of wave hw (rows hw + k*hstride): slots were loaded ahead; each slot is
-// refilled with the row NS further on as soon as it has been used.  Rows past the
-// vocabulary compute on the last row and store to the sink.
-template <bool Q8, bool CAP>
-__device__ __forceinline__ void head_rows(const FusedArgs a, FusedSmem& S, WRegs<Q8>& R, int hw, int hstride) {
-  const int lane = lane_id();
+  constexpr int NS = nhs<Q8>();
   f4 x[3];
   if constexpr (!Q8) {
     load_frag<3>(x, S.xs);
     layernorm_frag(x, S.lnf[0], S.lnf[1]);
   }
-  constexpr int NS = head_slots<Q8>();
 #pragma unroll
   for (int k = 0; k < HEAD_MAX_ROWS; ++k) {
-    // keep the loads in slot order: at most NS rows in flight per wave
+    // keep the loads in slot order: at most NHS rows in flight per wave
     __builtin_amdgcn_sched_barrier(0);
-    const int r = hw + k * hstride;
+    const int r = hw + k * HEAD_STRIDE;
     const int s = k % NS;
     float y;
     if constexpr (!Q8) {
-      y = dot_frag<3>(*reinterpret_cast<f4(*)[3]>(&R.r[hbase(s)]), x);
+      y = dot_frag<3>(*reinterpret_cast<f4(*)[3]>(&R.r[3 * s]), x);
     } else {
       int32_t* ca = CAP && r < V ? (int32_t*)(a.capture + cap_offset(0, M_HEAD) + cap_item(M_HEAD).acc) + (size_t)r * 12
                                  : nullptr;
       y = q8_dot<D>(*reinterpret_cast<i4(*)[1]>(&R.c[s]), R.sc[s], S.xc, S.xsc, ca);
       if (CAP && r < V && lane == 0) ((float*)(a.capture + cap_offset(0, M_HEAD) + cap_item(M_HEAD).y))[r] = y;
     }
-    *(r < V ? a.logits + r : (float*)(a.sinkw + ((size_t)blockIdx.x * 8 + (threadIdx.x >> 6)) * 16 + 8)) = y;
-    load_head<Q8>(R, a.w, s, r + NS * hstride);
+    *(r < V ? a.logits + r : sinkf) = y;
+    if (k + NS < HEAD_MAX_ROWS) load_head<Q8>(R, a.w, s, r + NS * HEAD_STRIDE);
   }
 }
 
-// ---- compute workgroups: waves 1..7 -----------------------------------------------
+// ---- regular units -------------------------------------------------------------
+// Wave 0 receives (reduce-scatters, all-gathers, the int8 LayerNorm) and holds no
+// weights; waves 1..7 compute from registers (and the fp32 MLP weights from LDS).
+// The two roles meet at the same sequence of workgroup barriers.
 template <bool Q8, bool CAP>
-__device__ void compute_waves(const FusedArgs a, FusedSmem& S, const Ctx c) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int X = c.X;
-  Units U;
-  U.X = X;
-  U.cw = (wave - 1) * (NR - CR0) + (c.rank - CR0);  // compute wave of the XCD
-  U.nh = heads_of(X);
-  U.hw = (wave - 1) * GRID + (int)blockIdx.x;  // first head row
-  U.hstride = NCW * GRID;
-  const int cw = U.cw, nh = U.nh;
+__device__ void regular_io(const FusedArgs& a, FusedSmem& S, const Ctx& c) {
+  const int lane = lane_id();
+  uint32_t* hdr = a.header;
   const uint32_t E = c.E;
-  // this wave's own sink line (stores of different waves never meet)
+  const bool cap0 = CAP && c.X == 0 && c.q == c.nh;  // one regular unit captures LayerNorm-output inputs
+  const bool capx = CAP && c.q == c.nh;              // one per XCD captures its GELU slice
+  const int o = RSN * c.q + min(lane, RSN - 1);
+  const int l0 = c.set;
+  stage_ln(S, a.w, l0);
+  stage_vec(S.lnf[0], a.w.small + sp::LNF_G);
+  stage_vec(S.lnf[1], a.w.small + sp::LNF_B);
+  float bo = small_p(a.w, l0, sp::B_O)[o];
+  float bpr = l0 > 0 ? small_p(a.w, l0 - 1, sp::B_PR)[o] : 0.0f;
+  float xr;
+  wg_barrier();  // B0
+  for (int l = l0; l < L; l += 2) {
+    u64* loc = loc_of(c, l);
+    if (l > 0) rs_pr_poll<Q8>(a, S, c, l - 1, 0);
+    dstamp(a.trace, l, 52);
+    wg_barrier();  // BA: the reduce-scatter terms are in LDS
+    dstamp(a.trace, l, 53);
+    if (l == 0) {
+      xr = embed(a, S.xs, c.q);
+    } else {
+      xr = rs_pr<Q8, CAP>(a, S, c, l - 1, bpr);
+      dstamp(a.trace, l, 54);
+      gather<12>(loc_of(c, l - 1) + LO_X2, E, S.xs, hdr);
+    }
+    if (lane == 0) stamp(a.trace, 1 + 4 * l);
+    if constexpr (Q8) layernorm_seq(S.xs, S.lnp[0], S.lnp[1], S.xn, S.lntmp);
+    wg_barrier();  // B1: QKV
+    if constexpr (Q8) {
+      wg_barrier();  // codes ready
+      if (cap0) capture_input(a, S, l, M_QKV, S.xn, 0, D, lane, 64);
+    }
+    xr = rs_o<Q8, CAP>(a, S, c, l, xr, bo);
+    dstamp(a.trace, l, 56);
+    gather<12>(loc + LO_X1, E, S.x1s, hdr);
+    if (lane == 0) stamp(a.trace, 3 + 4 * l);
+    if constexpr (Q8) layernorm_seq(S.x1s, S.lnp[2], S.lnp[3], S.xn, S.lntmp);
+    wg_barrier();  // B3: FC
+    if constexpr (Q8) {
+      wg_barrier();
+      if (cap0) capture_input(a, S, l, M_FC, S.xn, 0, D, lane, 64);
+    }
+    gather<GS / 64>(loc + LO_G, E, S.xg, hdr);
+    if (lane == 0) stamp(a.trace, 4 + 4 * l);
+    wg_barrier();  // B4: MLP projection
+    if constexpr (Q8) {
+      wg_barrier();
+      if (capx) capture_input(a, S, l, M_PR, S.xg, GS * c.X, GS * (c.X + 1), lane, 64);
+    }
+    // the next block of this set: its LayerNorm parameters and reduce-scatter biases
+    const int ln = l + 2;
+    if (FUSED_DELAY && ln < L) {
+      float v[12];
+      poll<12, true>(loc + LO_X2, D, [](int k) { return k; }, E, v, hdr);
+      wg_barrier();  // BD
+    }
+    if (ln < L) {
+      stage_ln(S, a.w, ln);
+      bo = small_p(a.w, ln, sp::B_O)[o];
+    }
+    if (ln - 1 < L) bpr = small_p(a.w, ln - 1, sp::B_PR)[o];
+  }
+  // the tied head: set 0 reduces block 11's MLP projection, both gather x12
+  if (c.set == 0) rs_pr_poll<Q8>(a, S, c, L - 1, 0);
+  wg_barrier();  // BT
+  if (c.set == 0) rs_pr<Q8, CAP>(a, S, c, L - 1, bpr);
+  gather<12>(loc_of(c, L - 1) + LO_X2, E, S.xs, hdr);
+  if (lane == 0) stamp(a.trace, 49);
+  if constexpr (Q8) layernorm_seq(S.xs, S.lnf[0], S.lnf[1], S.xn, S.lntmp);
+}
+
+template <bool Q8, bool CAP>
+__device__ void regular_compute(const FusedArgs& a, FusedSmem& S, const Ctx& c, WRegs<Q8>& R, int wave) {
+  const int lane = lane_id();
+  const uint32_t E = c.E;
   u64* sinkw = a.sinkw + ((size_t)blockIdx.x * 8 + wave) * 16;
   float* sinkf = (float*)(sinkw + 8);
-  auto qsync = [&]() {
-    if constexpr (Q8) wg_barrier();
-  };
-  using K0 = std::integral_constant<int, 0>;
-  using K1 = std::integral_constant<int, 1>;
-
-  WRegs<Q8> R;
-  load_qkv<Q8, 0>(R, a.w, 0, U, false);
-  load_qkv<Q8, 1>(R, a.w, 0, U, false);
-  load_o<Q8, 0>(R, a.w, 0, U, false);
-  if constexpr (!Q8) load_o<Q8, 1>(R, a.w, 0, U, false);
-  load_fc<Q8, 0>(R, a.w, 0, U, false);
-  load_fc<Q8, 1>(R, a.w, 0, U, false);
-  load_pr<Q8, 0>(R, a.w, 0, U, false);
-  load_pr<Q8, 1>(R, a.w, 0, U, false);
+  Units U;
+  U.X = c.X;
+  U.nh = c.nh;
+  U.cwn = NCW * (NQ - c.nh);
+  U.cw = (wave - 1) * (NQ - c.nh) + (c.q - c.nh);
+  const int l0 = c.set;
+  load_block<Q8>(R, S.pr, a.w, l0, U, wave);
   wg_barrier();  // B0
-
-  for (int l = 0; l < L; ++l) {
+  for (int l = l0; l < L; l += 2) {
     u64* loc = loc_of(c, l);
     u64* glb = glb_of(c, l);
-    const bool last = l + 1 == L;
-    const int ln = last ? l : l + 1;  // block whose weights are loaded next (head rows after the last)
-    // ---- QKV rows; k/v rows also go to the cache
-    wg_barrier();  // B1
+    if (l > 0) rs_pr_poll<Q8>(a, S, c, l - 1, wave);
+    wg_barrier();  // BA
+    wg_barrier();  // B1: QKV
+    if (wave == 1) dstamp(a.trace, l, 59);
     if constexpr (Q8) {
       quantize_groups(S, S.xn, 0, 0, D / 64, wave);
-      qsync();
+      wg_barrier();
     }
     {
       f4 x[3];
       if constexpr (!Q8) {
         load_frag<3>(x, S.xs);
-        layernorm_frag(x, S.lnp[l & 1][0], S.lnp[l & 1][1]);
+        layernorm_frag(x, S.lnp[0], S.lnp[1]);
       }
-      auto row = [&](auto kc) {
-        constexpr int k = decltype(kc)::value;
-        const int n = cw + CW * k;
-        const bool own = n < 192 * nh;
-        const int r = qkv_row(X, own ? n : 0);
+      if (wave == 1) dstamp(a.trace, l, 60);
+#pragma unroll
+      for (int k = 0; k < UPW; ++k) {
+        const int n = U.qkv(k);
+        const bool own = n < 192 * U.nh;
+        const int r = qkv_row(U.X, own ? n : 0);
         float y;
         if constexpr (!Q8) {
-          y = dot_frag<3>(*reinterpret_cast<f4(*)[3]>(&R.r[hbase(k)]), x);
+          y = dot_frag<3>(*reinterpret_cast<f4(*)[3]>(&R.r[3 * k]), x);
         } else {
           int32_t* ca = CAP && own ? (int32_t*)(a.capture + cap_offset(l, M_QKV) + cap_item(M_QKV).acc) + (size_t)r * 12
                                    : nullptr;
           y = q8_dot<D>(*reinterpret_cast<i4(*)[1]>(&R.c[k]), R.sc[k], S.xc, S.xsc, ca);
         }
         y = y + R.b[k];
-        st_loc(own ? loc + LO_QKV + n : sinkw, pack(y, E));
-        *(own && r >= D ? a.cache + ((size_t)a.pos * L + l) * KV_ROW + (r - D) : sinkf) = y;
+        if (store_lane(64)) {
+          st_loc(own ? loc + LO_QKV + n : sinkw, pack(y, E));
+          *(own && r >= D ? a.cache + ((size_t)a.pos * L + l) * KV_ROW + (r - D) : sinkf) = y;
+        }
         if (CAP && own && lane == 0) ((float*)(a.capture + cap_offset(l, M_QKV) + cap_item(M_QKV).y))[r] = y;
-        load_qkv<Q8, k>(R, a.w, ln, U, last);
-      };
-      row(K0{});
-      row(K1{});
-    }
-    if (l == 5 && wave == 1 && lane == 0) stamp(a.trace, 53);
-    // ---- output projection: one term per (head, output)
-    wg_barrier();  // B2
-    if constexpr (Q8) {
-      // the XCD's head groups: wave 1 quantizes head X, wave 2 head X + 8
-      if (wave - 1 < nh) {
-        const int hh = wave - 1, g = X + NX * hh;
-        float s;
-        const int q = quant_lane(S.att[DH * hh + lane], s);
-        S.xc[64 * g + lane] = (int8_t)q;
-        if (lane == 0) S.xsc[g] = s;
       }
-      qsync();
     }
-    if constexpr (!Q8) {
-      auto unit = [&](auto kc) {
-        constexpr int k = decltype(kc)::value;
-        const bool own = cw + CW * k < 192 * nh;
-        int u, hh, i, h;
-        o_unit_f32(U, k, u, hh, i, h);
-        const f4 xv = *(const f4*)(S.att + DH * hh + 4 * (lane % 16));
-        const float p = dot_q16(R.r[6 + k], xv);
-        st_sc1(own ? glb + GL_O + (size_t)h * D + i : sinkw, pack(p, E));
-        load_o<Q8, k>(R, a.w, ln, U, last);
-      };
-      unit(K0{});
-      unit(K1{});
-    } else {
-      const bool own = cw < 48 * nh;
-      int n, i, h;
-      o_unit_q8(U, n, i, h);
-      const i4 xv = *(const i4*)(S.xc + DH * h + 16 * (lane % 4));
-      const int acc = quad_acc(R.c[2], xv);
-      const float t = ((float)acc * R.sc[2]) * S.xsc[h];
-      st_sc1(own ? glb + GL_O + (size_t)h * D + i : sinkw, pack(t, E));
-      if (CAP && own && lane % 4 == 0)
-        ((int32_t*)(a.capture + cap_offset(l, M_O) + cap_item(M_O).acc))[(size_t)i * H + h] = acc;
-      load_o<Q8, 0>(R, a.w, ln, U, last);
-    }
-    if (l == 5 && wave == 1 && lane == 0) stamp(a.trace, 54);
-    // ---- FC rows and GELU
-    wg_barrier();  // B3
+    if (wave == 1 && lane == 0) stamp(a.trace, 2 + 4 * l);
+    wg_barrier();  // B3: FC
     if constexpr (Q8) {
       quantize_groups(S, S.xn, 0, 0, D / 64, wave);
-      qsync();
+      wg_barrier();
     }
     {
       f4 x[3];
       if constexpr (!Q8) {
-        load_frag<3>(x, S.xs);
-        layernorm_frag(x, S.lnp[l & 1][2], S.lnp[l & 1][3]);
+        load_frag<3>(x, S.x1s);
+        layernorm_frag(x, S.lnp[2], S.lnp[3]);
       }
-      auto row = [&](auto kc) {
-        constexpr int k = decltype(kc)::value;
-        const int n = cw + CW * k;
+#pragma unroll
+      for (int k = 0; k < UPW; ++k) {
+        const int n = U.cw + U.cwn * k;
         const bool own = n < GS;
-        const int r = GS * X + (own ? n : 0);
+        const int r = GS * U.X + (own ? n : 0);
         float y;
         if constexpr (!Q8) {
-          y = dot_frag<3>(*reinterpret_cast<f4(*)[3]>(&R.r[hbase(2 + k)]), x);
+          y = dot_frag<3>(*reinterpret_cast<f4(*)[3]>(&R.r[3 * (UPW + k)]), x);
         } else {
           int32_t* ca = CAP && own ? (int32_t*)(a.capture + cap_offset(l, M_FC) + cap_item(M_FC).acc) + (size_t)r * 12
                                    : nullptr;
-          y = q8_dot<D>(*reinterpret_cast<i4(*)[1]>(&R.c[3 + k]), R.sc[3 + k], S.xc, S.xsc, ca);
+          y = q8_dot<D>(*reinterpret_cast<i4(*)[1]>(&R.c[UPW + k]), R.sc[UPW + k], S.xc, S.xsc, ca);
         }
-        y = y + R.b[2 + k];
-        st_loc(own ? loc + LO_G + n : sinkw, pack(gelu_tanh(y), E));
+        y = y + R.b[UPW + k];
+        const float gy = gelu_tanh(y);
+        if (store_lane(64)) st_loc(own ? loc + LO_G + n : sinkw, pack(gy, E));
         if (CAP && own && lane == 0) ((float*)(a.capture + cap_offset(l, M_FC) + cap_item(M_FC).y))[r] = y;
-        load_fc<Q8, k>(R, a.w, ln, U, last);
-      };
-      row(K0{});
-      row(K1{});
+      }
     }
-    if (l == 5 && wave == 1 && lane == 0) stamp(a.trace, 56);
-    // ---- MLP projection: fp32 one partial per (slice, output), int8 one term per
-    // (group, output)
-    wg_barrier();  // B4
+    wg_barrier();  // B4: MLP projection
+    if (wave == 1) dstamp(a.trace, l, 62);
     if constexpr (Q8) {
-      quantize_groups(S, S.xg, GPS * X, GPS * X, GPS * (X + 1), wave);
-      qsync();
+      quantize_groups(S, S.xg, GPS * c.X, GPS * c.X, GPS * (c.X + 1), wave);
+      wg_barrier();
     }
     if constexpr (!Q8) {
-      auto unit = [&](auto kc) {
-        constexpr int k = decltype(kc)::value;
-        const int u0 = cw + CW * k;
+#pragma unroll
+      for (int k = 0; k < UPW; ++k) {
+        const int u0 = U.cw + U.cwn * k;
         const bool own = u0 < D / 2;
         const int u = own ? u0 : 0;
-        const int q = lane / 16, j = lane % 16;
+        const int qq = lane / 16, j = lane % 16;
         float qv[3];
 #pragma unroll
         for (int p = 0; p < 3; ++p) {
-          const int kk = 4 * p + q;
+          const int kk = 4 * p + qq;
           const f4 xv = *(const f4*)(S.xg + 64 * (kk % GPS) + 4 * j);
-          qv[p] = dot_q16(R.r[hbase(4 + k) + p], xv);
+          qv[p] = dot_q16(pr_w(S.pr, wave, k, p), xv);
         }
         auto val = [&](int kk) { return lane_val(qv[kk / 4], 16 * (kk % 4)); };
         float p0 = val(0), p1 = val(GPS);
@@ -757,154 +788,254 @@ __device__ void compute_waves(const FusedArgs a, FusedSmem& S, const Ctx c) {
         }
         // lanes 0..31 store row 2u, lanes 32..63 row 2u+1
         const int half = lane >> 5;
-        st_sc1(own ? glb + GL_P + (size_t)X * D + 2 * u + half : sinkw, pack(half ? p1 : p0, E));
-        load_pr<Q8, k>(R, a.w, ln, U, last);
-      };
-      unit(K0{});
-      unit(K1{});
+        if (store_lane(32)) st_sc1(own ? glb + GL_P + (size_t)U.X * D + 2 * u + half : sinkw, pack(half ? p1 : p0, E));
+      }
     } else {
-      auto unit = [&](auto kc) {
-        constexpr int k = decltype(kc)::value;
-        const int u0 = cw + CW * k;
+#pragma unroll
+      for (int k = 0; k < UPW; ++k) {
+        const int u0 = U.cw + U.cwn * k;
         const bool own = u0 < GPS * D / 16;
-        const int n = 16 * (own ? u0 : 0) + lane / 4, i = n / GPS, g = GPS * X + n % GPS;
+        const int n = 16 * (own ? u0 : 0) + lane / 4, i = n / GPS, g = GPS * U.X + n % GPS;
         const i4 xv = *(const i4*)(S.xc + 64 * g + 16 * (lane % 4));
-        const int acc = quad_acc(R.c[5 + k], xv);
-        const float t = ((float)acc * R.sc[5 + k]) * S.xsc[g];
-        st_sc1(own ? glb + GL_P + (size_t)g * D + i : sinkw, pack(t, E));
+        const int acc = quad_acc(R.c[2 * UPW + k], xv);
+        const float t = ((float)acc * R.sc[2 * UPW + k]) * S.xsc[g];
+        if (store_lane(4)) st_sc1(own ? glb + GL_P + (size_t)g * D + i : sinkw, pack(t, E));
         if (CAP && own && lane % 4 == 0)
           ((int32_t*)(a.capture + cap_offset(l, M_PR) + cap_item(M_PR).acc))[(size_t)i * NG_PR + g] = acc;
-        load_pr<Q8, k>(R, a.w, ln, U, last);
-      };
-      unit(K0{});
-      unit(K1{});
+      }
     }
-    if (l == 5 && wave == 1 && lane == 0) stamp(a.trace, 57);
+    if (wave == 1) dstamp(a.trace, l, 63);
+    if (FUSED_DELAY && l + 2 < L) wg_barrier();  // BD: the other set has its block input
+    // this block is done: the weights of the set's next block (or the first head rows)
+    if (l + 2 < L) load_block<Q8>(R, S.pr, a.w, l + 2, U, wave);
+    else load_head_slots<Q8>(R, a.w, wave * GRID + (int)blockIdx.x);
   }
-  // the head: its first rows were loaded during the last block
-  wg_barrier();  // B5
-  if constexpr (Q8) {
-    quantize_groups(S, S.xn, 0, 0, D / 64, wave);
-    qsync();
-  }
-  head_rows<Q8, CAP>(a, S, R, U.hw, U.hstride);
-  if (wave == 1 && lane == 0) stamp(a.trace, 50);
+  if (c.set == 0) rs_pr_poll<Q8>(a, S, c, L - 1, wave);
+  wg_barrier();  // BT
 }
 
-// ---- attention workgroups (ranks 0 and 1): head X + 8*rank when it exists ----------
+// ---- head units (head h = X + 8q) ---------------------------------------------------
+// Per block: its keys/values j < pos are in LDS; wave 0 takes the unit's
+// reduce-scatter of the previous block and polls the XCD's q/k/v of the head;
+// attention; all 8 waves compute the head's output-projection terms for the 768
+// outputs and publish them; wave 0 then takes the unit's reduce-scatter of x1.
+// Keys/values j < pos of head h at block l into LDS (all threads of a head unit).
+__device__ __forceinline__ void stage_kv(const FusedArgs& a, FusedSmem& S, int l, int h) {
+  const float* cl = a.cache + (size_t)l * KV_ROW + h * DH;
+  attn_stage_rows(S.at, [&](int j) { return cl + (size_t)j * CACHE_POS; }, 0, a.pos, 0, FT);
+}
+
 template <bool Q8, bool CAP>
-__device__ void attention_wg(const FusedArgs a, FusedSmem& S, const Ctx c) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const bool has_head = c.rank < heads_of(c.X);
-  const int h = c.X + NX * c.rank, pos = a.pos;
+__device__ void head_unit(const FusedArgs& a, FusedSmem& S, const Ctx& c, WRegs<Q8>& R, int wave) {
+  const int lane = lane_id();
   uint32_t* hdr = a.header;
+  const uint32_t E = c.E;
+  const int h = c.X + NX * c.q, pos = a.pos;
   AttnSmem& sm = S.at;
-  const int hw = (wave - 1) * GRID + (int)blockIdx.x;  // head rows of waves 1..7
-  const int hstride = NCW * GRID;
-  float xr = 0.0f;
+  const int o = RSN * c.q + min(lane, RSN - 1);
+  const int l0 = c.set;
+  u64* sinkw = a.sinkw + ((size_t)blockIdx.x * 8 + wave) * 16;
+  float bo = 0.0f, bpr = 0.0f, xr = 0.0f;
+  load_o_head<Q8>(R, (char*)&S.pr, a.w, l0, h);
+  stage_kv(a, S, l0, h);
   if (wave == 0) {
     stage_vec(S.lnf[0], a.w.small + sp::LNF_G);
     stage_vec(S.lnf[1], a.w.small + sp::LNF_B);
-    xr = embed(a, S.xs, c.rank);
-  }
-  for (int l = 0; l < L; ++l) {
-    u64* loc = loc_of(c, l);
-    if (has_head) {
-      const float* cl = a.cache + (size_t)l * KV_ROW + h * DH;
-      auto kv = [&](int j) { return cl + (size_t)j * CACHE_POS; };
-      attn_stage_rows(sm, kv, 0, pos, 64, FT - 64);
-      if (wave == 0) {
-        float v[3];
-        poll<3, true>(loc + LO_QKV + 192 * c.rank, 192, [](int k) { return k; }, c.E, v, hdr);
-        if (lane == 0) stamp(a.trace, 1 + 4 * l);
-        sm.q[lane] = v[0];
-        sm.k[pos][lane] = v[1];
-        sm.v[pos][lane] = v[2];
-      }
-      __syncthreads();
-      const float o = Q8 ? attn_compute_seq(sm, pos + 1) : attn_compute(sm, pos + 1, FT / 64);
-      if (wave == 0) {
-        st_loc(loc + LO_ATT + DH * c.rank + lane, pack(o, c.E));
-        if (lane == 0) stamp(a.trace, 2 + 4 * l);
-        if (CAP) {
-          float s;
-          const int q = quant_lane(o, s);
-          char* base = a.capture + cap_offset(l, M_O);
-          const CapLayout cl2 = cap_item(M_O);
-          ((float*)(base + cl2.in))[DH * h + lane] = o;
-          ((int8_t*)(base + cl2.codes))[DH * h + lane] = (int8_t)q;
-          if (lane == 0) ((float*)(base + cl2.xs))[h] = s;
-        }
-      }
-      __syncthreads();  // the LDS rows are free for the next block
-    }
-    if (wave == 0) {
-      rs_o<Q8, CAP>(a, S, c, l, xr);
-      if (lane == 0) stamp(a.trace, 3 + 4 * l);
-      rs_pr<Q8, CAP>(a, S, c, l, xr);
-      if (lane == 0) stamp(a.trace, 4 + 4 * l);
-    }
-  }
-  // the tied head: these workgroups take head rows too
-  WRegs<Q8> R;
-  if (wave >= 1) {
-#pragma unroll
-    for (int s = 0; s < head_slots<Q8>(); ++s) load_head<Q8>(R, a.w, s, hw + s * hstride);
-  }
-  if (wave == 0) {
-    gather<12>(loc_of(c, L - 1) + LO_X2, c.E, S.xs, hdr);
-    if constexpr (Q8) layernorm_seq(S.xs, S.lnf[0], S.lnf[1], S.xn, S.lntmp);
+    bo = small_p(a.w, l0, sp::B_O)[o];
+    if (l0 > 0) bpr = small_p(a.w, l0 - 1, sp::B_PR)[o];
   }
   wg_barrier();
-  if (wave >= 1) {
-    if constexpr (Q8) quantize_groups(S, S.xn, 0, 0, D / 64, wave);
+  for (int l = l0; l < L; l += 2) {
+    u64* glb = glb_of(c, l) + GL_O + (size_t)h * D;
+    if (l > 0) {
+      rs_pr_poll<Q8>(a, S, c, l - 1, wave);
+      wg_barrier();
+    }
+    if (wave == 0) {
+      dstamp(a.trace, l, 52);
+      xr = l == 0 ? embed(a, nullptr, c.q) : rs_pr<Q8, CAP>(a, S, c, l - 1, bpr);
+      if (lane == 0) stamp(a.trace, 1 + 4 * l);
+      float v[3];
+      poll<3, true>(loc_of(c, l) + LO_QKV + 192 * c.q, 192, [](int k) { return k; }, E, v, hdr);
+      dstamp(a.trace, l, 54);
+      sm.q[lane] = v[0];
+      sm.k[pos][lane] = v[1];
+      sm.v[pos][lane] = v[2];
+    }
+    wg_barrier();
+    const float at = Q8 ? attn_compute_seq(sm, pos + 1) : attn_compute(sm, pos + 1, NWV);
+    if (wave == 0) {
+      S.att[lane] = at;
+      if constexpr (Q8) {
+        float sx;
+        const int qv = quant_lane(at, sx);
+        S.xc[lane] = (int8_t)qv;
+        if (lane == 0) S.xsc[0] = sx;
+        if (CAP) {
+          char* base = a.capture + cap_offset(l, M_O);
+          const CapLayout cl2 = cap_item(M_O);
+          ((float*)(base + cl2.in))[DH * h + lane] = at;
+          ((int8_t*)(base + cl2.codes))[DH * h + lane] = (int8_t)qv;
+          if (lane == 0) ((float*)(base + cl2.xs))[h] = sx;
+        }
+      }
+      if (lane == 0) stamp(a.trace, 2 + 4 * l);
+    }
+    wg_barrier();  // attention output in LDS
+    // The output-projection terms.  fp32: a half dot is s_j = the fmaf chain over
+    // inputs 4j..4j+3 (j < 8 of its half), then ((s0+s1)+(s2+s3)) + ((s4+s5)+(s6+s7)),
+    // and the two halves are added across the lane pair: the same value as
+    // dot_q16 over the head's 64 inputs (its 16-lane tree, as o_row uses).  int8:
+    // the exact group accumulator, then ((float)acc * sw) * sx.
+#pragma unroll
+    for (int k = 0; k < O_HALF_PER_THREAD; ++k) {
+      const int hd = o_half(k), i = hd >> 1, half = hd & 1;
+      float t;
+      if constexpr (!Q8) {
+        const float* av = S.att + 32 * half;
+        float sj[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const f4 x = *(const f4*)(av + 4 * j);
+          const f4 wv4 = R.r[8 * k + j];
+          float acc = 0.0f;
+          acc = fmaf(wv4.x, x.x, acc);
+          acc = fmaf(wv4.y, x.y, acc);
+          acc = fmaf(wv4.z, x.z, acc);
+          acc = fmaf(wv4.w, x.w, acc);
+          sj[j] = acc;
+        }
+        const float hs = ((sj[0] + sj[1]) + (sj[2] + sj[3])) + ((sj[4] + sj[5]) + (sj[6] + sj[7]));
+        t = hs + dpp_f<DPP_QUAD_1032>(hs);
+      } else {
+        const int8_t* xv = S.xc + 32 * half;
+        const i4 x0 = *(const i4*)xv, x1 = *(const i4*)(xv + 16);
+        int acc = 0;
+        acc = __builtin_amdgcn_sdot4(R.c[2 * k].x, x0.x, acc, false);
+        acc = __builtin_amdgcn_sdot4(R.c[2 * k].y, x0.y, acc, false);
+        acc = __builtin_amdgcn_sdot4(R.c[2 * k].z, x0.z, acc, false);
+        acc = __builtin_amdgcn_sdot4(R.c[2 * k].w, x0.w, acc, false);
+        acc = __builtin_amdgcn_sdot4(R.c[2 * k + 1].x, x1.x, acc, false);
+        acc = __builtin_amdgcn_sdot4(R.c[2 * k + 1].y, x1.y, acc, false);
+        acc = __builtin_amdgcn_sdot4(R.c[2 * k + 1].z, x1.z, acc, false);
+        acc = __builtin_amdgcn_sdot4(R.c[2 * k + 1].w, x1.w, acc, false);
+        acc += dpp_i<DPP_QUAD_1032>(acc);
+        t = ((float)acc * R.sc[k]) * S.xsc[0];
+        if (CAP && half == 0) ((int32_t*)(a.capture + cap_offset(l, M_O) + cap_item(M_O).acc))[(size_t)i * H + h] = acc;
+      }
+      if (store_lane(2)) st_sc1(glb + i, pack(t, E));
+    }
+    if (wave == 1) dstamp(a.trace, l, 56);
+    if (wave == 0) {
+      xr = rs_o<Q8, CAP>(a, S, c, l, xr, bo);
+      if (lane == 0) stamp(a.trace, 3 + 4 * l);
+    }
+    wg_barrier();  // the keys/values of block l are no longer read
+    const int ln = l + 2;
+    if (FUSED_DELAY && ln < L) {
+      // start streaming once the other set has gathered its block input
+      if (wave == 0) {
+        float v[12];
+        poll<12, true>(loc_of(c, l) + LO_X2, D, [](int k) { return k; }, E, v, hdr);
+      }
+      wg_barrier();
+    }
+    if (ln < L) {
+      load_o_head<Q8>(R, (char*)&S.pr, a.w, ln, h);
+      stage_kv(a, S, ln, h);
+    } else {
+      load_head_slots<Q8>(R, a.w, wave * GRID + (int)blockIdx.x);
+    }
+    if (wave == 0) {
+      if (ln < L) bo = small_p(a.w, ln, sp::B_O)[o];
+      if (ln - 1 < L) bpr = small_p(a.w, ln - 1, sp::B_PR)[o];
+    }
+    wg_barrier();
   }
-  if constexpr (Q8) wg_barrier();
-  if (wave >= 1) head_rows<Q8, CAP>(a, S, R, hw, hstride);
+  if (c.set == 0) rs_pr_poll<Q8>(a, S, c, L - 1, wave);
+  wg_barrier();
+  if (wave == 0) {
+    if (c.set == 0) rs_pr<Q8, CAP>(a, S, c, L - 1, bpr);
+    gather<12>(loc_of(c, L - 1) + LO_X2, E, S.xs, hdr);
+    if (lane == 0) stamp(a.trace, 49);
+    if constexpr (Q8) layernorm_seq(S.xs, S.lnf[0], S.lnf[1], S.xn, S.lntmp);
+  }
 }
 
 template <bool Q8, bool CAP>
 __global__ __launch_bounds__(FT, 1) void k_fused(const FusedArgs a) {
   extern __shared__ __align__(16) char smem_raw[];
   FusedSmem& S = *(FusedSmem*)smem_raw;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   uint32_t* hdr = a.header;
   if (threadIdx.x == 0) stamp(a.trace, 0);
   Ctx c;
   c.E = ld32(&hdr[HDR_EPOCH]) + 1u;
   c.X = (int)xcc_id();
-  c.rank = (int)blockIdx.x / NX;
+  const int rank = (int)blockIdx.x / NX;
   if (c.X >= NX) {
     if (threadIdx.x == 0) set_error(hdr, ERR_XCC);
     c.X = 0;
   }
+  c.set = rank & 1;
+  c.q = rank >> 1;
+  c.nh = heads_of(c.X);
+  c.head = c.q < c.nh;
   c.loc = a.fx + (size_t)c.X * L * FX_LOC_PER_LAYER;
   c.glb = a.fx + LOC_WORDS;
-  if (c.rank < CR0) attention_wg<Q8, CAP>(a, S, c);
-  else if (wave == 0) io_wave<Q8, CAP>(a, S, c);
-  else compute_waves<Q8, CAP>(a, S, c);
+  float* sinkf = (float*)(a.sinkw + ((size_t)blockIdx.x * 8 + wave) * 16 + 8);
+  const int hw = wave * GRID + (int)blockIdx.x;  // first head row of this wave
 
+  WRegs<Q8> R;
+  if (c.head) head_unit<Q8, CAP>(a, S, c, R, wave);
+  else if (wave == 0) regular_io<Q8, CAP>(a, S, c);
+  else regular_compute<Q8, CAP>(a, S, c, R, wave);
+
+  // ---- the tied head: every wave takes its head rows (the first ones are in its
+  // registers already, except on wave 0 of a regular unit)
+  if (!c.head && wave == 0) load_head_slots<Q8>(R, a.w, hw);
+  wg_barrier();  // x12 (int8: its LayerNorm) is in LDS
+  if constexpr (Q8) {
+    for (int g = wave; g < D / 64; g += NWV) {
+      float s;
+      const int qv = quant_lane(S.xn[g * 64 + lane], s);
+      S.xc[g * 64 + lane] = (int8_t)qv;
+      if (lane == 0) S.xsc[g] = s;
+    }
+    wg_barrier();
+    if (CAP && blockIdx.x == 0 && wave == 0) capture_input(a, S, 0, M_HEAD, S.xn, 0, D, lane, 64);
+  }
+  head_rows<Q8, CAP>(a, S, R, hw, sinkf);
+  if (lane == 0 && wave == 1) stamp(a.trace, 50);
+
+  // Epilogue: the last workgroup to finish checks the placement (XCD(b) - b one
+  // constant mod NX, which the rank/XCD split above relies on; the waits would have
+  // given up otherwise), then clears the counter and advances the epoch.
+  __shared__ int s_last;
   __syncthreads();
+  u64* place = a.fx + LOC_WORDS + GLB_WORDS;
   if (threadIdx.x == 0) {
     stamp(a.trace, 51);
-    u64* place = a.fx + LOC_WORDS + GLB_WORDS;
     st_sc1(place + blockIdx.x, ((u64)c.E << 32) | (uint32_t)c.X);
-    const uint32_t done = atomicAdd(&hdr[HDR_DONE], 1u);
-    if (done == (uint32_t)GRID - 1) {
-      // placement check: XCD(b) - b must be one constant mod NX for the rank/XCD
-      // split above to hold (the waits would have given up otherwise)
-      int off = -1;
-      bool bad = false;
-      uint32_t spins = 0;  // one bound for the whole check
-      for (int b = 0; b < GRID; ++b) {
-        u64 w;
-        do {
-          w = ld_sc1(place + b);
-        } while (epoch_of(w) != c.E && ++spins < SPIN_LIMIT);
-        const int o = ((int)(uint32_t)w - b % NX + NX) % NX;
-        if (off < 0) off = o;
-        bad |= o != off || epoch_of(w) != c.E;
-      }
+    s_last = atomicAdd(&hdr[HDR_DONE], 1u) == (uint32_t)GRID - 1;
+  }
+  __syncthreads();
+  if (s_last) {
+    int bad = 0;
+    if (threadIdx.x < GRID) {
+      const int t = threadIdx.x;
+      u64 w0, w;
+      uint32_t spins = 0;
+      do {
+        w0 = ld_sc1(place);
+        w = ld_sc1(place + t);
+      } while ((epoch_of(w0) != c.E || epoch_of(w) != c.E) && ++spins < SPIN_LIMIT);
+      const int off0 = ((int)(uint32_t)w0 + NX) % NX;
+      const int off = ((int)(uint32_t)w - t % NX + NX) % NX;
+      bad = off != off0 || epoch_of(w) != c.E || epoch_of(w0) != c.E;
+    }
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0) {
       if (bad) set_error(hdr, ERR_XCC);
       hdr[HDR_DONE] = 0;
       __hip_atomic_store(&hdr[HDR_EPOCH], c.E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
