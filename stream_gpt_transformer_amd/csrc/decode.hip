@@ -169,7 +169,7 @@ __global__ __launch_bounds__(128) void k_attn(const ProjArgs a) {
   auto kv = [&](int j) { return cache + ((size_t)j * L + l) * KV_ROW + h * DH; };
   attn_stage(sm, kv, npos, a.k.qkv + (size_t)b * D3 + h * DH);
   __syncthreads();
-  const float o = SEQ ? attn_compute_seq(sm, npos) : attn_compute(sm, npos, 2);
+  const float o = SEQ ? attn_compute_seq(sm, npos) : attn_compute(sm, npos, 128);
   if (threadIdx.x < DH) a.k.att[(size_t)b * D + h * DH + threadIdx.x] = o;
 }
 

@@ -342,23 +342,25 @@ __device__ __forceinline__ void layernorm_lds(const float* xs, const float* __re
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // ---- attention (one session, one head) --------------------------------------
-// npos keys (1..128), thread t < 128 owns key t:
-//   s_t = ((c_0 + c_1) + (c_2 + c_3)) * 0.125 (1/sqrt(64)), where c_e is the sum over
-//   i ascending of q_{4i+e}*K_t,4i+e;
+// fp32 path, npos keys (1..128):
+//   P_t,r = ((a.x + a.y) + (a.z + a.w)) with a = the float4 sum over i = 0..3
+//     ascending of q[16r+4i..] * K_t[16r+4i..] (quarter r of the 64 dims);
+//   s_t = ((P_t,0 + P_t,1) + (P_t,2 + P_t,3)) * 0.125   (1/sqrt(64));
 //   m = max_t s_t;  e_t = exp_spec(s_t - m);
 //   Z = Z_0 + Z_1 with Z_w = wave_sum of e_t over t in [64w, 64w+64);
 //   w_t = e_t / Z;
-//   a_d = p_0 + p_1 + ... + p_7 with p_b = sum over t in [16b, 16b+16), t < npos,
-//   ascending, of w_t*V_t,d.
-// The key blocks b are spread over waves 0..nwav-1 of the block (every value is the
-// same for any nwav).
+//   p_b = sum over t in [8b, 8b+8), t < npos, ascending, of w_t*V_t,d (b < 16);
+//   a_d = ((((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7))) + (((p8+p9)+(p10+p11))+((p12+p13)+(p14+p15)))).
+// Every value is the same for any block size of 128 or more threads (the work is
+// dealt out in fixed units).
+constexpr int ATT_VB = 16;  // key blocks of the weighted sum
 struct AttnSmem {
   float k[PMAX][DH + 4];  // padded rows, 16-byte aligned
   float v[PMAX][DH];
   float q[DH];
-  float w[PMAX];
+  float w[PMAX];          // scores, then weights
   float red[4];
-  float part[8][DH];  // per key-block partial outputs
+  float part[ATT_VB][DH];  // per key-block partial outputs
 };
 
 // Stage key/value rows j0..j1-1 of one head into LDS with threads tid0..tid0+nthr-1
@@ -383,22 +385,28 @@ __device__ __forceinline__ void attn_stage(AttnSmem& sm, RowPtr kv, int npos, co
 }
 
 // Returns a_d in threads 0..63 (d = thread index); other threads return 0.  Every
-// thread of the block must call it (it synchronises the block); the block needs at
-// least 128 threads and nwav waves.
-__device__ __forceinline__ float attn_compute(AttnSmem& sm, int npos, int nwav) {
+// thread of the block (nthr threads, a multiple of 128) must call it; it
+// synchronises the block through LDS-only barriers.
+__device__ __forceinline__ float attn_compute(AttnSmem& sm, int npos, int nthr) {
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
   const bool act = t < 128;
-  float s = -INFINITY;
-  if (act && t < npos) {
+  // scores: unit u = 4*key + quarter, a lane quad per key
+  for (int u = t; u < 4 * PMAX; u += nthr) {
+    const int key = u >> 2, r = u & 3;
     f4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int i = 0; i < DH / 4; ++i) {
-      const f4 kr = *(const f4*)&sm.k[t][4 * i];
-      const f4 qq = *(const f4*)&sm.q[4 * i];
+    for (int i = 0; i < 4; ++i) {
+      const f4 kr = *(const f4*)&sm.k[key][16 * r + 4 * i];
+      const f4 qq = *(const f4*)&sm.q[16 * r + 4 * i];
       acc = acc + qq * kr;
     }
-    s = ((acc.x + acc.y) + (acc.z + acc.w)) * 0.125f;
+    float P = (acc.x + acc.y) + (acc.z + acc.w);
+    P = P + dpp_f<DPP_QUAD_1032>(P);
+    P = P + dpp_f<DPP_QUAD_2301>(P);
+    if (r == 0 && key < npos) sm.w[key] = P * 0.125f;
   }
+  lds_barrier();
+  const float s = (act && t < npos) ? sm.w[t] : -INFINITY;
   const float mw = wave_max(s);
   if (act && lane == 0) sm.red[wv] = mw;
   lds_barrier();
@@ -411,25 +419,28 @@ __device__ __forceinline__ float attn_compute(AttnSmem& sm, int npos, int nwav) 
   const float Z = sm.red[2] + sm.red[3];
   if (act) sm.w[t] = e / Z;
   lds_barrier();
-  if (wv < nwav) {
-    for (int b = wv; b < 8; b += nwav) {
-      float p = 0.0f;
-      const int j0 = 16 * b, j1 = min(j0 + 16, npos);
-      if (j1 - j0 == 16) {
+  for (int b = wv; b < ATT_VB; b += nthr / 64) {
+    float p = 0.0f;
+    const int j0 = 8 * b, j1 = min(j0 + 8, npos);
+    if (j1 - j0 == 8) {
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) p = p + sm.w[j0 + jj] * sm.v[j0 + jj][lane];
-      } else {
-        for (int j = j0; j < j1; ++j) p = p + sm.w[j] * sm.v[j][lane];
-      }
-      sm.part[b][lane] = p;
+      for (int jj = 0; jj < 8; ++jj) p = p + sm.w[j0 + jj] * sm.v[j0 + jj][lane];
+    } else {
+      for (int j = j0; j < j1; ++j) p = p + sm.w[j] * sm.v[j][lane];
     }
+    sm.part[b][lane] = p;
   }
   lds_barrier();
   float acc = 0.0f;
   if (wv == 0) {
-    acc = sm.part[0][lane];
+    float p[ATT_VB];
 #pragma unroll
-    for (int b = 1; b < 8; ++b) acc = acc + sm.part[b][lane];
+    for (int b = 0; b < ATT_VB; ++b) p[b] = sm.part[b][lane];
+#pragma unroll
+    for (int w2 = 1; w2 < ATT_VB; w2 *= 2)
+#pragma unroll
+      for (int b = 0; b < ATT_VB; b += 2 * w2) p[b] = p[b] + p[b + w2];
+    acc = p[0];
   }
   return acc;
 }

@@ -863,7 +863,7 @@ __device__ void head_unit(const FusedArgs& a, FusedSmem& S, const Ctx& c, WRegs<
       sm.v[pos][lane] = v[2];
     }
     wg_barrier();
-    const float at = Q8 ? attn_compute_seq(sm, pos + 1) : attn_compute(sm, pos + 1, NWV);
+    const float at = Q8 ? attn_compute_seq(sm, pos + 1) : attn_compute(sm, pos + 1, FT);
     if (wave == 0) {
       S.att[lane] = at;
       if constexpr (Q8) {
