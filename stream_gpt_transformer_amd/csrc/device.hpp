@@ -75,6 +75,42 @@ __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_f<DPP_ROW_BCAST31, 0xc>(v));
   return bcast_lane(v, 63);
 }
+// N independent wave sums in lock step (the same tree as wave_sum for each value,
+// interleaved so that the lane moves of one hide the latency of the others).
+template <int N>
+__device__ __forceinline__ void wave_sum_n(float (&v)[N]) {
+#pragma unroll
+  for (int k = 0; k < N; ++k) v[k] = v[k] + dpp_f<DPP_QUAD_1032>(v[k]);
+#pragma unroll
+  for (int k = 0; k < N; ++k) v[k] = v[k] + dpp_f<DPP_QUAD_2301>(v[k]);
+#pragma unroll
+  for (int k = 0; k < N; ++k) v[k] = v[k] + dpp_f<DPP_ROW_HALF_MIRROR>(v[k]);
+#pragma unroll
+  for (int k = 0; k < N; ++k) v[k] = v[k] + dpp_f<DPP_ROW_MIRROR>(v[k]);
+#pragma unroll
+  for (int k = 0; k < N; ++k) v[k] = v[k] + dpp_f<DPP_ROW_BCAST15, 0xa>(v[k]);
+#pragma unroll
+  for (int k = 0; k < N; ++k) v[k] = v[k] + dpp_f<DPP_ROW_BCAST31, 0xc>(v[k]);
+#pragma unroll
+  for (int k = 0; k < N; ++k) v[k] = bcast_lane(v[k], 63);
+}
+// The 16-lane tree of row16_sum evaluated inside one lane on s[0..15] (s[j] being
+// what lane j of the row holds): the same value, by commutativity of each add.
+__device__ __forceinline__ float row16_tree(const float (&s)[16]) {
+  const float a = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+  const float b = ((s[8] + s[9]) + (s[10] + s[11])) + ((s[12] + s[13]) + (s[14] + s[15]));
+  return a + b;
+}
+// The lane part of dot_q16: the fmaf chain over one float4.
+__device__ __forceinline__ float fma4(const f4 w, const f4 x) {
+  float acc = 0.0f;
+  acc = fmaf(w.x, x.x, acc);
+  acc = fmaf(w.y, x.y, acc);
+  acc = fmaf(w.z, x.z, acc);
+  acc = fmaf(w.w, x.w, acc);
+  return acc;
+}
+
 // Exact integer sum over each 4-lane quad (every lane of the quad gets it).
 __device__ __forceinline__ int quad_sum(int p) {
   p += dpp_i<DPP_QUAD_1032>(p);
@@ -138,6 +174,19 @@ __device__ __forceinline__ void layernorm_frag(f4 (&x)[3], const float* __restri
 // One output of an fp32 projection: lane l accumulates its 4*NI products with an
 // explicit fmaf chain in (i, e) order, then wave_sum adds the 64 lane partials.
 // The returned value (identical in every lane) excludes the bias.
+// dot_frag's lane part (before wave_sum).
+template <int NI>
+__device__ __forceinline__ float dot_lane(const f4* w, const f4 (&x)[NI]) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    acc = fmaf(w[i].x, x[i].x, acc);
+    acc = fmaf(w[i].y, x[i].y, acc);
+    acc = fmaf(w[i].z, x[i].z, acc);
+    acc = fmaf(w[i].w, x[i].w, acc);
+  }
+  return acc;
+}
 template <int NI>
 __device__ __forceinline__ float dot_frag(const f4 (&w)[NI], const f4 (&x)[NI]) {
   float acc = 0.0f;

@@ -75,6 +75,9 @@ constexpr int HEAD_MAX_ROWS = (V + HEAD_STRIDE - 1) / HEAD_STRIDE;
 #ifndef FUSED_DELAY
 #define FUSED_DELAY 0
 #endif
+#ifndef FUSED_DEFER
+#define FUSED_DEFER 1
+#endif
 #ifndef FUSED_MASKED
 #define FUSED_MASKED 0
 #endif
@@ -498,6 +501,15 @@ __device__ __forceinline__ float embed(const FusedArgs& a, float* xs, int q) {
   return a.w.wte[(size_t)a.token * D + o] + a.w.wpe[(size_t)a.pos * D + o];
 }
 
+// Set 1 defers its first weight loads until set 0 has published its first QKV
+// rows: at launch both sets would otherwise share the HBM bandwidth and delay block
+// 0, while set 1's weights are only needed a block later.
+__device__ __forceinline__ void defer_set1(const Ctx& c, uint32_t* hdr) {
+  if (!FUSED_DEFER || c.set == 0) return;
+  float v[1];
+  poll<1, true>(loc_of(c, 0) + LO_QKV, 1, [](int k) { return k; }, c.E, v, hdr);
+}
+
 // Reduce-scatter of block l's MLP projection by a unit of the set that computes
 // block l+1: every wave polls its share of the terms (rs_pr_poll), then after a
 // workgroup barrier wave 0 forms x_{l+1}[o] = x1_l[o] + (sum + bias) and publishes
@@ -687,6 +699,7 @@ __device__ void regular_compute(const FusedArgs& a, FusedSmem& S, const Ctx& c, 
   U.cwn = NCW * (NQ - c.nh);
   U.cw = (wave - 1) * (NQ - c.nh) + (c.q - c.nh);
   const int l0 = c.set;
+  defer_set1(c, a.header);
   load_block<Q8>(R, S.pr, a.w, l0, U, wave);
   wg_barrier();  // B0
   for (int l = l0; l < L; l += 2) {
@@ -836,6 +849,8 @@ __device__ void head_unit(const FusedArgs& a, FusedSmem& S, const Ctx& c, WRegs<
   const int l0 = c.set;
   u64* sinkw = a.sinkw + ((size_t)blockIdx.x * 8 + wave) * 16;
   float bo = 0.0f, bpr = 0.0f, xr = 0.0f;
+  if (wave == 0) defer_set1(c, hdr);
+  wg_barrier();
   load_o_head<Q8>(R, (char*)&S.pr, a.w, l0, h);
   stage_kv(a, S, l0, h);
   if (wave == 0) {
