@@ -184,7 +184,7 @@ int gpt2_test_quantize(const float* x_dev, int n, int8_t* codes_dev, float* scal
 int gpt2_test_special(int kind, uint32_t first_bits, size_t n, float* y, void* stream);
 
 /* C[M][N] = A[M][K] * W[N][K]^T with the prefill matrix-core kernel
- * (M 1..128, N a multiple of 32, K a multiple of 16). */
+ * (M 1..128, N a multiple of 32, K a multiple of 32). */
 int gpt2_test_gemm(const float* A_dev, const float* W_dev, float* C_dev, int M, int N, int K, void* stream);
 
 /* Bytes of the capture buffer of gpt2_q8_cached_step_capture. */

@@ -183,7 +183,7 @@ int gpt2_test_special(int kind, uint32_t first_bits, size_t n, float* y, void* s
 }
 
 int gpt2_test_gemm(const float* A, const float* W, float* C, int M, int N, int K, void* stream) {
-  if (!A || !W || !C || M < 1 || M > PMAX || N < 32 || N % 32 || K < 16 || K % 16) return GPT2_EARG;
+  if (!A || !W || !C || M < 1 || M > PMAX || N < 32 || N % 32 || K < 32 || K % 32) return GPT2_EARG;
   return launch_gemm_test(A, W, C, M, N, K, (hipStream_t)stream) == hipSuccess ? GPT2_OK : GPT2_EHIP;
 }
 

@@ -2,11 +2,11 @@
 // as row batches through the 12 blocks; only the final row reaches the tied head.
 //
 // The block projections are dense T x K by K x N contractions on the fp32 matrix
-// cores (v_mfma_f32_16x16x4_f32).  With T <= 128 rows every projection is short
-// and wide, so each wavefront owns a 32 x 32 output tile over a slice of K and
-// streams both operands straight from memory into registers, four 16-deep K steps
-// ahead; the K dimension is split so that every projection launches about 200
-// workgroups or fewer, one per compute unit.  The split partial sums are
+// cores (v_mfma_f32_32x32x2_f32).  With T <= 128 rows every projection is short
+// and wide: a workgroup owns all rows and 32 or 64 output columns over a slice of
+// K, stages both operands through LDS, and the K dimension is split so that every
+// projection launches about 200 workgroups, one per compute unit.  The split
+// partial sums are
 // added in a fixed order by the kernel that applies the epilogue (bias, GELU,
 // residual, and the LayerNorm that follows a residual), so results do not depend
 // on timing.  Causal attention stages each head's key/value rows in LDS once per
@@ -16,90 +16,123 @@
 
 namespace g2 {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 enum Epi { EPI_STORE = 0, EPI_PART = 1 };
 
+// Tile geometry of k_gemm.  A workgroup owns all GM = 128 rows of the row batch
+// and NT output columns (NT = 64: eight waves, NT = 32: four), over one slice of
+// K.  The slice is streamed in stages of GK = 32 elements: the 128 activation
+// rows and NT weight rows of a stage (128 bytes each) are loaded with coalesced
+// 16-byte reads (eight consecutive threads read one row), held in registers PF
+// stages ahead, and written to one of two LDS buffers.  Chunk c (16 bytes) of
+// staged row r sits at LDS slot c ^ (r % 8) of that row, so that the eight lanes
+// of an MFMA operand read, which take the same chunk of eight consecutive rows,
+// hit distinct banks.
+constexpr int GK = 32;
+constexpr int GM = 128;
+template <int NT>
+struct GemmCfg {
+  static constexpr int NW = 4 * NT / 32;        // waves: row quarter x column half
+  static constexpr int NTH = 64 * NW;
+  static constexpr int ROWS = GM + NT;          // staged rows per stage
+  static constexpr int U = ROWS * 8 / NTH;      // 16-byte chunks per thread per stage
+  static constexpr int UA = GM * 8 / NTH;       // of which activation chunks (u < UA)
+  static constexpr int BUF = ROWS * GK * 4;     // bytes of one LDS buffer
+  static_assert(U * NTH == ROWS * 8, "whole chunks per thread");
+};
+
 // C = A[M][K] * W[N][K]^T over the K range [z*klen, (z+1)*klen) (z = blockIdx.y).
-// Workgroup: 4 waves, wave w owns rows 32w..32w+31 and the workgroup's 32 columns
-// n0 = 32*blockIdx.x.  Rows at or past M read row M-1 and store nothing.
-// MFMA 16x16x4 f32 operand layout: lane l supplies A[l%16][kk] and B[kk][l%16]
-// with kk = l/16; result register r of lane l is C[4*(l/16) + r][l%16].  Within a
-// 16-wide K step, sub-step s feeds kk = l/16 the element k + 4*(l/16) + s to both
-// operands, so each lane reads four consecutive K elements as one 16-byte load
-// and the four sub-steps cover the step's 16 elements once each.
-// PF steps are in flight per wave.  Every loop pass issues the same loads (past
-// the last step they re-read it), so the compiler's wait counts stay exact and a
-// wait never drains the prefetches behind it.
-// EPI_STORE: C = acc + bias (bias may be null);
-// EPI_PART: part[z][row][col] = acc (ldc = N).
-template <int EPI, int PF>
-__global__ __launch_bounds__(256) void k_mm(const float* __restrict__ A, int lda, const float* __restrict__ W,
-                                           int ldw, int M, int N, const float* __restrict__ bias,
-                                           float* __restrict__ C, int ldc, int klen) {
+// Wave w computes rows 32(w%4)..+31 and columns n0 + 32(w/4)..+31 with
+// v_mfma_f32_32x32x2_f32: lane l supplies A[l%32][k] and B[k][l%32] for
+// k = l/32, and result register r of lane l is C[8(r/4) + 4(l/32) + r%4][l%32].
+// Within a stage, lane half h = l/32 reads chunk 2q + h (q < 4) of its operand
+// rows, and sub-step s of that chunk feeds element 8q + 4h + s, so the 32
+// elements of a stage are consumed once each; even and odd q accumulate into
+// separate registers, added at the end.  Rows at or past M read row M-1 and store
+// nothing.  Every loop pass issues the same loads (past the last stage they
+// re-read it), so the compiler's wait counts stay exact.
+// EPI_STORE: C = acc + bias (bias may be null); EPI_PART: part[z][row][col] = acc.
+template <int NT, int EPI, int PF>
+__global__ __launch_bounds__(GemmCfg<NT>::NTH) void k_gemm(const float* __restrict__ A, int lda,
+                                                          const float* __restrict__ W, int ldw, int M,
+                                                          const float* __restrict__ bias, float* __restrict__ C,
+                                                          int ldc, int klen) {
+  using G = GemmCfg<NT>;
+  static_assert(PF % 2 == 0, "the LDS buffer of a stage follows from the unrolled pass");
+  __shared__ __align__(16) char lds[2 * G::BUF];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int m0 = 32 * wave;
-  if (m0 >= M) return;
-  const int n0 = 32 * blockIdx.x;
-  const int kbeg = blockIdx.y * klen;
-  const int r = lane & 15, kq = 4 * (lane >> 4);
-  const float* ap[2];
-  const float* bp[2];
+  const int n0 = NT * blockIdx.x, kbeg = blockIdx.y * klen;
+  const int nsteps = klen / GK;
+  const float* src[G::U];
+  int dst[G::U];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = min(m0 + 16 * i + r, M - 1);
-    ap[i] = A + (size_t)row * lda + kbeg + kq;
-    bp[i] = W + (size_t)(n0 + 16 * i + r) * ldw + kbeg + kq;
+  for (int u = 0; u < G::U; ++u) {
+    const int idx = (int)threadIdx.x + G::NTH * u, rr = idx >> 3, c = idx & 7;
+    src[u] = (u < G::UA ? A + (size_t)min(rr, M - 1) * lda : W + (size_t)(n0 + rr - GM) * ldw) + kbeg + 4 * c;
+    dst[u] = rr * (GK * 4) + 16 * (c ^ (rr & 7));
   }
-  f32x4 acc[2][2];
+  f4 pre[PF][G::U];
+  auto gload = [&](int slot, int t) {
+    const int o = GK * min(t, nsteps - 1);
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  const int nsteps = klen >> 4;
-  f4 ra[PF][2], rb[PF][2];
-  auto load = [&](int p, int t) {
-    const int o = 16 * min(t, nsteps - 1);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      ra[p][i] = *(const f4*)(ap[i] + o);
-      rb[p][i] = *(const f4*)(bp[i] + o);
-    }
+    for (int u = 0; u < G::U; ++u)  // weights are read once: no cache residency
+      pre[slot][u] = u < G::UA ? *(const f4*)(src[u] + o) : __builtin_nontemporal_load((const f4*)(src[u] + o));
   };
+  auto lstore = [&](int slot, int buf) {
 #pragma unroll
-  for (int p = 0; p < PF; ++p) load(p, p);
+    for (int u = 0; u < G::U; ++u) *(f4*)(lds + buf * G::BUF + dst[u]) = pre[slot][u];
+  };
+  const int wr = wave & 3, wc = wave >> 2, h = lane >> 5, sw = lane & 7;
+  const int aoff = (32 * wr + (lane & 31)) * (GK * 4), boff = (GM + 32 * wc + (lane & 31)) * (GK * 4);
+  f32x16 acc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0.0f;
+
+#pragma unroll
+  for (int p = 0; p < PF; ++p) gload(p, p);
+  lstore(0, 0);
+  gload(0, PF);
+  __syncthreads();
   for (int t0 = 0; t0 < nsteps; t0 += PF) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
       if (t0 + p < nsteps) {
+        const char* b = lds + (p & 1) * G::BUF;
+        f4 fa[4], fb[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int q = 0; q < 4; ++q) {
+          const int slot = 16 * ((2 * q + h) ^ sw);
+          fa[q] = *(const f4*)(b + aoff + slot);
+          fb[q] = *(const f4*)(b + boff + slot);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // all reads of the stage in flight before the first product
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(ra[p][i][s], rb[p][j][s], acc[i][j], 0, 0, 0);
+          for (int s = 0; s < 4; ++s)
+            acc[q & 1] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[q][s], fb[q][s], acc[q & 1], 0, 0, 0);
       }
-      load(p, t0 + p + PF);
+      const int nx = (p + 1) % PF;
+      lstore(nx, (p + 1) & 1);
+      gload(nx, t0 + p + 1 + PF);
+      __syncthreads();
     }
   }
+  const int col = n0 + 32 * wc + (lane & 31);
+  const float bv = (EPI == EPI_STORE && bias) ? bias[col] : 0.0f;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = m0 + 16 * i + 4 * (lane >> 4) + e;
-        const int col = n0 + 16 * j + r;
-        if (row >= M) continue;
-        const float v = acc[i][j][e];
-        if constexpr (EPI == EPI_PART) {
-          C[((size_t)blockIdx.y * M + row) * ldc + col] = v;
-        } else {
-          const float y = bias ? v + bias[col] : v;
-          C[(size_t)row * ldc + col] = y;
-        }
-      }
+  for (int r = 0; r < 16; ++r) {
+    const int row = 32 * wr + 8 * (r >> 2) + 4 * h + (r & 3);
+    if (row >= M) continue;
+    const float v = acc[0][r] + acc[1][r];
+    if constexpr (EPI == EPI_PART)
+      C[((size_t)blockIdx.y * M + row) * ldc + col] = v;
+    else
+      C[(size_t)row * ldc + col] = v + bv;
+  }
 }
 
 // out[t][n] = act(((part0 + part1) + ... + part{S-1}) + bias)  (fixed order), four
@@ -256,23 +289,25 @@ __global__ __launch_bounds__(256) void k_pf_attn(const float* __restrict__ qkv, 
 hipError_t launch_head_f32(const Weights& w, const float* x_row, float* logits, hipStream_t s);
 
 // Split-K factors: the K range of every projection is cut into S equal runs of
-// whole 16-element steps; N/32 column tiles x S workgroups per launch.
-constexpr int S_QKV = 3, S_O = 8, S_FC = 2, S_PR = 8;
+// whole GK-element stages; N/NT column tiles x S workgroups per launch.
+constexpr int S_QKV = 6, S_O = 8, S_FC = 4, S_PR = 8;
 static_assert((size_t)S_QKV * D3 * PMAX <= PF_PART_WORDS && (size_t)S_FC * F * PMAX <= PF_PART_WORDS &&
                   (size_t)S_O * D * PMAX <= PF_PART_WORDS && (size_t)S_PR * D * PMAX <= PF_PART_WORDS,
               "partial-sum buffer");
-static_assert(D % (16 * S_QKV) == 0 && D % (16 * S_O) == 0 && D % (16 * S_FC) == 0 && F % (16 * S_PR) == 0,
-              "split K ranges are whole 16-element steps");
+static_assert(D % (GK * S_QKV) == 0 && D % (GK * S_O) == 0 && D % (GK * S_FC) == 0 && F % (GK * S_PR) == 0,
+              "split K ranges are whole stages");
 
+// NT = 64 where N allows it, else 32 (N must be a multiple of 32, K of GK * split).
 template <int EPI>
 static void mm(const float* A, int lda, const float* W, int K, int M, int N, const float* bias, float* C, int ldc,
-               int split, hipStream_t s) {
-  const dim3 grid(N / 32, split);
-  const int klen = K / split, steps = klen / 16;
-  if (steps % 4 == 0)
-    hipLaunchKernelGGL((k_mm<EPI, 4>), grid, dim3(256), 0, s, A, lda, W, K, M, N, bias, C, ldc, klen);
+               int split, bool wide, hipStream_t s) {
+  const int klen = K / split;
+  if (wide)
+    hipLaunchKernelGGL((k_gemm<64, EPI, 2>), dim3(N / 64, split), dim3(GemmCfg<64>::NTH), 0, s, A, lda, W, K, M,
+                       bias, C, ldc, klen);
   else
-    hipLaunchKernelGGL((k_mm<EPI, 2>), grid, dim3(256), 0, s, A, lda, W, K, M, N, bias, C, ldc, klen);
+    hipLaunchKernelGGL((k_gemm<32, EPI, 2>), dim3(N / 32, split), dim3(GemmCfg<32>::NTH), 0, s, A, lda, W, K, M,
+                       bias, C, ldc, klen);
 }
 
 hipError_t launch_infer(const Weights& w, const Work& k, const uint32_t* toks, int n, float* logits,
@@ -282,17 +317,17 @@ hipError_t launch_infer(const Weights& w, const Work& k, const uint32_t* toks, i
   hipLaunchKernelGGL(k_pf_embed_ln, dim3(n), dim3(64), 0, s, w, tk, k.pf_x, small_p(w, 0, sp::LN1_G),
                      small_p(w, 0, sp::LN1_B), k.pf_h);
   for (int l = 0; l < L; ++l) {
-    mm<EPI_PART>(k.pf_h, D, f32_mat(w, l, M_QKV), D, n, D3, nullptr, k.pf_part, D3, S_QKV, s);
+    mm<EPI_PART>(k.pf_h, D, f32_mat(w, l, M_QKV), D, n, D3, nullptr, k.pf_part, D3, S_QKV, true, s);
     hipLaunchKernelGGL((k_pf_sum<false, S_QKV>), dim3((n * D3 / 4 + 255) / 256), dim3(256), 0, s, k.pf_part,
                        n * D3, D3, small_p(w, l, sp::B_QKV), k.pf_qkv);
     hipLaunchKernelGGL(k_pf_attn, dim3(H, (n + PF_ROWS - 1) / PF_ROWS), dim3(256), 0, s, k.pf_qkv, n, k.pf_att);
-    mm<EPI_PART>(k.pf_att, D, f32_mat(w, l, M_O), D, n, D, nullptr, k.pf_part, D, S_O, s);
+    mm<EPI_PART>(k.pf_att, D, f32_mat(w, l, M_O), D, n, D, nullptr, k.pf_part, D, S_O, false, s);
     hipLaunchKernelGGL(k_pf_resid_ln<S_O>, dim3(n), dim3(64), 0, s, k.pf_part, n, small_p(w, l, sp::B_O), k.pf_x,
                        small_p(w, l, sp::LN2_G), small_p(w, l, sp::LN2_B), k.pf_h);
-    mm<EPI_PART>(k.pf_h, D, f32_mat(w, l, M_FC), D, n, F, nullptr, k.pf_part, F, S_FC, s);
+    mm<EPI_PART>(k.pf_h, D, f32_mat(w, l, M_FC), D, n, F, nullptr, k.pf_part, F, S_FC, true, s);
     hipLaunchKernelGGL((k_pf_sum<true, S_FC>), dim3((n * F / 4 + 255) / 256), dim3(256), 0, s, k.pf_part, n * F,
                        F, small_p(w, l, sp::B_FC), k.pf_u);
-    mm<EPI_PART>(k.pf_u, F, f32_mat(w, l, M_PR), F, n, D, nullptr, k.pf_part, D, S_PR, s);
+    mm<EPI_PART>(k.pf_u, F, f32_mat(w, l, M_PR), F, n, D, nullptr, k.pf_part, D, S_PR, false, s);
     const bool last = l + 1 == L;
     hipLaunchKernelGGL(k_pf_resid_ln<S_PR>, dim3(n), dim3(64), 0, s, k.pf_part, n, small_p(w, l, sp::B_PR), k.pf_x,
                        last ? nullptr : small_p(w, l + 1, sp::LN1_G), last ? nullptr : small_p(w, l + 1, sp::LN1_B),
@@ -302,7 +337,7 @@ hipError_t launch_infer(const Weights& w, const Work& k, const uint32_t* toks, i
 }
 
 hipError_t launch_gemm_test(const float* A, const float* W, float* C, int M, int N, int K, hipStream_t s) {
-  mm<EPI_STORE>(A, K, W, K, M, N, nullptr, C, N, 1, s);
+  mm<EPI_STORE>(A, K, W, K, M, N, nullptr, C, N, 1, N % 64 == 0, s);
   return hipGetLastError();
 }
 
