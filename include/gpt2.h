@@ -175,6 +175,13 @@ void gpt2_test_fused_plain_launch(int on);
 /* Group-64 quantizer alone: n (a multiple of 64) values -> codes [n], scales [n/64]. */
 int gpt2_test_quantize(const float* x_dev, int n, int8_t* codes_dev, float* scales_dev, void* stream);
 
+/* The int8 path's LayerNorm (ordered sums, one rounding per operation, gamma/beta
+ * of 768 values), as the single-launch int8 step evaluates it with a whole
+ * workgroup: rows x 768 values x -> y, bit for bit the ordered loop's result for
+ * finite inputs.  rows 0 does nothing; rows < 0 is GPT2_EARG. */
+int gpt2_test_layernorm_seq(const float* x_dev, int rows, const float* gamma_dev, const float* beta_dev,
+                            float* y_dev, void* stream);
+
 /* The library's exponential (kind 0) or tanh (kind 1) of every binary32 value whose
  * bit pattern is first_bits + i, i < n, into y[i].  The exponential is the ordered
  * binary32 approximation the decode path uses (LeanExe GPT-2 README, numerical

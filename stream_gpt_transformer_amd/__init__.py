@@ -47,6 +47,7 @@ SIGNATURES = {
     "gpt2_test_quantize": (_i, [_vp, _i, _vp, _vp, _vp]),
     "gpt2_test_gemm": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
     "gpt2_test_special": (_i, [_i, _u32, _sz, _vp, _vp]),
+    "gpt2_test_layernorm_seq": (_i, [_vp, _i, _vp, _vp, _vp, _vp]),
     "gpt2_q8_capture_nbytes": (_sz, []),
     "gpt2_test_force_phase_kernels": (None, [_i]),
     "gpt2_test_fused_trace": (None, [_vp]),
@@ -148,6 +149,10 @@ def gpt2_test_quantize(x_dev, n, codes_dev, scales_dev, stream=0) -> int:
 
 def gpt2_test_special(kind, first_bits, n, y_dev, stream=0) -> int:
     return lib().gpt2_test_special(kind, first_bits, n, y_dev, stream)
+
+
+def gpt2_test_layernorm_seq(x_dev, rows, gamma_dev, beta_dev, y_dev, stream=0) -> int:
+    return lib().gpt2_test_layernorm_seq(x_dev, rows, gamma_dev, beta_dev, y_dev, stream)
 
 
 def gpt2_test_gemm(A_dev, W_dev, C_dev, M, N, K, stream=0) -> int:

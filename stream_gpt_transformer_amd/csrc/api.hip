@@ -177,6 +177,12 @@ int gpt2_test_quantize(const float* x, int n, int8_t* codes, float* scales, void
   return launch_quantize(x, n, codes, scales, (hipStream_t)stream) == hipSuccess ? GPT2_OK : GPT2_EHIP;
 }
 
+int gpt2_test_layernorm_seq(const float* x, int rows, const float* gamma, const float* beta, float* y,
+                            void* stream) {
+  if (rows < 0 || (rows && (!x || !gamma || !beta || !y))) return GPT2_EARG;
+  return launch_layernorm_seq(x, rows, gamma, beta, y, (hipStream_t)stream) == hipSuccess ? GPT2_OK : GPT2_EHIP;
+}
+
 int gpt2_test_special(int kind, uint32_t first_bits, size_t n, float* y, void* stream) {
   if ((kind != 0 && kind != 1) || n > ((size_t)1 << 32) - first_bits || (n && !y)) return GPT2_EARG;
   return launch_special_bits(kind, first_bits, (long long)n, y, (hipStream_t)stream) == hipSuccess ? GPT2_OK : GPT2_EHIP;

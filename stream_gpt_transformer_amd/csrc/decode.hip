@@ -249,6 +249,27 @@ __global__ __launch_bounds__(64) void k_quantize(const float* x, int8_t* codes, 
   if (lane == 0) scales[g] = s;
 }
 
+// The int8 path's LayerNorm by a 512-thread workgroup per row (test hook).
+__global__ __launch_bounds__(512) void k_layernorm_seq(const float* x, const float* gamma, const float* beta,
+                                                       float* y) {
+  __shared__ __align__(16) float xs[D];
+  __shared__ __align__(16) float ys[D];
+  __shared__ __align__(16) float tmp[D];
+  __shared__ __align__(16) float g[D];
+  __shared__ __align__(16) float b[D];
+  __shared__ __align__(16) float tab[SEQ_TAB_FLOATS];
+  const size_t o = (size_t)blockIdx.x * D;
+  for (int i = threadIdx.x; i < D; i += 512) {
+    xs[i] = x[o + i];
+    g[i] = gamma[i];
+    b[i] = beta[i];
+  }
+  __syncthreads();
+  layernorm_seq_wg(xs, g, b, ys, tmp, tab);
+  __syncthreads();
+  for (int i = threadIdx.x; i < D; i += 512) y[o + i] = ys[i];
+}
+
 // The specified exponential (kind 0) or tanh (kind 1) of the binary32 value whose
 // bit pattern is first + i (test hook).
 __global__ __launch_bounds__(256) void k_special_bits(int kind, uint32_t first, long long n, float* y) {
@@ -342,6 +363,12 @@ hipError_t launch_head_f32(const Weights& w, const float* x_row, float* logits, 
 
 hipError_t launch_special_bits(int kind, uint32_t first, long long n, float* y, hipStream_t s) {
   if (n > 0) hipLaunchKernelGGL(k_special_bits, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, kind, first, n, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_layernorm_seq(const float* x, int rows, const float* gamma, const float* beta, float* y,
+                                hipStream_t s) {
+  if (rows > 0) hipLaunchKernelGGL(k_layernorm_seq, dim3(rows), dim3(512), 0, s, x, gamma, beta, y);
   return hipGetLastError();
 }
 

@@ -375,6 +375,137 @@ __device__ __forceinline__ void layernorm_seq(const float* xs, const float* __re
   store_frag<3>(ys, d);
 }
 
+// ---- the same sequential sums, evaluated by a whole workgroup -----------------
+// seq_sum768_wg returns (((0 + t_0) + t_1) + ... + t_767), one binary32 rounding per
+// add, bit for bit the sequential loop's value for finite t, in about two thirds
+// of the loop's latency.  All 512 threads (8 waves) of the workgroup call it.
+//  1. Estimates: every wave forms the binary64 prefix sums of t (lane i sums
+//     t[12i..12i+11], then an inclusive scan over the lanes) and rounds the prefix
+//     at each segment start to binary32: E_k for segment k = t[96k..96k+95], k < 8.
+//  2. Candidates: lane j of wave k runs the ordered chain of segment k from the
+//     binary32 value j - 32 steps away from E_k (steps through consecutive
+//     representable values) and stores where it ends.
+//  3. Walk: with S_0 = +0 the true start of segment 0, wave 0 follows the segments
+//     in order.  If S_k is one of the 64 candidates of segment k, the chain that
+//     started exactly at S_k ended at S_(k+1); otherwise the wave runs the chain
+//     of segment k from S_k itself.
+// Every chain is the loop's own sequence of roundings from its start value, and a
+// candidate is used only when its start equals the loop's running sum, so the
+// estimates affect only how often step 3 runs a chain itself.  (The running sum
+// is never -0: it starts at +0 and a round-to-nearest sum is -0 only when both
+// operands are.)  tab is SEQ_TAB_FLOATS floats of LDS scratch; t must be in LDS
+// and not change during the call; the call has two workgroup barriers, and tab
+// may be written again after the caller's next one.
+__device__ __forceinline__ int f_ord(int bits) { return bits < 0 ? -(bits & 0x7fffffff) : bits; }
+__device__ __forceinline__ int f_from_ord(int o) { return o < 0 ? (int)(0x80000000u | (uint32_t)(-o)) : o; }
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_d0(double v) {  // lanes without a source read 0
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)b, CTRL, ROWS, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, ROWS, 0xf, false);
+  return __longlong_as_double(((long long)hi << 32) | (uint32_t)lo);
+}
+// s + t[0] + ... + t[95] in order (t in LDS; 32 values in flight while 32 are added).
+__device__ __forceinline__ float seq_chain96(float s, const float* t) {
+  f4 a[8], b[8];
+  lds_load32(a, t);
+  lds_load32(b, t + 32);
+  __builtin_amdgcn_sched_barrier(0);
+  seq_add32(s, a);
+  __builtin_amdgcn_sched_barrier(0);
+  lds_load32(a, t + 64);
+  __builtin_amdgcn_sched_barrier(0);
+  seq_add32(s, b);
+  __builtin_amdgcn_sched_barrier(0);
+  seq_add32(s, a);
+  return s;
+}
+constexpr int SEQ_NS = 8, SEQ_NC = 64, SEQ_LEN = 768 / SEQ_NS;
+constexpr int SEQ_TAB_STRIDE = 12;                         // floats per candidate row (bank spread)
+constexpr int SEQ_TAB_RESULT = SEQ_NC * SEQ_TAB_STRIDE;    // the sum, handed to every wave
+constexpr int SEQ_TAB_FLOATS = SEQ_TAB_RESULT + 4;
+__device__ __forceinline__ float seq_sum768_wg(const float* t, float* tab) {
+  const int lane = (int)(threadIdx.x & 63), wave = (int)(threadIdx.x >> 6);
+  // 1. binary64 prefix sums
+  double p;
+  {
+    const f4 a = *(const f4*)(t + 12 * lane), b = *(const f4*)(t + 12 * lane + 4), c = *(const f4*)(t + 12 * lane + 8);
+    p = (((double)a.x + (double)a.y) + ((double)a.z + (double)a.w)) +
+        (((double)b.x + (double)b.y) + ((double)b.z + (double)b.w)) +
+        (((double)c.x + (double)c.y) + ((double)c.z + (double)c.w));
+  }
+  p = p + dpp_d0<0x111, 0xf>(p);  // row_shr:1
+  p = p + dpp_d0<0x112, 0xf>(p);  // row_shr:2
+  p = p + dpp_d0<0x114, 0xf>(p);  // row_shr:4
+  p = p + dpp_d0<0x118, 0xf>(p);  // row_shr:8
+  p = p + dpp_d0<DPP_ROW_BCAST15, 0xa>(p);
+  p = p + dpp_d0<DPP_ROW_BCAST31, 0xc>(p);
+  const int ebits = __float_as_int((float)p);  // lane i: prefix through t[12i+11]
+  // 2. candidate chains: segment k = wave starts after lane 8k-1's prefix
+  {
+    const int ek = wave == 0 ? 0 : f_ord(__builtin_amdgcn_readlane(ebits, 8 * wave - 1));
+    const float start = __int_as_float(f_from_ord(ek + lane - SEQ_NC / 2));
+    tab[lane * SEQ_TAB_STRIDE + wave] = seq_chain96(start, t + SEQ_LEN * wave);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // 3. the walk, by wave 0 alone (its steps are scalar instructions, which the
+  // waves of a compute unit would otherwise queue for), then handed to every wave
+  // through LDS.
+  if (wave == 0) {
+    f4 tv[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) tv[i] = *(const f4*)(tab + lane * SEQ_TAB_STRIDE + 4 * i);
+    // Step k names the candidate whose start is the running sum S: with E the
+    // estimate, its index is ord(S) - ord(E) + 32.  When S and E have the same
+    // sign that is (bits(S) - bits(E)) + 32, or (bits(E) - bits(S)) + 32 for
+    // negative E, i.e. (bits(S) ^ m) - c with m = 0 or ~0 by the sign of E and c
+    // from E; an S of the other sign gives an index far out of range (the running
+    // sum is never -0) and counts as a miss.  All of it in wrapping 32-bit
+    // arithmetic.
+    uint32_t sm[SEQ_NS], sc[SEQ_NS];
+#pragma unroll
+    for (int k = 0; k < SEQ_NS; ++k) {
+      const int eb = k == 0 ? 0 : __builtin_amdgcn_readlane(ebits, 8 * k - 1);
+      sm[k] = eb < 0 ? 0xffffffffu : 0u;
+      sc[k] = eb < 0 ? ~((uint32_t)eb + (uint32_t)(SEQ_NC / 2)) : (uint32_t)eb - (uint32_t)(SEQ_NC / 2);
+      asm volatile("" : "+s"(sm[k]), "+s"(sc[k]));  // formed before the walk, not inside its steps
+    }
+    // The steps run straight through; a miss runs the segment's chain in place.
+    uint32_t sb = 0;
+#pragma unroll
+    for (int k = 0; k < SEQ_NS; ++k) {
+      const uint32_t dd = (sb ^ sm[k]) - sc[k];
+      if (__builtin_expect(dd < (uint32_t)SEQ_NC, 1))
+        sb = (uint32_t)__builtin_amdgcn_readlane(__float_as_int(tv[k / 4][k % 4]), (int)dd);
+      else
+        sb = (uint32_t)__builtin_amdgcn_readfirstlane(
+            __float_as_int(seq_chain96(__uint_as_float(sb), t + SEQ_LEN * k)));
+    }
+    if (lane == 0) tab[SEQ_TAB_RESULT] = __uint_as_float(sb);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  return tab[SEQ_TAB_RESULT];
+}
+
+// The sequential LayerNorm of layernorm_seq by all 512 threads of a workgroup, with
+// both sums taken by seq_sum768_wg: the same output bits.  xs, ys (LDS, distinct),
+// tmp (768 floats) and tab of LDS scratch.  ys is complete for the
+// workgroup after the caller's next barrier.  tab: SEQ_TAB_FLOATS floats.
+__device__ __forceinline__ void layernorm_seq_wg(const float* xs, const float* __restrict__ gamma,
+                                                 const float* __restrict__ beta, float* ys, float* tmp, float* tab) {
+  const float mean = seq_sum768_wg(xs, tab) / 768.0f;
+  const int T = (int)threadIdx.x;
+  f4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (T < 192) {
+    d = *(const f4*)(xs + 4 * T) - mean;
+    *(f4*)(tmp + 4 * T) = d * d;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  const float var = seq_sum768_wg(tmp, tab) / 768.0f;
+  const float r = 1.0f / sqrtf(var + 1e-5f);
+  if (T < 192) *(f4*)(ys + 4 * T) = (d * r) * *(const f4*)(gamma + 4 * T) + *(const f4*)(beta + 4 * T);
+}
+
 // LayerNorm of a 768-vector in LDS by one wave (layernorm_frag), written to ys
 // (which may be xs).
 __device__ __forceinline__ void layernorm_lds(const float* xs, const float* __restrict__ gamma,

@@ -456,6 +456,11 @@ struct FusedSmem {
     PrLds pr;           // regular units, fp32
   };
 };
+// int8 path: the candidate table of the workgroup LayerNorm sums.  It shares the
+// union: int8 regular units keep no weights in LDS, and head units take a
+// LayerNorm only after their last attention.
+__device__ __forceinline__ float* seq_tab(FusedSmem& S) { return reinterpret_cast<float*>(&S.pr); }
+static_assert(sizeof(PrLds) >= SEQ_TAB_FLOATS * sizeof(float), "LayerNorm candidate table");
 
 // Per-workgroup constants.
 struct Ctx {
@@ -613,7 +618,7 @@ __device__ __forceinline__ void head_rows(const FusedArgs a, FusedSmem& S, WRegs
 // weights; waves 1..7 compute from registers (and the fp32 MLP weights from LDS).
 // The two roles meet at the same sequence of workgroup barriers.
 template <bool Q8, bool CAP>
-__device__ void regular_io(const FusedArgs& a, FusedSmem& S, const Ctx& c) {
+__device__ __forceinline__ void regular_io(const FusedArgs& a, FusedSmem& S, const Ctx& c) {
   const int lane = lane_id();
   uint32_t* hdr = a.header;
   const uint32_t E = c.E;
@@ -642,7 +647,10 @@ __device__ void regular_io(const FusedArgs& a, FusedSmem& S, const Ctx& c) {
       gather<12>(loc_of(c, l - 1) + LO_X2, E, S.xs, hdr);
     }
     if (lane == 0) stamp(a.trace, 1 + 4 * l);
-    if constexpr (Q8) layernorm_seq(S.xs, S.lnp[0], S.lnp[1], S.xn, S.lntmp);
+    if constexpr (Q8) {
+      wg_barrier();  // the block input is in LDS
+      layernorm_seq_wg(S.xs, S.lnp[0], S.lnp[1], S.xn, S.lntmp, seq_tab(S));
+    }
     wg_barrier();  // B1: QKV
     if constexpr (Q8) {
       wg_barrier();  // codes ready
@@ -652,7 +660,10 @@ __device__ void regular_io(const FusedArgs& a, FusedSmem& S, const Ctx& c) {
     dstamp(a.trace, l, 56);
     gather<12>(loc + LO_X1, E, S.x1s, hdr);
     if (lane == 0) stamp(a.trace, 3 + 4 * l);
-    if constexpr (Q8) layernorm_seq(S.x1s, S.lnp[2], S.lnp[3], S.xn, S.lntmp);
+    if constexpr (Q8) {
+      wg_barrier();  // x1 is in LDS
+      layernorm_seq_wg(S.x1s, S.lnp[2], S.lnp[3], S.xn, S.lntmp, seq_tab(S));
+    }
     wg_barrier();  // B3: FC
     if constexpr (Q8) {
       wg_barrier();
@@ -684,11 +695,10 @@ __device__ void regular_io(const FusedArgs& a, FusedSmem& S, const Ctx& c) {
   if (c.set == 0) rs_pr<Q8, CAP>(a, S, c, L - 1, bpr);
   gather<12>(loc_of(c, L - 1) + LO_X2, E, S.xs, hdr);
   if (lane == 0) stamp(a.trace, 49);
-  if constexpr (Q8) layernorm_seq(S.xs, S.lnf[0], S.lnf[1], S.xn, S.lntmp);
 }
 
 template <bool Q8, bool CAP>
-__device__ void regular_compute(const FusedArgs& a, FusedSmem& S, const Ctx& c, WRegs<Q8>& R, int wave) {
+__device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S, const Ctx& c, WRegs<Q8>& R, int wave) {
   const int lane = lane_id();
   const uint32_t E = c.E;
   u64* sinkw = a.sinkw + ((size_t)blockIdx.x * 8 + wave) * 16;
@@ -707,6 +717,10 @@ __device__ void regular_compute(const FusedArgs& a, FusedSmem& S, const Ctx& c, 
     u64* glb = glb_of(c, l);
     if (l > 0) rs_pr_poll<Q8>(a, S, c, l - 1, wave);
     wg_barrier();  // BA
+    if constexpr (Q8) {
+      wg_barrier();
+      layernorm_seq_wg(S.xs, S.lnp[0], S.lnp[1], S.xn, S.lntmp, seq_tab(S));
+    }
     wg_barrier();  // B1: QKV
     if (wave == 1) dstamp(a.trace, l, 59);
     if constexpr (Q8) {
@@ -742,6 +756,10 @@ __device__ void regular_compute(const FusedArgs& a, FusedSmem& S, const Ctx& c, 
       }
     }
     if (wave == 1 && lane == 0) stamp(a.trace, 2 + 4 * l);
+    if constexpr (Q8) {
+      wg_barrier();
+      layernorm_seq_wg(S.x1s, S.lnp[2], S.lnp[3], S.xn, S.lntmp, seq_tab(S));
+    }
     wg_barrier();  // B3: FC
     if constexpr (Q8) {
       quantize_groups(S, S.xn, 0, 0, D / 64, wave);
@@ -839,7 +857,7 @@ __device__ __forceinline__ void stage_kv(const FusedArgs& a, FusedSmem& S, int l
 }
 
 template <bool Q8, bool CAP>
-__device__ void head_unit(const FusedArgs& a, FusedSmem& S, const Ctx& c, WRegs<Q8>& R, int wave) {
+__device__ __forceinline__ void head_unit(const FusedArgs& a, FusedSmem& S, const Ctx& c, WRegs<Q8>& R, int wave) {
   const int lane = lane_id();
   uint32_t* hdr = a.header;
   const uint32_t E = c.E;
@@ -973,7 +991,6 @@ __device__ void head_unit(const FusedArgs& a, FusedSmem& S, const Ctx& c, WRegs<
     if (c.set == 0) rs_pr<Q8, CAP>(a, S, c, L - 1, bpr);
     gather<12>(loc_of(c, L - 1) + LO_X2, E, S.xs, hdr);
     if (lane == 0) stamp(a.trace, 49);
-    if constexpr (Q8) layernorm_seq(S.xs, S.lnf[0], S.lnf[1], S.xn, S.lntmp);
   }
 }
 
@@ -1009,8 +1026,10 @@ __global__ __launch_bounds__(FT, 1) void k_fused(const FusedArgs a) {
   // ---- the tied head: every wave takes its head rows (the first ones are in its
   // registers already, except on wave 0 of a regular unit)
   if (!c.head && wave == 0) load_head_slots<Q8>(R, a.w, hw);
-  wg_barrier();  // x12 (int8: its LayerNorm) is in LDS
+  wg_barrier();  // x12 is in LDS
   if constexpr (Q8) {
+    layernorm_seq_wg(S.xs, S.lnf[0], S.lnf[1], S.xn, S.lntmp, seq_tab(S));
+    wg_barrier();
     for (int g = wave; g < D / 64; g += NWV) {
       float s;
       const int qv = quant_lane(S.xn[g * 64 + lane], s);

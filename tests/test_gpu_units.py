@@ -118,3 +118,48 @@ def test_prefill_gemm_matches_float64(M, N, K):
     ref = A.astype(np.float64) @ W.astype(np.float64).T
     bound = 2 * K * 2.0 ** -24 * (np.abs(A).astype(np.float64) @ np.abs(W).T.astype(np.float64))
     assert np.all(np.abs(C.cpu().numpy() - ref) <= bound + 1e-30)
+
+
+WIDTH = 768  # model width: the LayerNorm length
+
+
+def _ln_rows(rng):
+    """Rows that stress the workgroup evaluation of the ordered LayerNorm sums: zero
+    mean (the running sum passes near 0, where its estimate is many steps off), a
+    large offset, outliers, magnitudes from 1e-30 to 1e15, exact zeros, constants,
+    cancelling pairs, and the residual-stream scale of the decode path."""
+    n = WIDTH
+    rows = [
+        rng.standard_normal(n),
+        0.03 * rng.standard_normal(n),
+        1000.0 + rng.standard_normal(n),
+        0.05 * rng.standard_normal(n) + (rng.random(n) < 0.01) * 30.0 * rng.standard_normal(n),
+        rng.standard_normal(n) * 10.0 ** rng.integers(-30, 15, n),
+        np.zeros(n),
+        np.full(n, 0.1),
+        np.repeat([1e7, -1e7], n // 2) + rng.standard_normal(n),
+        np.ravel(np.column_stack([rng.standard_normal(n // 2), -rng.standard_normal(n // 2)])),
+        1e-39 * rng.standard_normal(n),
+    ]
+    rows += [rng.standard_normal(n) * rng.uniform(0.01, 10) + rng.uniform(-1, 1) for _ in range(54)]
+    return np.stack(rows).astype(np.float32)
+
+
+def test_workgroup_sequential_layernorm_bit_exact():
+    """The int8 path's LayerNorm, evaluated by the workgroup speculation, against the
+    oracle's ordered loop: every output bit equal, on rows chosen so that the
+    speculation misses (and falls back) often as well as never."""
+    need_gpu()
+    rng = np.random.default_rng(1234)
+    x = _ln_rows(rng)
+    gam = (1.0 + 0.1 * rng.standard_normal(WIDTH)).astype(np.float32)
+    bet = (0.1 * rng.standard_normal(WIDTH)).astype(np.float32)
+    xd, gd, bd = (torch.from_numpy(a).cuda() for a in (x, gam, bet))
+    y = torch.full_like(xd, np.nan)
+    assert g.gpt2_test_layernorm_seq(xd.data_ptr(), x.shape[0], gd.data_ptr(), bd.data_ptr(), y.data_ptr(), 0) == 0
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    for r in range(x.shape[0]):
+        ref = oracle.layernorm(x[r].copy(), gam, bet)
+        assert np.array_equal(got[r].view(np.uint32), ref.view(np.uint32)), f"row {r}"
+    assert g.gpt2_test_layernorm_seq(0, 0, 0, 0, 0, 0) == 0  # no rows: nothing to do
