@@ -42,6 +42,45 @@ def step_bytes(fixed: int, p: int) -> int:
     return fixed + KV_PER_POS * (p + 1) + LOGITS
 
 
+# Measured memory traffic of the fp32 step kernel: a text summary under profiles/
+# (two rocprofv3 --pmc runs of `bench.py --pmc-probe`, FETCH_SIZE then WRITE_SIZE,
+# scaled by a plain copy of known size).  Its figures hold for the kernel sources
+# they name by SHA-256; after any change to those sources the traffic is unknown
+# (null) until the counters are taken again.
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_fused_f32_b1_traffic.md")
+KERNEL_SOURCES = ["fused.hip", "device.hpp", "internal.hpp", "layout.hpp"]
+PMC_COPY_BYTES = 256 << 20
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+    hsh = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "stream_gpt_transformer_amd", "csrc", name), "rb") as f:
+            hsh.update(f.read())
+    return hsh.hexdigest()
+
+
+def measured_traffic():
+    """Bytes per fp32 step launch from the committed counter summary, or None."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            text = f.read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].split(": ", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -49,6 +88,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=128)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU-oracle baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="for counter runs: 128 fp32 then 128 int8 steps (positions 0..127) and one "
+                         "device copy of 256 MiB, nothing timed or printed")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the decode step is a single-GPU path); got --gpus {args.gpus}",
@@ -93,6 +135,17 @@ def main() -> int:
         ms = e0.elapsed_time(e1)
         nbytes = sum(step_bytes(F32_FIXED if fn is g.gpt2_cached_step else Q8_FIXED, i % 128) for i in range(steps))
         return ms, nbytes
+
+    if args.pmc_probe:
+        run(g.gpt2_cached_step, 128)
+        run(g.gpt2_q8_cached_step, 128)
+        src = torch.ones(PMC_COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        m.close()
+        return 0
 
     ms32, b32 = timed(g.gpt2_cached_step, args.steps, args.warmup)
     ms8, b8 = timed(g.gpt2_q8_cached_step, args.steps, args.warmup)
@@ -149,7 +202,7 @@ def main() -> int:
         "config": {"workload": "GPT-2 124M batch-1 cachedStep, 128-position session, fp32",
                    "positions": "0..127 cycled", "batch": 1},
         "roofline": {"bound": "hbm", "achieved": round(gbs32, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs32 / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(gbs32 / HBM_PEAK_GBS, 4), "traffic": measured_traffic()},
         "int8_g64": {"value": round(tok8, 1), "unit": "tok/s", "ms_per_step": round(ms8 / args.steps, 5),
                      "roofline": {"bound": "hbm", "achieved": round(gbs8, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": round(gbs8 / HBM_PEAK_GBS, 4)}},
