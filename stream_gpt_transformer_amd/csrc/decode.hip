@@ -265,7 +265,7 @@ __global__ __launch_bounds__(512) void k_layernorm_seq(const float* x, const flo
     b[i] = beta[i];
   }
   __syncthreads();
-  layernorm_seq_wg(xs, g, b, ys, tmp, tab);
+  layernorm_seq_wg<2>(xs, g, b, ys, tmp, tab);
   __syncthreads();
   for (int i = threadIdx.x; i < D; i += 512) y[o + i] = ys[i];
 }

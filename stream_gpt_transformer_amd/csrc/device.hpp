@@ -424,6 +424,9 @@ constexpr int SEQ_NS = 8, SEQ_NC = 64, SEQ_LEN = 768 / SEQ_NS;
 constexpr int SEQ_TAB_STRIDE = 12;                         // floats per candidate row (bank spread)
 constexpr int SEQ_TAB_RESULT = SEQ_NC * SEQ_TAB_STRIDE;    // the sum, handed to every wave
 constexpr int SEQ_TAB_FLOATS = SEQ_TAB_RESULT + 4;
+// WALK: 1 if the calling wave is wave 0, 0 if it is not, 2 if that is known only
+// at run time (a wave that cannot be wave 0 carries none of the walk's code).
+template <int WALK>
 __device__ __forceinline__ float seq_sum768_wg(const float* t, float* tab) {
   const int lane = (int)(threadIdx.x & 63), wave = (int)(threadIdx.x >> 6);
   // 1. binary64 prefix sums
@@ -451,7 +454,7 @@ __device__ __forceinline__ float seq_sum768_wg(const float* t, float* tab) {
   // 3. the walk, by wave 0 alone (its steps are scalar instructions, which the
   // waves of a compute unit would otherwise queue for), then handed to every wave
   // through LDS.
-  if (wave == 0) {
+  if (WALK == 1 || (WALK == 2 && wave == 0)) {
     f4 tv[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) tv[i] = *(const f4*)(tab + lane * SEQ_TAB_STRIDE + 4 * i);
@@ -487,13 +490,44 @@ __device__ __forceinline__ float seq_sum768_wg(const float* t, float* tab) {
   return tab[SEQ_TAB_RESULT];
 }
 
+// The group-64 quantizer of quant_lane on a group held as 16 float4 by the 16
+// lanes of a DPP row (thread T holds elements 4T..4T+3, group T/16): the same
+// maximum (exact), scale m/127 and codes; codes go to xc[4T..4T+3], the scale of
+// group g to xsc[g].
+__device__ __forceinline__ int quant_code(float x, float s) {
+  float q = rintf(x / s);
+  if (q != q) q = 0.0f;
+  q = fminf(fmaxf(q, -127.0f), 127.0f);
+  return (int)q;
+}
+__device__ __forceinline__ void quant_frag16(const f4 y, int8_t* xc, float* xsc, int T) {
+  float m = fmaxf(fmaxf(fabsf(y.x), fabsf(y.y)), fmaxf(fabsf(y.z), fabsf(y.w)));
+  m = fmaxf(m, dpp_f<DPP_QUAD_1032>(m));
+  m = fmaxf(m, dpp_f<DPP_QUAD_2301>(m));
+  m = fmaxf(m, dpp_f<DPP_ROW_HALF_MIRROR>(m));
+  m = fmaxf(m, dpp_f<DPP_ROW_MIRROR>(m));
+  int packed = 0;
+  float s = 0.0f;
+  if (m != 0.0f) {
+    s = m / 127.0f;
+    packed = (quant_code(y.x, s) & 0xff) | (quant_code(y.y, s) & 0xff) << 8 | (quant_code(y.z, s) & 0xff) << 16 |
+             (quant_code(y.w, s) & 0xff) << 24;
+  }
+  *(int*)(xc + 4 * T) = packed;
+  if ((T & 15) == 0) xsc[T >> 4] = s;
+}
+
 // The sequential LayerNorm of layernorm_seq by all 512 threads of a workgroup, with
 // both sums taken by seq_sum768_wg: the same output bits.  xs, ys (LDS, distinct),
 // tmp (768 floats) and tab of LDS scratch.  ys is complete for the
-// workgroup after the caller's next barrier.  tab: SEQ_TAB_FLOATS floats.
+// workgroup after the caller's next barrier.  tab: SEQ_TAB_FLOATS floats.  WALK as
+// for seq_sum768_wg.  With xc given, the output is also quantized in groups of 64
+// (quant_frag16): codes into xc[0..767], scales into xsc[0..11].
+template <int WALK>
 __device__ __forceinline__ void layernorm_seq_wg(const float* xs, const float* __restrict__ gamma,
-                                                 const float* __restrict__ beta, float* ys, float* tmp, float* tab) {
-  const float mean = seq_sum768_wg(xs, tab) / 768.0f;
+                                                 const float* __restrict__ beta, float* ys, float* tmp, float* tab,
+                                                 int8_t* xc = nullptr, float* xsc = nullptr) {
+  const float mean = seq_sum768_wg<WALK>(xs, tab) / 768.0f;
   const int T = (int)threadIdx.x;
   f4 d = {0.0f, 0.0f, 0.0f, 0.0f};
   if (T < 192) {
@@ -501,9 +535,13 @@ __device__ __forceinline__ void layernorm_seq_wg(const float* xs, const float* _
     *(f4*)(tmp + 4 * T) = d * d;
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  const float var = seq_sum768_wg(tmp, tab) / 768.0f;
+  const float var = seq_sum768_wg<WALK>(tmp, tab) / 768.0f;
   const float r = 1.0f / sqrtf(var + 1e-5f);
-  if (T < 192) *(f4*)(ys + 4 * T) = (d * r) * *(const f4*)(gamma + 4 * T) + *(const f4*)(beta + 4 * T);
+  if (T < 192) {
+    const f4 y = (d * r) * *(const f4*)(gamma + 4 * T) + *(const f4*)(beta + 4 * T);
+    *(f4*)(ys + 4 * T) = y;
+    if (xc) quant_frag16(y, xc, xsc, T);
+  }
 }
 
 // LayerNorm of a 768-vector in LDS by one wave (layernorm_frag), written to ys
@@ -680,10 +718,7 @@ __device__ __forceinline__ int quant_lane(float x, float& s_out) {
   if (m == 0.0f) { s_out = 0.0f; return 0; }
   const float s = m / 127.0f;
   s_out = s;
-  float q = rintf(x / s);
-  if (q != q) q = 0.0f;
-  q = fminf(fmaxf(q, -127.0f), 127.0f);
-  return (int)q;
+  return quant_code(x, s);
 }
 
 // One output of an int8 group-64 projection with K inputs.  Lane l holds the row's

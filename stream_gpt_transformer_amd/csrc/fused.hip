@@ -649,11 +649,10 @@ __device__ __forceinline__ void regular_io(const FusedArgs& a, FusedSmem& S, con
     if (lane == 0) stamp(a.trace, 1 + 4 * l);
     if constexpr (Q8) {
       wg_barrier();  // the block input is in LDS
-      layernorm_seq_wg(S.xs, S.lnp[0], S.lnp[1], S.xn, S.lntmp, seq_tab(S));
+      layernorm_seq_wg<1>(S.xs, S.lnp[0], S.lnp[1], S.xn, S.lntmp, seq_tab(S), S.xc, S.xsc);
     }
-    wg_barrier();  // B1: QKV
+    wg_barrier();  // B1: QKV (int8: its input codes are in LDS)
     if constexpr (Q8) {
-      wg_barrier();  // codes ready
       if (cap0) capture_input(a, S, l, M_QKV, S.xn, 0, D, lane, 64);
     }
     xr = rs_o<Q8, CAP>(a, S, c, l, xr, bo);
@@ -662,11 +661,10 @@ __device__ __forceinline__ void regular_io(const FusedArgs& a, FusedSmem& S, con
     if (lane == 0) stamp(a.trace, 3 + 4 * l);
     if constexpr (Q8) {
       wg_barrier();  // x1 is in LDS
-      layernorm_seq_wg(S.x1s, S.lnp[2], S.lnp[3], S.xn, S.lntmp, seq_tab(S));
+      layernorm_seq_wg<1>(S.x1s, S.lnp[2], S.lnp[3], S.xn, S.lntmp, seq_tab(S), S.xc, S.xsc);
     }
-    wg_barrier();  // B3: FC
+    wg_barrier();  // B3: FC (int8: its input codes are in LDS)
     if constexpr (Q8) {
-      wg_barrier();
       if (cap0) capture_input(a, S, l, M_FC, S.xn, 0, D, lane, 64);
     }
     gather<GS / 64>(loc + LO_G, E, S.xg, hdr);
@@ -719,14 +717,10 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
     wg_barrier();  // BA
     if constexpr (Q8) {
       wg_barrier();
-      layernorm_seq_wg(S.xs, S.lnp[0], S.lnp[1], S.xn, S.lntmp, seq_tab(S));
+      layernorm_seq_wg<0>(S.xs, S.lnp[0], S.lnp[1], S.xn, S.lntmp, seq_tab(S), S.xc, S.xsc);
     }
     wg_barrier();  // B1: QKV
     if (wave == 1) dstamp(a.trace, l, 59);
-    if constexpr (Q8) {
-      quantize_groups(S, S.xn, 0, 0, D / 64, wave);
-      wg_barrier();
-    }
     {
       f4 x[3];
       if constexpr (!Q8) {
@@ -758,13 +752,9 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
     if (wave == 1 && lane == 0) stamp(a.trace, 2 + 4 * l);
     if constexpr (Q8) {
       wg_barrier();
-      layernorm_seq_wg(S.x1s, S.lnp[2], S.lnp[3], S.xn, S.lntmp, seq_tab(S));
+      layernorm_seq_wg<0>(S.x1s, S.lnp[2], S.lnp[3], S.xn, S.lntmp, seq_tab(S), S.xc, S.xsc);
     }
     wg_barrier();  // B3: FC
-    if constexpr (Q8) {
-      quantize_groups(S, S.xn, 0, 0, D / 64, wave);
-      wg_barrier();
-    }
     {
       f4 x[3];
       if constexpr (!Q8) {
@@ -1028,14 +1018,7 @@ __global__ __launch_bounds__(FT, 1) void k_fused(const FusedArgs a) {
   if (!c.head && wave == 0) load_head_slots<Q8>(R, a.w, hw);
   wg_barrier();  // x12 is in LDS
   if constexpr (Q8) {
-    layernorm_seq_wg(S.xs, S.lnf[0], S.lnf[1], S.xn, S.lntmp, seq_tab(S));
-    wg_barrier();
-    for (int g = wave; g < D / 64; g += NWV) {
-      float s;
-      const int qv = quant_lane(S.xn[g * 64 + lane], s);
-      S.xc[g * 64 + lane] = (int8_t)qv;
-      if (lane == 0) S.xsc[g] = s;
-    }
+    layernorm_seq_wg<2>(S.xs, S.lnf[0], S.lnf[1], S.xn, S.lntmp, seq_tab(S), S.xc, S.xsc);
     wg_barrier();
     if (CAP && blockIdx.x == 0 && wave == 0) capture_input(a, S, 0, M_HEAD, S.xn, 0, D, lane, 64);
   }
