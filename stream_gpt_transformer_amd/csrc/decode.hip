@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256) void k_proj(const ProjArgs a) {
 // at (source*12 + layer)*1536 + offset.
 template <bool SEQ>
 __global__ __launch_bounds__(128) void k_attn(const ProjArgs a) {
-  __shared__ AttnSmem sm;
+  __shared__ __align__(16) AttnSmem sm;
   const int h = blockIdx.x, b = blockIdx.y;
   const int npos = a.ss.pos[b] + 1;
   const float* cache = a.caches + (size_t)b * a.cache_stride;

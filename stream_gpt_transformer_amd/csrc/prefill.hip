@@ -204,69 +204,76 @@ __global__ __launch_bounds__(64) void k_pf_embed_ln(const Weights w, const Toks 
   store_frag<3>(h + (size_t)t * D, e);
 }
 
-constexpr int PF_ROWS = 8;  // query rows per attention workgroup (2 per wave)
+constexpr int PF_ROWS = 8;  // query rows per attention workgroup (one per wave)
+constexpr int PF_ATT_THREADS = 64 * PF_ROWS;
 
 struct PfAttnSmem {
-  float k[PMAX][DH + 4];
+  float k[PMAX][DH + 4];  // padded rows: lane j reading row j hits distinct banks
   float v[PMAX][DH];
-  float q[4][DH];
-  float w[4][PMAX];
+  float q[PF_ROWS][DH];
+  float w[PF_ROWS][PMAX + 4];  // padded: the eight rows' reads of one column hit distinct banks
+  float part[PF_ROWS][PF_ROWS][DH];  // per-wave partial weighted sums [wave][row][d]
 };
 
 // Causal attention of head blockIdx.x for query rows t0..t0+7 (t0 = 8*blockIdx.y)
-// over the row-batch QKV buffer [n][3D].  Wave w takes rows t0+w and t0+w+4: lane j
-// scores keys j and j+64, the softmax maximum and sum are wave reductions, and
-// lane d sums w_j * v_j[d] over j ascending.
-__global__ __launch_bounds__(256) void k_pf_attn(const float* __restrict__ qkv, int n, float* __restrict__ att) {
-  __shared__ PfAttnSmem sm;
+// over the row-batch QKV buffer [n][3D].  The key/value rows 0..t0+7 and the eight
+// query rows are staged in LDS once; wave w then takes row t = t0 + w: lane j
+// scores keys j and j+64 (four interleaved partial dot products), and the softmax
+// maximum and sum are wave reductions.  The weighted sums are split over the keys:
+// wave w sums keys 16w..16w+15 for all eight rows and 64 outputs (lane l: row l/8,
+// outputs 8(l%8)..+7), and the eight partial sums are added in wave order.
+__global__ __launch_bounds__(PF_ATT_THREADS) void k_pf_attn(const float* __restrict__ qkv, int n,
+                                                            float* __restrict__ att) {
+  __shared__ __align__(16) PfAttnSmem sm;
   const int h = blockIdx.x, t0 = PF_ROWS * blockIdx.y;
   const int tend = min(t0 + PF_ROWS, n);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  // Stage rows 0..tend-1: 16 threads per row, each 16 keys and 16 values.  All
-  // loads are issued before any store (indexes past the last row re-read it).
+  // Stage rows 0..tend-1: 16 threads per row, each 16 keys and 16 values, and the
+  // query rows (indexes past the last row re-read it; all loads before any store).
   {
-    constexpr int U = PMAX * 16 / 256;
-    f4 kk[U], vv[U];
+    constexpr int U = PMAX * 16 / PF_ATT_THREADS;
+    f4 kk[U], vv[U], qq;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int idx = threadIdx.x + 256 * u;
+      const int idx = threadIdx.x + PF_ATT_THREADS * u;
       const int j = min(idx >> 4, tend - 1), c = (idx & 15) * 4;
       const float* row = qkv + (size_t)j * D3 + h * DH;
       kk[u] = *(const f4*)(row + D + c);
       vv[u] = *(const f4*)(row + 2 * D + c);
     }
+    const int qr = threadIdx.x >> 4, qc = (threadIdx.x & 15) * 4;  // 128 threads: 8 rows x 16 float4
+    if (threadIdx.x < PF_ROWS * 16) qq = *(const f4*)(qkv + (size_t)min(t0 + qr, tend - 1) * D3 + h * DH + qc);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int idx = threadIdx.x + 256 * u;
+      const int idx = threadIdx.x + PF_ATT_THREADS * u;
       const int j = idx >> 4, c = (idx & 15) * 4;
       if (j < tend) {
         *(f4*)&sm.k[j][c] = kk[u];
         *(f4*)&sm.v[j][c] = vv[u];
       }
     }
+    if (threadIdx.x < PF_ROWS * 16) *(f4*)&sm.q[qr][qc] = qq;
   }
   __syncthreads();
-  for (int t = t0 + wave; t < tend; t += 4) {
-    sm.q[wave][lane] = qkv[(size_t)t * D3 + h * DH + lane];
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  const int t = t0 + wave;
+  if (t < tend) {
     float s[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int j = lane + 64 * u;
       s[u] = -INFINITY;
       if (j <= t) {
-        float acc = 0.0f;
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < DH / 4; ++i) {
-          const f4 kk = *(const f4*)&sm.k[j][4 * i];
-          const f4 qq = *(const f4*)&sm.q[wave][4 * i];
-          acc = acc + qq.x * kk.x;
-          acc = acc + qq.y * kk.y;
-          acc = acc + qq.z * kk.z;
-          acc = acc + qq.w * kk.w;
+          const f4 kv = *(const f4*)&sm.k[j][4 * i];
+          const f4 qv = *(const f4*)&sm.q[wave][4 * i];
+          acc[i & 3] = fmaf(qv.x, kv.x, acc[i & 3]);
+          acc[i & 3] = fmaf(qv.y, kv.y, acc[i & 3]);
+          acc[i & 3] = fmaf(qv.z, kv.z, acc[i & 3]);
+          acc[i & 3] = fmaf(qv.w, kv.w, acc[i & 3]);
         }
-        s[u] = acc * 0.125f;
+        s[u] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * 0.125f;
       }
     }
     const float m = wave_max(fmaxf(s[0], s[1]));
@@ -276,13 +283,46 @@ __global__ __launch_bounds__(256) void k_pf_attn(const float* __restrict__ qkv, 
     const float Z = wave_sum(e[0] + e[1]);
 #pragma unroll
     for (int u = 0; u < 2; ++u) sm.w[wave][lane + 64 * u] = e[u] / Z;
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    float o = 0.0f;
-#pragma unroll 8
-    for (int j = 0; j <= t; ++j) o = o + sm.w[wave][j] * sm.v[j][lane];
-    att[(size_t)t * D + h * DH + lane] = o;
-    __builtin_amdgcn_wave_barrier();
+  } else {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) sm.w[wave][lane + 64 * u] = 0.0f;
+  }
+  __syncthreads();
+  // weighted sums over keys 16w..16w+15 (weights past a row's own position are 0;
+  // keys past tend-1 are not staged and contribute nothing)
+  {
+    const int r = lane >> 3, d0 = 8 * (lane & 7), j0 = 16 * wave;
+    f4 o0 = {0.0f, 0.0f, 0.0f, 0.0f}, o1 = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (j0 < tend) {
+#pragma unroll
+      for (int jj = 0; jj < 16; jj += 4) {
+        const f4 wv = *(const f4*)&sm.w[r][j0 + jj];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = min(j0 + jj + i, tend - 1);  // a weight-0 key past tend-1 reads the last staged row
+          const float wj = i == 0 ? wv.x : i == 1 ? wv.y : i == 2 ? wv.z : wv.w;
+          const f4 v0 = *(const f4*)&sm.v[j][d0], v1 = *(const f4*)&sm.v[j][d0 + 4];
+          o0.x = fmaf(wj, v0.x, o0.x);
+          o0.y = fmaf(wj, v0.y, o0.y);
+          o0.z = fmaf(wj, v0.z, o0.z);
+          o0.w = fmaf(wj, v0.w, o0.w);
+          o1.x = fmaf(wj, v1.x, o1.x);
+          o1.y = fmaf(wj, v1.y, o1.y);
+          o1.z = fmaf(wj, v1.z, o1.z);
+          o1.w = fmaf(wj, v1.w, o1.w);
+        }
+      }
+    }
+    *(f4*)&sm.part[wave][r][d0] = o0;
+    *(f4*)&sm.part[wave][r][d0 + 4] = o1;
+  }
+  __syncthreads();
+  {
+    const int r = threadIdx.x >> 6, d = threadIdx.x & 63;  // one output per thread
+    float acc = sm.part[0][r][d];
+#pragma unroll
+    for (int w2 = 1; w2 < PF_ROWS; ++w2) acc = acc + sm.part[w2][r][d];
+    if (t0 + r < tend) att[(size_t)(t0 + r) * D + h * DH + d] = acc;
   }
 }
 
@@ -320,7 +360,7 @@ hipError_t launch_infer(const Weights& w, const Work& k, const uint32_t* toks, i
     mm<EPI_PART>(k.pf_h, D, f32_mat(w, l, M_QKV), D, n, D3, nullptr, k.pf_part, D3, S_QKV, true, s);
     hipLaunchKernelGGL((k_pf_sum<false, S_QKV>), dim3((n * D3 / 4 + 255) / 256), dim3(256), 0, s, k.pf_part,
                        n * D3, D3, small_p(w, l, sp::B_QKV), k.pf_qkv);
-    hipLaunchKernelGGL(k_pf_attn, dim3(H, (n + PF_ROWS - 1) / PF_ROWS), dim3(256), 0, s, k.pf_qkv, n, k.pf_att);
+    hipLaunchKernelGGL(k_pf_attn, dim3(H, (n + PF_ROWS - 1) / PF_ROWS), dim3(PF_ATT_THREADS), 0, s, k.pf_qkv, n, k.pf_att);
     mm<EPI_PART>(k.pf_att, D, f32_mat(w, l, M_O), D, n, D, nullptr, k.pf_part, D, S_O, false, s);
     hipLaunchKernelGGL(k_pf_resid_ln<S_O>, dim3(n), dim3(64), 0, s, k.pf_part, n, small_p(w, l, sp::B_O), k.pf_x,
                        small_p(w, l, sp::LN2_G), small_p(w, l, sp::LN2_B), k.pf_h);
