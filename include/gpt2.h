@@ -194,6 +194,12 @@ int gpt2_test_special(int kind, uint32_t first_bits, size_t n, float* y, void* s
  * (M 1..128, N a multiple of 32, K a multiple of 32). */
 int gpt2_test_gemm(const float* A_dev, const float* W_dev, float* C_dev, int M, int N, int K, void* stream);
 
+/* C[M][N] = A[M][K] * W[N][K]^T + bias[N], then tanh-GELU when gelu is 1, with the
+ * prefill's full-K kernel for the wide projections (M 1..128, N a multiple of 16,
+ * K a multiple of 32; gelu 0 or 1). */
+int gpt2_test_gemm_bias(const float* A_dev, const float* W_dev, const float* bias_dev, float* C_dev, int M, int N,
+                        int K, int gelu, void* stream);
+
 /* Bytes of the capture buffer of gpt2_q8_cached_step_capture. */
 size_t gpt2_q8_capture_nbytes(void);
 

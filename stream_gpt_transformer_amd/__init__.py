@@ -46,6 +46,7 @@ SIGNATURES = {
     "gpt2_infer": (_i, [_vp, _vp, _i, _vp, _vp, _vp]),
     "gpt2_test_quantize": (_i, [_vp, _i, _vp, _vp, _vp]),
     "gpt2_test_gemm": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
+    "gpt2_test_gemm_bias": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
     "gpt2_test_special": (_i, [_i, _u32, _sz, _vp, _vp]),
     "gpt2_test_layernorm_seq": (_i, [_vp, _i, _vp, _vp, _vp, _vp]),
     "gpt2_q8_capture_nbytes": (_sz, []),
@@ -157,6 +158,10 @@ def gpt2_test_layernorm_seq(x_dev, rows, gamma_dev, beta_dev, y_dev, stream=0) -
 
 def gpt2_test_gemm(A_dev, W_dev, C_dev, M, N, K, stream=0) -> int:
     return lib().gpt2_test_gemm(A_dev, W_dev, C_dev, M, N, K, stream)
+
+
+def gpt2_test_gemm_bias(A_dev, W_dev, bias_dev, C_dev, M, N, K, gelu, stream=0) -> int:
+    return lib().gpt2_test_gemm_bias(A_dev, W_dev, bias_dev, C_dev, M, N, K, gelu, stream)
 
 
 def gpt2_test_force_phase_kernels(on: bool) -> None:

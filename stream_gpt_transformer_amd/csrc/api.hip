@@ -193,6 +193,13 @@ int gpt2_test_gemm(const float* A, const float* W, float* C, int M, int N, int K
   return launch_gemm_test(A, W, C, M, N, K, (hipStream_t)stream) == hipSuccess ? GPT2_OK : GPT2_EHIP;
 }
 
+int gpt2_test_gemm_bias(const float* A, const float* W, const float* bias, float* C, int M, int N, int K, int gelu,
+                        void* stream) {
+  if (!A || !W || !bias || !C || M < 1 || M > PMAX || N < 16 || N % 16 || K < 32 || K % 32 || (gelu != 0 && gelu != 1))
+    return GPT2_EARG;
+  return launch_gemm16_test(A, W, bias, C, M, N, K, gelu != 0, (hipStream_t)stream) == hipSuccess ? GPT2_OK : GPT2_EHIP;
+}
+
 void gpt2_test_force_phase_kernels(int on) { g_force_phase_kernels = on != 0; }
 
 void gpt2_test_fused_trace(void* trace_dev) { g_fused_trace = (uint64_t*)trace_dev; }

@@ -67,6 +67,8 @@ hipError_t launch_special_bits(int kind, uint32_t first, long long n, float* y, 
 hipError_t launch_layernorm_seq(const float* x, int rows, const float* gamma, const float* beta, float* y,
                                 hipStream_t s);
 hipError_t launch_quantize(const float* x, int n, int8_t* codes, float* scales, hipStream_t s);
+hipError_t launch_gemm16_test(const float* A, const float* W, const float* bias, float* C, int M, int N, int K,
+                              bool gelu, hipStream_t s);
 hipError_t launch_gemm_test(const float* A, const float* W, float* C, int M, int N, int K, hipStream_t s);
 
 }  // namespace g2

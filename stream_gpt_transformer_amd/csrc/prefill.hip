@@ -3,13 +3,13 @@
 //
 // The block projections are dense T x K by K x N contractions on the fp32 matrix
 // cores (v_mfma_f32_32x32x2_f32).  With T <= 128 rows every projection is short
-// and wide: a workgroup owns all rows and 32 or 64 output columns over a slice of
-// K, stages both operands through LDS, and the K dimension is split so that every
-// projection launches about 200 workgroups, one per compute unit.  The split
-// partial sums are
-// added in a fixed order by the kernel that applies the epilogue (bias, GELU,
-// residual, and the LayerNorm that follows a residual), so results do not depend
-// on timing.  Causal attention stages each head's key/value rows in LDS once per
+// and wide: a workgroup owns all rows and 16, 32 or 64 output columns, stages both
+// operands through LDS, and launches about 150-200 workgroups, one per compute
+// unit.  The wide projections (QKV, FC) run over all of K in 16-column tiles with
+// the bias (and GELU) in the epilogue; the 768-output ones (O, MLP projection)
+// split K, and their partial sums are added in a fixed order by the kernel that
+// applies the residual and the LayerNorm that follows it, so results do not
+// depend on timing.  Causal attention stages each head's key/value rows in LDS once per
 // eight query rows.
 #include "device.hpp"
 #include "internal.hpp"
@@ -135,27 +135,128 @@ __global__ __launch_bounds__(GemmCfg<NT>::NTH) void k_gemm(const float* __restri
   }
 }
 
-// out[t][n] = act(((part0 + part1) + ... + part{S-1}) + bias)  (fixed order), four
-// consecutive elements per thread; all S loads are issued before the sum.
-template <bool GELU, int S>
-__global__ __launch_bounds__(256) void k_pf_sum(const float* __restrict__ part, int MN, int N,
-                                               const float* __restrict__ bias, float* __restrict__ out) {
-  const int i = 4 * (blockIdx.x * 256 + threadIdx.x);
-  if (i >= MN) return;
-  f4 p[S];
+// Narrow full-K variant for the wide projections (QKV, FC): a workgroup owns all
+// 128 rows and 16 output columns over the whole of K, so no split partial sums
+// and no reduction launch are needed; the epilogue adds the bias (and applies
+// GELU).  Eight waves, wave w computing rows 16w..16w+15 with
+// v_mfma_f32_16x16x4_f32: lane l supplies A[l%16][k] and B[k][l%16] with its
+// K-group kg = l/16, and result register r of lane l is C[4(l/16) + r][l%16].
+// K is staged KS elements at a time (CH = KS/4 chunks of 16 bytes per row, chunk c
+// of row r at slot c ^ (r % 8)); group kg reads chunks kg*CH/4 .. (kg+1)*CH/4 - 1 of
+// its operand rows, and product s (< KS/4) of a stage feeds element kg*KS/4 + s,
+// so a stage's elements are consumed once each.  Loads are held in registers PF
+// stages ahead; a pass reads the next stage's fragments before multiplying the
+// current one's, then stores stage t+2 into the buffer stage t occupied.  The
+// stage's 16 weight rows are read by the first 16*CH threads (the others re-read
+// one of those chunks and do not store it, so every thread issues the same loads).
+constexpr int G16_NTH = 512;
+template <int KS>
+struct G16 {
+  static constexpr int CH = KS / 4, ROWS = GM + 16, RB = KS * 4, BUF = ROWS * RB;
+  static constexpr int UA = GM * CH / G16_NTH, U = UA + 1, NB = 16 * CH;
+  static_assert(UA * G16_NTH == GM * CH && NB <= G16_NTH, "whole chunks per thread");
+};
+template <int KS, bool GELU, int PF>
+__global__ __launch_bounds__(G16_NTH) void k_gemm16(const float* __restrict__ A, int lda, const float* __restrict__ W,
+                                                   int ldw, int M, int K, const float* __restrict__ bias,
+                                                   float* __restrict__ C, int ldc) {
+  using G = G16<KS>;
+  static_assert(PF % 2 == 0, "the LDS buffer of a stage follows from the unrolled pass");
+  extern __shared__ __align__(16) char lds[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n0 = 16 * blockIdx.x;
+  const int nsteps = K / KS;
+  const float* src[G::U];
+  int dst[G::U];
 #pragma unroll
-  for (int s = 0; s < S; ++s) p[s] = *(const f4*)(part + (size_t)s * MN + i);
-  f4 v = p[0];
-#pragma unroll
-  for (int s = 1; s < S; ++s) v = v + p[s];
-  v = v + *(const f4*)(bias + i % N);
-  if (GELU) {
-    v.x = gelu_tanh(v.x);
-    v.y = gelu_tanh(v.y);
-    v.z = gelu_tanh(v.z);
-    v.w = gelu_tanh(v.w);
+  for (int u = 0; u < G::U; ++u) {
+    const int idx = u < G::UA ? (int)threadIdx.x + G16_NTH * u : GM * G::CH + ((int)threadIdx.x % G::NB);
+    const int rr = idx / G::CH, c = idx % G::CH;
+    src[u] = (u < G::UA ? A + (size_t)min(rr, M - 1) * lda : W + (size_t)(n0 + rr - GM) * ldw) + 4 * c;
+    dst[u] = rr * G::RB + 16 * (c ^ (rr & 7));
   }
-  *(f4*)(out + i) = v;
+  const bool bstore = (int)threadIdx.x < G::NB;
+  f4 pre[PF][G::U];
+  auto gload = [&](int slot, int t) {
+    const int o = KS * min(t, nsteps - 1);
+#pragma unroll
+    for (int u = 0; u < G::U; ++u)
+      pre[slot][u] = u < G::UA ? *(const f4*)(src[u] + o) : __builtin_nontemporal_load((const f4*)(src[u] + o));
+  };
+  auto lstore = [&](int slot, int buf) {
+#pragma unroll
+    for (int u = 0; u < G::U; ++u)
+      if (u < G::UA || bstore) *(f4*)(lds + buf * G::BUF + dst[u]) = pre[slot][u];
+  };
+  constexpr int FR = G::CH / 4;  // chunks per K-group per stage
+  const int kg = lane >> 4, sw = lane & 7;
+  const int aoff = (16 * wave + (lane & 15)) * G::RB, boff = (GM + (lane & 15)) * G::RB;
+  auto lread = [&](f4 (&fa)[FR], f4 (&fb)[FR], int buf) {
+    const char* b = lds + buf * G::BUF;
+#pragma unroll
+    for (int h = 0; h < FR; ++h) {
+      const int slot = 16 * ((FR * kg + h) ^ sw);
+      fa[h] = *(const f4*)(b + aoff + slot);
+      fb[h] = *(const f4*)(b + boff + slot);
+    }
+  };
+  f4 acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+  f4 fa[2][FR], fb[2][FR];
+  // stages 0 and 1 into the two LDS buffers, stages 2..PF+1 in flight
+#pragma unroll
+  for (int p = 0; p < PF; ++p) gload(p, p);
+  lstore(0, 0);
+  gload(0, PF);
+  lstore(1, 1);
+  gload(1, PF + 1);
+  __syncthreads();
+  lread(fa[0], fb[0], 0);
+  __syncthreads();  // pass 0 overwrites buffer 0
+  for (int t0 = 0; t0 < nsteps; t0 += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      const int cur = p & 1;
+      lread(fa[cur ^ 1], fb[cur ^ 1], cur ^ 1);
+      if (t0 + p < nsteps) {
+#pragma unroll
+        for (int h = 0; h < FR; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[e & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[cur][h][e], fb[cur][h][e], acc[e & 1], 0, 0, 0);
+      }
+      const int sl = (p + 2) % PF;
+      lstore(sl, cur);
+      gload(sl, t0 + p + 2 + PF);
+      __syncthreads();
+    }
+  }
+  const int col = n0 + (lane & 15);
+  const float bv = bias[col];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 16 * wave + 4 * kg + r;
+    if (row >= M) continue;
+    float y = (acc[0][r] + acc[1][r]) + bv;
+    if (GELU) y = gelu_tanh(y);
+    C[(size_t)row * ldc + col] = y;
+  }
+}
+
+// Stage depth of the full-K kernel (K elements per LDS stage) and its launch.
+constexpr int G16_KS = 32;
+template <bool GELU>
+static hipError_t gemm16(const float* A, int lda, const float* W, int M, int N, int K, const float* bias, float* C,
+                         int ldc, hipStream_t s) {
+  constexpr size_t lds = 2 * (size_t)G16<G16_KS>::BUF;
+  static bool attr = false;
+  if (!attr) {
+    const hipError_t e =
+        hipFuncSetAttribute((const void*)k_gemm16<G16_KS, GELU, 2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL((k_gemm16<G16_KS, GELU, 2>), dim3(N / 16), dim3(G16_NTH), lds, s, A, lda, W, K, M, K, bias, C, ldc);
+  return hipGetLastError();
 }
 
 // One wave per row t: x[t] += (sum of the S parts, fixed order) + bias; then, when
@@ -330,12 +431,11 @@ hipError_t launch_head_f32(const Weights& w, const float* x_row, float* logits, 
 
 // Split-K factors: the K range of every projection is cut into S equal runs of
 // whole GK-element stages; N/NT column tiles x S workgroups per launch.
-constexpr int S_QKV = 6, S_O = 8, S_FC = 4, S_PR = 8;
-static_assert((size_t)S_QKV * D3 * PMAX <= PF_PART_WORDS && (size_t)S_FC * F * PMAX <= PF_PART_WORDS &&
-                  (size_t)S_O * D * PMAX <= PF_PART_WORDS && (size_t)S_PR * D * PMAX <= PF_PART_WORDS,
+constexpr int S_O = 8, S_PR = 8;
+static_assert((size_t)S_O * D * PMAX <= PF_PART_WORDS && (size_t)S_PR * D * PMAX <= PF_PART_WORDS,
               "partial-sum buffer");
-static_assert(D % (GK * S_QKV) == 0 && D % (GK * S_O) == 0 && D % (GK * S_FC) == 0 && F % (GK * S_PR) == 0,
-              "split K ranges are whole stages");
+static_assert(D % (GK * S_O) == 0 && F % (GK * S_PR) == 0, "split K ranges are whole stages");
+static_assert(D3 % 16 == 0 && F % 16 == 0 && D % G16_KS == 0, "k_gemm16 tiles");
 
 // NT = 64 where N allows it, else 32 (N must be a multiple of 32, K of GK * split).
 template <int EPI>
@@ -353,20 +453,18 @@ static void mm(const float* A, int lda, const float* W, int K, int M, int N, con
 hipError_t launch_infer(const Weights& w, const Work& k, const uint32_t* toks, int n, float* logits,
                         hipStream_t s) {
   Toks tk{};
+  hipError_t e;
   for (int t = 0; t < n; ++t) tk.t[t] = toks[t];
   hipLaunchKernelGGL(k_pf_embed_ln, dim3(n), dim3(64), 0, s, w, tk, k.pf_x, small_p(w, 0, sp::LN1_G),
                      small_p(w, 0, sp::LN1_B), k.pf_h);
   for (int l = 0; l < L; ++l) {
-    mm<EPI_PART>(k.pf_h, D, f32_mat(w, l, M_QKV), D, n, D3, nullptr, k.pf_part, D3, S_QKV, true, s);
-    hipLaunchKernelGGL((k_pf_sum<false, S_QKV>), dim3((n * D3 / 4 + 255) / 256), dim3(256), 0, s, k.pf_part,
-                       n * D3, D3, small_p(w, l, sp::B_QKV), k.pf_qkv);
+    if ((e = gemm16<false>(k.pf_h, D, f32_mat(w, l, M_QKV), n, D3, D, small_p(w, l, sp::B_QKV), k.pf_qkv, D3, s)))
+      return e;
     hipLaunchKernelGGL(k_pf_attn, dim3(H, (n + PF_ROWS - 1) / PF_ROWS), dim3(PF_ATT_THREADS), 0, s, k.pf_qkv, n, k.pf_att);
     mm<EPI_PART>(k.pf_att, D, f32_mat(w, l, M_O), D, n, D, nullptr, k.pf_part, D, S_O, false, s);
     hipLaunchKernelGGL(k_pf_resid_ln<S_O>, dim3(n), dim3(64), 0, s, k.pf_part, n, small_p(w, l, sp::B_O), k.pf_x,
                        small_p(w, l, sp::LN2_G), small_p(w, l, sp::LN2_B), k.pf_h);
-    mm<EPI_PART>(k.pf_h, D, f32_mat(w, l, M_FC), D, n, F, nullptr, k.pf_part, F, S_FC, true, s);
-    hipLaunchKernelGGL((k_pf_sum<true, S_FC>), dim3((n * F / 4 + 255) / 256), dim3(256), 0, s, k.pf_part, n * F,
-                       F, small_p(w, l, sp::B_FC), k.pf_u);
+    if ((e = gemm16<true>(k.pf_h, D, f32_mat(w, l, M_FC), n, F, D, small_p(w, l, sp::B_FC), k.pf_u, F, s))) return e;
     mm<EPI_PART>(k.pf_u, F, f32_mat(w, l, M_PR), F, n, D, nullptr, k.pf_part, D, S_PR, false, s);
     const bool last = l + 1 == L;
     hipLaunchKernelGGL(k_pf_resid_ln<S_PR>, dim3(n), dim3(64), 0, s, k.pf_part, n, small_p(w, l, sp::B_PR), k.pf_x,
@@ -374,6 +472,12 @@ hipError_t launch_infer(const Weights& w, const Work& k, const uint32_t* toks, i
                        k.pf_h);
   }
   return launch_head_f32(w, k.pf_x + (size_t)(n - 1) * D, logits, s);
+}
+
+hipError_t launch_gemm16_test(const float* A, const float* W, const float* bias, float* C, int M, int N, int K,
+                              bool gelu, hipStream_t s) {
+  if (K % G16_KS) return hipErrorInvalidValue;
+  return gelu ? gemm16<true>(A, K, W, M, N, K, bias, C, N, s) : gemm16<false>(A, K, W, M, N, K, bias, C, N, s);
 }
 
 hipError_t launch_gemm_test(const float* A, const float* W, float* C, int M, int N, int K, hipStream_t s) {

@@ -88,5 +88,8 @@ def test_test_hook_validation():
     assert g.gpt2_test_gemm(FAKE, FAKE, FAKE, 129, 64, 32) == g.GPT2_EARG
     assert g.gpt2_test_gemm(FAKE, FAKE, FAKE, 8, 65, 32) == g.GPT2_EARG
     assert g.gpt2_test_gemm(FAKE, FAKE, FAKE, 8, 64, 33) == g.GPT2_EARG
+    assert g.gpt2_test_gemm_bias(FAKE, FAKE, FAKE, FAKE, 8, 24, 32, 0) == g.GPT2_EARG
+    assert g.gpt2_test_gemm_bias(FAKE, FAKE, FAKE, FAKE, 8, 32, 48, 0) == g.GPT2_EARG
+    assert g.gpt2_test_gemm_bias(FAKE, FAKE, FAKE, FAKE, 8, 32, 64, 2) == g.GPT2_EARG
     assert g.gpt2_test_layernorm_seq(FAKE, -1, FAKE, FAKE, FAKE) == g.GPT2_EARG
     assert g.gpt2_test_layernorm_seq(0, 2, FAKE, FAKE, FAKE) == g.GPT2_EARG

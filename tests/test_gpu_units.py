@@ -120,6 +120,32 @@ def test_prefill_gemm_matches_float64(M, N, K):
     assert np.all(np.abs(C.cpu().numpy() - ref) <= bound + 1e-30)
 
 
+@pytest.mark.parametrize("M,N,K,gelu", [(128, 2304, 768, 0), (128, 3072, 768, 1), (77, 2304, 768, 0), (1, 16, 64, 1),
+                                        (33, 48, 128, 0)])
+def test_prefill_full_k_gemm_bias_gelu(M, N, K, gelu):
+    """The wide projections' kernel (all of K in 16-column tiles, bias and GELU in
+    the epilogue) against float64 products; with GELU, against the oracle's GELU of
+    the float64 result, within the GELU's slope times the product bound plus a few
+    ulps of its own rounding."""
+    need_gpu()
+    rng = np.random.default_rng(M * 11 + N + K + gelu)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    W = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    b = (0.1 * rng.standard_normal(N)).astype(np.float32)
+    Ad, Wd, bd = (torch.from_numpy(x).cuda() for x in (A, W, b))
+    C = torch.full((M, N), np.nan, dtype=torch.float32, device="cuda")
+    assert g.gpt2_test_gemm_bias(Ad.data_ptr(), Wd.data_ptr(), bd.data_ptr(), C.data_ptr(), M, N, K, gelu, 0) == 0
+    torch.cuda.synchronize()
+    got = C.cpu().numpy().astype(np.float64)
+    lin = A.astype(np.float64) @ W.astype(np.float64).T + b.astype(np.float64)
+    bound = 2 * (K + 1) * 2.0 ** -24 * (np.abs(A).astype(np.float64) @ np.abs(W).T.astype(np.float64) + np.abs(b))
+    if not gelu:
+        assert np.all(np.abs(got - lin) <= bound + 1e-30)
+    else:
+        ref = oracle.gelu(lin.astype(np.float32).ravel()).reshape(M, N).astype(np.float64)
+        assert np.all(np.abs(got - ref) <= 1.2 * bound + 8 * 2.0 ** -24 * np.abs(ref) + 1e-7)
+
+
 WIDTH = 768  # model width: the LayerNorm length
 
 
