@@ -154,6 +154,24 @@ def main() -> int:
     gbs32 = b32 / (ms32 * 1e-3) / 1e9
     gbs8 = b8 / (ms8 * 1e-3) / 1e9
 
+    # greedy generation on the device: an 8-token prompt and 120 chosen tokens
+    # (127 steps and 120 on-device choices per call), median of 5 calls
+    gprompt = toks[:8].tolist()
+    gcache = torch.zeros(128 * PER, dtype=torch.float32, device=dev)
+    gout = torch.empty(120, dtype=torch.int32, device=dev)
+    gst = torch.empty(1, dtype=torch.int32, device=dev)
+    gts = []
+    for i in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        m.generate(gcache, gprompt, 120, logits, gout, gst)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i:
+            gts.append(e0.elapsed_time(e1))
+    assert int(gst.item()) == 0
+    gms = statistics.median(gts)
+
     # prefill: median of 20 infer(128) calls after warm-up
     ptoks = synth.make_tokens(synth.SEED_PREFILL, 128).tolist()
     for _ in range(3):
@@ -206,6 +224,8 @@ def main() -> int:
         "int8_g64": {"value": round(tok8, 1), "unit": "tok/s", "ms_per_step": round(ms8 / args.steps, 5),
                      "roofline": {"bound": "hbm", "achieved": round(gbs8, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": round(gbs8 / HBM_PEAK_GBS, 4)}},
+        "generate": {"value": round(120 / (gms * 1e-3), 1), "unit": "tok/s", "ms_per_call": round(gms, 3),
+                     "sample": "fp32 greedy, 8-token prompt + 120 tokens chosen on the GPU (127 steps)"},
         "prefill": {"value": round(128 / (pms * 1e-3), 1), "unit": "tok/s", "ms_median": round(pms, 4),
                     "roofline": {"bound": "mfma", "achieved": round(PREFILL_FLOP / (pms * 1e-3) / 1e12, 2),
                                  "peak": FP32_MFMA_PEAK_TF, "unit": "TFLOP/s",

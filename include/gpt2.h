@@ -172,6 +172,29 @@ void gpt2_test_fused_trace(void* trace_dev);
  * cooperative one (its waits are bounded either way). */
 void gpt2_test_fused_plain_launch(int on);
 
+/* Greedy generation on the device.  The `lean` page's GPU path picks the next
+ * token on the GPU, so a step never waits for the logits to reach the host; the
+ * LeanExe README's command-line host generates a continuation greedily and rejects
+ * non-finite logits.
+ * Steps positions 0..n_prompt-1 with prompt (HOST array of n_prompt token ids),
+ * then feeds each step the first maximum of the previous step's logits, until
+ * n_gen tokens are chosen: tokens_out[i] (device, uint32[n_gen]) is the choice
+ * made from the logits of position n_prompt-1+i, and the last choice is not
+ * stepped, so positions 0..n_prompt+n_gen-2 are computed.  q8 = 0: fp32 steps
+ * (GPT2_PACK_F32); q8 = 1: int8 steps (GPT2_PACK_Q8).  cache (device) holds at
+ * least (n_prompt+n_gen-1) * 18,432 words; it starts empty (position 0) and ends
+ * holding those positions' rows.  logits receives the last step's logits.
+ * *status (device int32) is 0 when every step's logits were finite, else k+1 for
+ * the first step k (counted from the choice tokens_out[0]) whose logits held a
+ * non-finite value: that choice and every later one are 50,257 (no token) and the
+ * steps after it are fed token 0.  Everything is enqueued without host
+ * synchronisation.  Errors: GPT2_ETOKEN for n_prompt < 1, n_gen < 1,
+ * n_prompt+n_gen-1 > 128 or a prompt token >= 50,257; GPT2_ECACHE for a short or
+ * null cache; GPT2_ENOTPACKED; GPT2_EARG otherwise. */
+int gpt2_generate(const gpt2_model* model, float* cache_dev, size_t cache_capacity_nwords, const uint32_t* prompt,
+                  int n_prompt, int n_gen, int q8, void* ws_dev, float* logits_dev, uint32_t* tokens_out_dev,
+                  int32_t* status_dev, void* stream);
+
 /* Group-64 quantizer alone: n (a multiple of 64) values -> codes [n], scales [n/64]. */
 int gpt2_test_quantize(const float* x_dev, int n, int8_t* codes_dev, float* scales_dev, void* stream);
 

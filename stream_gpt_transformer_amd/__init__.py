@@ -44,6 +44,7 @@ SIGNATURES = {
     "gpt2_q8_cached_step": (_i, [_vp, _vp, _sz, _u32, ctypes.c_int32, _vp, _vp, _vp]),
     "gpt2_batched_cached_step": (_i, [_vp, _vp, _sz, _vp, _vp, _vp, _i, _vp, _vp, _vp]),
     "gpt2_infer": (_i, [_vp, _vp, _i, _vp, _vp, _vp]),
+    "gpt2_generate": (_i, [_vp, _vp, _sz, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "gpt2_test_quantize": (_i, [_vp, _i, _vp, _vp, _vp]),
     "gpt2_test_gemm": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
     "gpt2_test_gemm_bias": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
@@ -142,6 +143,13 @@ def gpt2_infer(model, tokens: Sequence[int], ws_dev, logits_dev, stream=0) -> in
     tk = _u32_array([t & 0xFFFFFFFF for t in tokens]) if len(tokens) else None
     return lib().gpt2_infer(model, ctypes.cast(tk, _vp) if tk is not None else None, len(tokens), ws_dev,
                             logits_dev, stream)
+
+
+def gpt2_generate(model, cache_dev, cache_capacity_nwords, prompt: Sequence[int], n_gen, q8, ws_dev, logits_dev,
+                  tokens_out_dev, status_dev, stream=0) -> int:
+    tk = _u32_array([t & 0xFFFFFFFF for t in prompt]) if len(prompt) else None
+    return lib().gpt2_generate(model, cache_dev, cache_capacity_nwords, ctypes.cast(tk, _vp) if tk is not None else None,
+                               len(prompt), n_gen, q8, ws_dev, logits_dev, tokens_out_dev, status_dev, stream)
 
 
 def gpt2_test_quantize(x_dev, n, codes_dev, scales_dev, stream=0) -> int:
@@ -259,6 +267,14 @@ class Model:
                                       self.ws.data_ptr(), logits.data_ptr(), _stream())
         if rc:
             raise Gpt2Error(rc, "gpt2_batched_cached_step")
+
+    def generate(self, cache, prompt, n_gen: int, logits, tokens_out, status, q8: bool = False) -> None:
+        """Greedy generation on the device (gpt2_generate): cache, logits, tokens_out
+        (uint32 or int32, n_gen) and status (int32, 1) are device tensors."""
+        rc = gpt2_generate(self.handle, cache.data_ptr(), cache.numel(), list(prompt), n_gen, 1 if q8 else 0,
+                           self.ws.data_ptr(), logits.data_ptr(), tokens_out.data_ptr(), status.data_ptr(), _stream())
+        if rc:
+            raise Gpt2Error(rc, "gpt2_generate")
 
     def infer(self, tokens, logits) -> None:
         rc = gpt2_infer(self.handle, list(tokens), self.ws.data_ptr(), logits.data_ptr(), _stream())

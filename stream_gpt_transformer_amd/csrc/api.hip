@@ -90,22 +90,29 @@ int gpt2_pack_weights(const void* ckpt_dev, size_t ckpt_nbytes, void* packed_dev
 
 void gpt2_release(gpt2_model* model) { delete model; }
 
-int gpt2_cached_step(const gpt2_model* m, float* cache, size_t cache_nwords, uint32_t token, int32_t pos,
-                     void* ws, float* logits, void* stream) {
-  const int rc = step_checks(m, GPT2_PACK_F32, cache, cache_nwords, token, pos, ws, logits);
-  if (rc) return rc;
+// One validated batch-1 step: the single-launch kernel, or the per-phase kernels
+// where it cannot run.  tokp: read the token from device memory instead.
+static int enqueue_step(const gpt2_model* m, bool q8, float* cache, uint32_t token, const uint32_t* tokp,
+                        int32_t pos, void* ws, float* logits, char* capture, hipStream_t s) {
   const Work k = work_ptrs(ws, MAX_BATCH);
   bool used = false;
-  if (!g_force_phase_kernels &&
-      launch_fused(false, m->w, k, token, pos, cache, logits, nullptr, (hipStream_t)stream, &used) != hipSuccess)
+  if (!g_force_phase_kernels && launch_fused(q8, m->w, k, token, pos, cache, logits, capture, s, &used, tokp) != hipSuccess)
     return GPT2_EHIP;
   if (used) return GPT2_OK;
   Sessions ss{};
   ss.B = 1;
   ss.tok[0] = token;
   ss.pos[0] = pos;
-  const hipError_t e = launch_step_f32(m->w, k, ss, cache, 0, logits, (hipStream_t)stream);
+  const hipError_t e = q8 ? launch_step_q8(m->w, k, ss, cache, logits, capture, s, tokp)
+                          : launch_step_f32(m->w, k, ss, cache, 0, logits, s, tokp);
   return e == hipSuccess ? GPT2_OK : GPT2_EHIP;
+}
+
+int gpt2_cached_step(const gpt2_model* m, float* cache, size_t cache_nwords, uint32_t token, int32_t pos,
+                     void* ws, float* logits, void* stream) {
+  const int rc = step_checks(m, GPT2_PACK_F32, cache, cache_nwords, token, pos, ws, logits);
+  if (rc) return rc;
+  return enqueue_step(m, false, cache, token, nullptr, pos, ws, logits, nullptr, (hipStream_t)stream);
 }
 
 static int q8_step(const gpt2_model* m, float* cache, size_t cache_nwords, uint32_t token, int32_t pos, void* ws,
@@ -113,18 +120,33 @@ static int q8_step(const gpt2_model* m, float* cache, size_t cache_nwords, uint3
   const int rc = step_checks(m, GPT2_PACK_Q8, cache, cache_nwords, token, pos, ws, logits);
   if (rc) return rc;
   if (capture && !aligned16(capture)) return GPT2_EARG;
-  const Work k = work_ptrs(ws, MAX_BATCH);
-  bool used = false;
-  if (!g_force_phase_kernels &&
-      launch_fused(true, m->w, k, token, pos, cache, logits, (char*)capture, (hipStream_t)stream, &used) != hipSuccess)
-    return GPT2_EHIP;
-  if (used) return GPT2_OK;
-  Sessions ss{};
-  ss.B = 1;
-  ss.tok[0] = token;
-  ss.pos[0] = pos;
-  const hipError_t e = launch_step_q8(m->w, k, ss, cache, logits, (char*)capture, (hipStream_t)stream);
-  return e == hipSuccess ? GPT2_OK : GPT2_EHIP;
+  return enqueue_step(m, true, cache, token, nullptr, pos, ws, logits, (char*)capture, (hipStream_t)stream);
+}
+
+int gpt2_generate(const gpt2_model* m, float* cache, size_t cache_capacity_nwords, const uint32_t* prompt,
+                  int n_prompt, int n_gen, int q8, void* ws, float* logits, uint32_t* tokens_out, int32_t* status,
+                  void* stream) {
+  if (!m || (q8 != 0 && q8 != 1)) return GPT2_EARG;
+  if (!(m->flags & (q8 ? GPT2_PACK_Q8 : GPT2_PACK_F32))) return GPT2_ENOTPACKED;
+  if (!prompt || n_prompt < 1 || n_gen < 1 || n_prompt + n_gen - 1 > PMAX) return GPT2_ETOKEN;
+  for (int t = 0; t < n_prompt; ++t)
+    if (prompt[t] >= (uint32_t)V) return GPT2_ETOKEN;
+  const int nsteps = n_prompt + n_gen - 1;
+  if (!cache || !aligned16(cache) || cache_capacity_nwords < (size_t)nsteps * CACHE_POS) return GPT2_ECACHE;
+  if (!ws || !aligned16(ws) || !logits || !aligned4(logits) || !tokens_out || !aligned4(tokens_out) || !status ||
+      !aligned4(status))
+    return GPT2_EARG;
+  const hipStream_t s = (hipStream_t)stream;
+  uint32_t* next = work_ptrs(ws, MAX_BATCH).header + HDR_WORD_NEXT_TOKEN;
+  for (int p = 0; p < nsteps; ++p) {
+    const bool fed = p >= n_prompt;
+    const int rc = enqueue_step(m, q8 != 0, cache, fed ? 0u : prompt[p], fed ? next : nullptr, p, ws, logits,
+                                nullptr, s);
+    if (rc) return rc;
+    if (p >= n_prompt - 1 && launch_argmax(logits, next, tokens_out, status, p - (n_prompt - 1), s) != hipSuccess)
+      return GPT2_EHIP;
+  }
+  return GPT2_OK;
 }
 
 int gpt2_q8_cached_step(const gpt2_model* m, float* cache, size_t cache_nwords, uint32_t token, int32_t pos,

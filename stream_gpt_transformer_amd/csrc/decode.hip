@@ -30,9 +30,10 @@ __device__ __forceinline__ T nt_load(const T* p) {
 }
 
 // x += wte[tok] + wpe[pos]: one block of 192 threads per session.
-__global__ __launch_bounds__(192) void k_embed(const Weights w, const Sessions ss, float* x) {
+__global__ __launch_bounds__(192) void k_embed(const Weights w, const Sessions ss, float* x, const uint32_t* tokp) {
   const int b = blockIdx.x, t = threadIdx.x;
-  const f4 e = *(const f4*)(w.wte + (size_t)ss.tok[b] * D + 4 * t);
+  const uint32_t tok = b == 0 && tokp ? min(*tokp, (uint32_t)V - 1) : ss.tok[b];
+  const f4 e = *(const f4*)(w.wte + (size_t)tok * D + 4 * t);
   const f4 p = *(const f4*)(w.wpe + (size_t)ss.pos[b] * D + 4 * t);
   *(f4*)(x + (size_t)b * D + 4 * t) = e + p;
 }
@@ -249,6 +250,61 @@ __global__ __launch_bounds__(64) void k_quantize(const float* x, int8_t* codes, 
   if (lane == 0) scales[g] = s;
 }
 
+// Greedy choice of one generation step (the `lean` page's GPU path: the next token
+// is picked on the GPU; LeanExe GPT-2 README, CLI paragraph: the host rejects
+// non-finite logits).  The first maximum of the 50,257 logits: each thread scans
+// indexes t, t+1024, ... keeping the first strictly larger value, and pairs are
+// combined by (larger value, then smaller index).  Any non-finite logit rejects the
+// step: status = step + 1 (the first such step), its token and every later one is
+// 50,257 (no token), and the fed token is 0.  Step 0 also resets the status.
+__global__ __launch_bounds__(1024) void k_argmax(const float* __restrict__ logits, uint32_t* next,
+                                                 uint32_t* tokens_out, int32_t* status, int step) {
+  __shared__ float sv[16];
+  __shared__ int si[16], sbad[16];
+  float bv = -INFINITY;
+  int bi = V, bad = 0;
+  for (int i = threadIdx.x; i < V; i += 1024) {
+    const float v = logits[i];
+    bad |= !__builtin_isfinite(v);
+    if (v > bv) {
+      bv = v;
+      bi = i;
+    }
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o);
+    const int oi = __shfl_xor(bi, o);
+    if (ov > bv || (ov == bv && oi < bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  bad = __any(bad) ? 1 : 0;
+  if (lane == 0) {
+    sv[wave] = bv;
+    si[wave] = bi;
+    sbad[wave] = bad;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w2 = 1; w2 < 16; ++w2) {
+      if (sv[w2] > bv || (sv[w2] == bv && si[w2] < bi)) {
+        bv = sv[w2];
+        bi = si[w2];
+      }
+      bad |= sbad[w2];
+    }
+    const int before = step == 0 ? 0 : *status;
+    uint32_t tok = (uint32_t)bi;
+    if (before != 0 || bad || bi >= V) tok = (uint32_t)V;
+    if (before == 0) *status = bad || bi >= V ? step + 1 : 0;
+    tokens_out[step] = tok;
+    *next = tok < (uint32_t)V ? tok : 0u;
+  }
+}
+
 // The int8 path's LayerNorm by a 512-thread workgroup per row (test hook).
 __global__ __launch_bounds__(512) void k_layernorm_seq(const float* x, const float* gamma, const float* beta,
                                                        float* y) {
@@ -303,7 +359,7 @@ static void launch_layers(ProjArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_step_f32(const Weights& w, const Work& k, const Sessions& ss, float* caches,
-                           size_t cache_stride, float* logits, hipStream_t s) {
+                           size_t cache_stride, float* logits, hipStream_t s, const uint32_t* tokp) {
   ProjArgs a{};
   a.w = w;
   a.k = k;
@@ -312,7 +368,7 @@ hipError_t launch_step_f32(const Weights& w, const Work& k, const Sessions& ss, 
   a.cache_stride = cache_stride;
   a.logits = logits;
   a.capture = nullptr;
-  hipLaunchKernelGGL(k_embed, dim3(ss.B), dim3(192), 0, s, w, ss, k.x);
+  hipLaunchKernelGGL(k_embed, dim3(ss.B), dim3(192), 0, s, w, ss, k.x, tokp);
   if (ss.B == 1)
     launch_layers<2, 1, 1>(a, s);
   else
@@ -328,7 +384,7 @@ static void launch_q8(const ProjArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_step_q8(const Weights& w, const Work& k, const Sessions& ss, float* cache,
-                          float* logits, char* capture, hipStream_t s) {
+                          float* logits, char* capture, hipStream_t s, const uint32_t* tokp) {
   ProjArgs a{};
   a.w = w;
   a.k = k;
@@ -337,7 +393,7 @@ hipError_t launch_step_q8(const Weights& w, const Work& k, const Sessions& ss, f
   a.cache_stride = 0;
   a.logits = logits;
   a.capture = capture;
-  hipLaunchKernelGGL(k_embed, dim3(1), dim3(192), 0, s, w, ss, k.x);
+  hipLaunchKernelGGL(k_embed, dim3(1), dim3(192), 0, s, w, ss, k.x, tokp);
   for (int l = 0; l < L; ++l) {
     a.layer = l;
     launch_q8<MODE_QKV, 2>(a, s);
@@ -369,6 +425,12 @@ hipError_t launch_special_bits(int kind, uint32_t first, long long n, float* y, 
 hipError_t launch_layernorm_seq(const float* x, int rows, const float* gamma, const float* beta, float* y,
                                 hipStream_t s) {
   if (rows > 0) hipLaunchKernelGGL(k_layernorm_seq, dim3(rows), dim3(512), 0, s, x, gamma, beta, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax(const float* logits, uint32_t* next, uint32_t* tokens_out, int32_t* status, int step,
+                         hipStream_t s) {
+  hipLaunchKernelGGL(k_argmax, dim3(1), dim3(1024), 0, s, logits, next, tokens_out, status, step);
   return hipGetLastError();
 }
 

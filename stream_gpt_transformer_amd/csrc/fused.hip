@@ -122,7 +122,11 @@ struct FusedArgs {
   uint64_t* trace;   // timeline test hook or null: [grid][64] timestamps
   uint32_t token;
   int32_t pos;
+  const uint32_t* tokp;  // when set, the token is read from here (a generation step)
 };
+__device__ __forceinline__ uint32_t step_token(const FusedArgs& a) {
+  return a.tokp ? min(*a.tokp, (uint32_t)V - 1) : a.token;
+}
 
 // Timeline test hook (100 MHz wall clock), per workgroup: 0 start; for block l
 // computed by the workgroup's set, 1+4l block input ready (head units: after their
@@ -499,11 +503,11 @@ __device__ __forceinline__ float embed(const FusedArgs& a, float* xs, int q) {
 #pragma unroll
     for (int j = 0; j < 12; ++j) {
       const int i = lane + 64 * j;
-      xs[i] = a.w.wte[(size_t)a.token * D + i] + a.w.wpe[(size_t)a.pos * D + i];
+      xs[i] = a.w.wte[(size_t)step_token(a) * D + i] + a.w.wpe[(size_t)a.pos * D + i];
     }
   }
   const int o = RSN * q + min(lane, RSN - 1);
-  return a.w.wte[(size_t)a.token * D + o] + a.w.wpe[(size_t)a.pos * D + o];
+  return a.w.wte[(size_t)step_token(a) * D + o] + a.w.wpe[(size_t)a.pos * D + o];
 }
 
 // Set 1 defers its first weight loads until set 0 has published its first QKV
@@ -1088,7 +1092,7 @@ static hipError_t fused_config(FusedConfig& c) {
 
 template <bool Q8, bool CAP>
 static hipError_t launch_fused_t(const Weights& w, const Work& k, uint32_t token, int32_t pos, float* cache,
-                                 float* logits, char* capture, hipStream_t s, bool* used) {
+                                 float* logits, char* capture, hipStream_t s, bool* used, const uint32_t* tokp) {
   *used = false;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -1107,6 +1111,7 @@ static hipError_t launch_fused_t(const Weights& w, const Work& k, uint32_t token
   a.trace = g_fused_trace;
   a.token = token;
   a.pos = pos;
+  a.tokp = tokp;
   void* args[] = {&a};
   if (g_fused_plain_launch)
     e = hipLaunchKernel((const void*)k_fused<Q8, CAP>, dim3(GRID), dim3(FT), args, sizeof(FusedSmem), s);
@@ -1117,10 +1122,10 @@ static hipError_t launch_fused_t(const Weights& w, const Work& k, uint32_t token
 }
 
 hipError_t launch_fused(bool q8, const Weights& w, const Work& k, uint32_t token, int32_t pos, float* cache,
-                        float* logits, char* capture, hipStream_t s, bool* used) {
-  if (!q8) return launch_fused_t<false, false>(w, k, token, pos, cache, logits, nullptr, s, used);
-  if (capture) return launch_fused_t<true, true>(w, k, token, pos, cache, logits, capture, s, used);
-  return launch_fused_t<true, false>(w, k, token, pos, cache, logits, nullptr, s, used);
+                        float* logits, char* capture, hipStream_t s, bool* used, const uint32_t* tokp) {
+  if (!q8) return launch_fused_t<false, false>(w, k, token, pos, cache, logits, nullptr, s, used, tokp);
+  if (capture) return launch_fused_t<true, true>(w, k, token, pos, cache, logits, capture, s, used, tokp);
+  return launch_fused_t<true, false>(w, k, token, pos, cache, logits, nullptr, s, used, tokp);
 }
 
 }  // namespace g2

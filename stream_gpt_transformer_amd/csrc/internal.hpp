@@ -52,14 +52,22 @@ struct Work {
 Work work_ptrs(void* ws, int max_batch);
 
 hipError_t launch_pack(const float* ckpt, char* packed, int flags, hipStream_t s);
+// Header word of the workspace that carries the token a generation step is fed
+// (written by k_argmax, read by the step's embedding).
+constexpr int HDR_WORD_NEXT_TOKEN = 3;
+
+// tokp: when given, session 0's token is read from device memory at run time
+// instead of ss.tok[0] / token.
 hipError_t launch_step_f32(const Weights& w, const Work& k, const Sessions& ss, float* caches,
-                           size_t cache_stride, float* logits, hipStream_t s);
+                           size_t cache_stride, float* logits, hipStream_t s, const uint32_t* tokp = nullptr);
 hipError_t launch_step_q8(const Weights& w, const Work& k, const Sessions& ss, float* cache,
-                          float* logits, char* capture, hipStream_t s);
+                          float* logits, char* capture, hipStream_t s, const uint32_t* tokp = nullptr);
+hipError_t launch_argmax(const float* logits, uint32_t* next, uint32_t* tokens_out, int32_t* status, int step,
+                         hipStream_t s);
 hipError_t launch_infer(const Weights& w, const Work& k, const uint32_t* toks, int n, float* logits,
                         hipStream_t s);
 hipError_t launch_fused(bool q8, const Weights& w, const Work& k, uint32_t token, int32_t pos, float* cache,
-                        float* logits, char* capture, hipStream_t s, bool* used);
+                        float* logits, char* capture, hipStream_t s, bool* used, const uint32_t* tokp = nullptr);
 extern bool g_force_phase_kernels;
 extern uint64_t* g_fused_trace;
 extern int g_fused_plain_launch;

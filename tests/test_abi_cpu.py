@@ -93,3 +93,7 @@ def test_test_hook_validation():
     assert g.gpt2_test_gemm_bias(FAKE, FAKE, FAKE, FAKE, 8, 32, 64, 2) == g.GPT2_EARG
     assert g.gpt2_test_layernorm_seq(FAKE, -1, FAKE, FAKE, FAKE) == g.GPT2_EARG
     assert g.gpt2_test_layernorm_seq(0, 2, FAKE, FAKE, FAKE) == g.GPT2_EARG
+
+
+def test_generate_validation_without_model():
+    assert g.gpt2_generate(None, FAKE, 20 * g.GPT2_CACHE_WORDS_PER_POS, [1, 2], 4, 0, FAKE, FAKE, FAKE, FAKE) == g.GPT2_EARG
