@@ -91,12 +91,14 @@ int gpt2_pack_weights(const void* ckpt_dev, size_t ckpt_nbytes, void* packed_dev
 void gpt2_release(gpt2_model* model) { delete model; }
 
 // One validated batch-1 step: the single-launch kernel, or the per-phase kernels
-// where it cannot run.  tokp: read the token from device memory instead.
+// where it cannot run.  tokp: read the token from device memory instead (it must be
+// the workspace header's word HDR_WORD_NEXT_TOKEN).
 static int enqueue_step(const gpt2_model* m, bool q8, float* cache, uint32_t token, const uint32_t* tokp,
                         int32_t pos, void* ws, float* logits, char* capture, hipStream_t s) {
   const Work k = work_ptrs(ws, MAX_BATCH);
   bool used = false;
-  if (!g_force_phase_kernels && launch_fused(q8, m->w, k, token, pos, cache, logits, capture, s, &used, tokp) != hipSuccess)
+  if (!g_force_phase_kernels &&
+      launch_fused(q8, m->w, k, token, pos, cache, logits, capture, s, &used, tokp != nullptr) != hipSuccess)
     return GPT2_EHIP;
   if (used) return GPT2_OK;
   Sessions ss{};

@@ -122,11 +122,7 @@ struct FusedArgs {
   uint64_t* trace;   // timeline test hook or null: [grid][64] timestamps
   uint32_t token;
   int32_t pos;
-  const uint32_t* tokp;  // when set, the token is read from here (a generation step)
 };
-__device__ __forceinline__ uint32_t step_token(const FusedArgs& a) {
-  return a.tokp ? min(*a.tokp, (uint32_t)V - 1) : a.token;
-}
 
 // Timeline test hook (100 MHz wall clock), per workgroup: 0 start; for block l
 // computed by the workgroup's set, 1+4l block input ready (head units: after their
@@ -497,17 +493,21 @@ __device__ __forceinline__ void stage_ln(FusedSmem& S, const Weights& w, int l) 
 }
 
 // x = wte[token] + wpe[pos] into LDS (if xs) ; lanes < RSN return element RSN*q + lane.
+// TOKP (a generation step): the token is the one the previous step's greedy choice
+// left in the workspace header, not the launch argument.
+template <bool TOKP>
 __device__ __forceinline__ float embed(const FusedArgs& a, float* xs, int q) {
   const int lane = lane_id();
+  const uint32_t tok = TOKP ? min(ld32(&a.header[HDR_WORD_NEXT_TOKEN]), (uint32_t)V - 1) : a.token;
   if (xs) {
 #pragma unroll
     for (int j = 0; j < 12; ++j) {
       const int i = lane + 64 * j;
-      xs[i] = a.w.wte[(size_t)step_token(a) * D + i] + a.w.wpe[(size_t)a.pos * D + i];
+      xs[i] = a.w.wte[(size_t)tok * D + i] + a.w.wpe[(size_t)a.pos * D + i];
     }
   }
   const int o = RSN * q + min(lane, RSN - 1);
-  return a.w.wte[(size_t)step_token(a) * D + o] + a.w.wpe[(size_t)a.pos * D + o];
+  return a.w.wte[(size_t)tok * D + o] + a.w.wpe[(size_t)a.pos * D + o];
 }
 
 // Set 1 defers its first weight loads until set 0 has published its first QKV
@@ -621,7 +621,7 @@ __device__ __forceinline__ void head_rows(const FusedArgs a, FusedSmem& S, WRegs
 // Wave 0 receives (reduce-scatters, all-gathers, the int8 LayerNorm) and holds no
 // weights; waves 1..7 compute from registers (and the fp32 MLP weights from LDS).
 // The two roles meet at the same sequence of workgroup barriers.
-template <bool Q8, bool CAP>
+template <bool Q8, bool CAP, bool TOKP>
 __device__ __forceinline__ void regular_io(const FusedArgs& a, FusedSmem& S, const Ctx& c) {
   const int lane = lane_id();
   uint32_t* hdr = a.header;
@@ -644,7 +644,7 @@ __device__ __forceinline__ void regular_io(const FusedArgs& a, FusedSmem& S, con
     wg_barrier();  // BA: the reduce-scatter terms are in LDS
     dstamp(a.trace, l, 53);
     if (l == 0) {
-      xr = embed(a, S.xs, c.q);
+      xr = embed<TOKP>(a, S.xs, c.q);
     } else {
       xr = rs_pr<Q8, CAP>(a, S, c, l - 1, bpr);
       dstamp(a.trace, l, 54);
@@ -850,7 +850,7 @@ __device__ __forceinline__ void stage_kv(const FusedArgs& a, FusedSmem& S, int l
   attn_stage_rows(S.at, [&](int j) { return cl + (size_t)j * CACHE_POS; }, 0, a.pos, 0, FT);
 }
 
-template <bool Q8, bool CAP>
+template <bool Q8, bool CAP, bool TOKP>
 __device__ __forceinline__ void head_unit(const FusedArgs& a, FusedSmem& S, const Ctx& c, WRegs<Q8>& R, int wave) {
   const int lane = lane_id();
   uint32_t* hdr = a.header;
@@ -880,7 +880,7 @@ __device__ __forceinline__ void head_unit(const FusedArgs& a, FusedSmem& S, cons
     }
     if (wave == 0) {
       dstamp(a.trace, l, 52);
-      xr = l == 0 ? embed(a, nullptr, c.q) : rs_pr<Q8, CAP>(a, S, c, l - 1, bpr);
+      xr = l == 0 ? embed<TOKP>(a, nullptr, c.q) : rs_pr<Q8, CAP>(a, S, c, l - 1, bpr);
       if (lane == 0) stamp(a.trace, 1 + 4 * l);
       float v[3];
       poll<3, true>(loc_of(c, l) + LO_QKV + 192 * c.q, 192, [](int k) { return k; }, E, v, hdr);
@@ -988,7 +988,7 @@ __device__ __forceinline__ void head_unit(const FusedArgs& a, FusedSmem& S, cons
   }
 }
 
-template <bool Q8, bool CAP>
+template <bool Q8, bool CAP, bool TOKP>
 __global__ __launch_bounds__(FT, 1) void k_fused(const FusedArgs a) {
   extern __shared__ __align__(16) char smem_raw[];
   FusedSmem& S = *(FusedSmem*)smem_raw;
@@ -1013,8 +1013,8 @@ __global__ __launch_bounds__(FT, 1) void k_fused(const FusedArgs a) {
   const int hw = wave * GRID + (int)blockIdx.x;  // first head row of this wave
 
   WRegs<Q8> R;
-  if (c.head) head_unit<Q8, CAP>(a, S, c, R, wave);
-  else if (wave == 0) regular_io<Q8, CAP>(a, S, c);
+  if (c.head) head_unit<Q8, CAP, TOKP>(a, S, c, R, wave);
+  else if (wave == 0) regular_io<Q8, CAP, TOKP>(a, S, c);
   else regular_compute<Q8, CAP>(a, S, c, R, wave);
 
   // ---- the tied head: every wave takes its head rows (the first ones are in its
@@ -1069,11 +1069,11 @@ __global__ __launch_bounds__(FT, 1) void k_fused(const FusedArgs a) {
 struct FusedConfig {
   int ok;  // 1 usable, 0 not yet probed, -1 unusable (fall back to per-phase kernels)
 };
-static FusedConfig g_cfg[3][64];
+static FusedConfig g_cfg[5][64];
 uint64_t* g_fused_trace = nullptr;  // timeline test hook
 int g_fused_plain_launch = 1;       // 1: ordinary launch (default), 0: cooperative launch
 
-template <bool Q8, bool CAP>
+template <bool Q8, bool CAP, bool TOKP>
 static hipError_t fused_config(FusedConfig& c) {
   if (c.ok) return hipSuccess;
   int dev = 0, cus = 0;
@@ -1081,24 +1081,25 @@ static hipError_t fused_config(FusedConfig& c) {
   if ((e = hipGetDevice(&dev))) return e;
   if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev))) return e;
   const size_t lds = sizeof(FusedSmem);
-  if ((e = hipFuncSetAttribute((const void*)k_fused<Q8, CAP>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)))
+  if ((e = hipFuncSetAttribute((const void*)k_fused<Q8, CAP, TOKP>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)lds)))
     return e;
   int per_cu = 0;
-  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_fused<Q8, CAP>, FT, lds))) return e;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_fused<Q8, CAP, TOKP>, FT, lds))) return e;
   // One workgroup per compute unit, 32 per XCD: the grid is the whole chip.
   c.ok = (cus == GRID && per_cu >= 1) ? 1 : -1;
   return hipSuccess;
 }
 
-template <bool Q8, bool CAP>
+template <bool Q8, bool CAP, bool TOKP>
 static hipError_t launch_fused_t(const Weights& w, const Work& k, uint32_t token, int32_t pos, float* cache,
-                                 float* logits, char* capture, hipStream_t s, bool* used, const uint32_t* tokp) {
+                                 float* logits, char* capture, hipStream_t s, bool* used) {
   *used = false;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e) return e;
-  FusedConfig& c = g_cfg[Q8 ? (CAP ? 2 : 1) : 0][dev & 63];
-  if ((e = fused_config<Q8, CAP>(c))) return e;
+  FusedConfig& c = g_cfg[TOKP ? (Q8 ? 4 : 3) : Q8 ? (CAP ? 2 : 1) : 0][dev & 63];
+  if ((e = fused_config<Q8, CAP, TOKP>(c))) return e;
   if (c.ok != 1) return hipSuccess;
   FusedArgs a{};
   a.w = w;
@@ -1111,21 +1112,26 @@ static hipError_t launch_fused_t(const Weights& w, const Work& k, uint32_t token
   a.trace = g_fused_trace;
   a.token = token;
   a.pos = pos;
-  a.tokp = tokp;
   void* args[] = {&a};
   if (g_fused_plain_launch)
-    e = hipLaunchKernel((const void*)k_fused<Q8, CAP>, dim3(GRID), dim3(FT), args, sizeof(FusedSmem), s);
+    e = hipLaunchKernel((const void*)k_fused<Q8, CAP, TOKP>, dim3(GRID), dim3(FT), args, sizeof(FusedSmem), s);
   else
-    e = hipLaunchCooperativeKernel((const void*)k_fused<Q8, CAP>, dim3(GRID), dim3(FT), args, sizeof(FusedSmem), s);
+    e = hipLaunchCooperativeKernel((const void*)k_fused<Q8, CAP, TOKP>, dim3(GRID), dim3(FT), args, sizeof(FusedSmem),
+                                   s);
   if (e == hipSuccess) *used = true;
   return e;
 }
 
 hipError_t launch_fused(bool q8, const Weights& w, const Work& k, uint32_t token, int32_t pos, float* cache,
-                        float* logits, char* capture, hipStream_t s, bool* used, const uint32_t* tokp) {
-  if (!q8) return launch_fused_t<false, false>(w, k, token, pos, cache, logits, nullptr, s, used, tokp);
-  if (capture) return launch_fused_t<true, true>(w, k, token, pos, cache, logits, capture, s, used, tokp);
-  return launch_fused_t<true, false>(w, k, token, pos, cache, logits, nullptr, s, used, tokp);
+                        float* logits, char* capture, hipStream_t s, bool* used, bool device_token) {
+  if (device_token) {
+    if (capture) return hipErrorInvalidValue;
+    return q8 ? launch_fused_t<true, false, true>(w, k, token, pos, cache, logits, nullptr, s, used)
+              : launch_fused_t<false, false, true>(w, k, token, pos, cache, logits, nullptr, s, used);
+  }
+  if (!q8) return launch_fused_t<false, false, false>(w, k, token, pos, cache, logits, nullptr, s, used);
+  if (capture) return launch_fused_t<true, true, false>(w, k, token, pos, cache, logits, capture, s, used);
+  return launch_fused_t<true, false, false>(w, k, token, pos, cache, logits, nullptr, s, used);
 }
 
 }  // namespace g2

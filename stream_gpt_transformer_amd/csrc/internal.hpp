@@ -66,8 +66,10 @@ hipError_t launch_argmax(const float* logits, uint32_t* next, uint32_t* tokens_o
                          hipStream_t s);
 hipError_t launch_infer(const Weights& w, const Work& k, const uint32_t* toks, int n, float* logits,
                         hipStream_t s);
+// device_token: a generation step, whose token is the workspace header's word
+// HDR_WORD_NEXT_TOKEN (a separate kernel instantiation; capture must be null).
 hipError_t launch_fused(bool q8, const Weights& w, const Work& k, uint32_t token, int32_t pos, float* cache,
-                        float* logits, char* capture, hipStream_t s, bool* used, const uint32_t* tokp = nullptr);
+                        float* logits, char* capture, hipStream_t s, bool* used, bool device_token = false);
 extern bool g_force_phase_kernels;
 extern uint64_t* g_fused_trace;
 extern int g_fused_plain_launch;
