@@ -252,22 +252,30 @@ __global__ __launch_bounds__(64) void k_quantize(const float* x, int8_t* codes, 
 
 // Greedy choice of one generation step (the `lean` page's GPU path: the next token
 // is picked on the GPU; LeanExe GPT-2 README, CLI paragraph: the host rejects
-// non-finite logits).  The first maximum of the 50,257 logits: each thread scans
-// indexes t, t+1024, ... keeping the first strictly larger value, and pairs are
-// combined by (larger value, then smaller index).  Any non-finite logit rejects the
+// non-finite logits).  The first maximum of the 50,257 logits: each thread loads
+// indexes t, t+1024, ... at once and keeps the first strictly larger value, and
+// pairs are combined by (larger value, then smaller index).  Any non-finite logit rejects the
 // step: status = step + 1 (the first such step), its token and every later one is
 // 50,257 (no token), and the fed token is 0.  Step 0 also resets the status.
 __global__ __launch_bounds__(1024) void k_argmax(const float* __restrict__ logits, uint32_t* next,
                                                  uint32_t* tokens_out, int32_t* status, int step) {
   __shared__ float sv[16];
   __shared__ int si[16], sbad[16];
+  constexpr int PER = (V + 1023) / 1024;
+  float v[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {  // every load in flight before the first compare
+    const int i = threadIdx.x + 1024 * j;
+    v[j] = i < V ? logits[i] : -INFINITY;
+  }
   float bv = -INFINITY;
   int bi = V, bad = 0;
-  for (int i = threadIdx.x; i < V; i += 1024) {
-    const float v = logits[i];
-    bad |= !__builtin_isfinite(v);
-    if (v > bv) {
-      bv = v;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = threadIdx.x + 1024 * j;
+    bad |= i < V && !__builtin_isfinite(v[j]);
+    if (v[j] > bv) {
+      bv = v[j];
       bi = i;
     }
   }
