@@ -172,6 +172,18 @@ void gpt2_test_fused_trace(void* trace_dev);
  * cooperative one (its waits are bounded either way). */
 void gpt2_test_fused_plain_launch(int on);
 
+/* Prefill that hands the session over to the cached step.  This is an extension:
+ * the LeanExe README's infer returns logits only; the `lean` page's engine reuses
+ * a prefix's cache.  It is gpt2_infer, plus the key/value rows of positions
+ * 0..n-1 written into cache (device, at least n * 18,432 words) in the
+ * cachedStep layout, so the session continues with gpt2_cached_step at position
+ * n.  The rows are the ones the prefill's own attention used, so they are not
+ * bit-identical to rows built by n cached steps (the sums are ordered
+ * differently).  Errors: as gpt2_infer, and GPT2_ECACHE for a short or null
+ * cache. */
+int gpt2_prefill(const gpt2_model* model, const uint32_t* tokens, int n, float* cache_dev,
+                 size_t cache_capacity_nwords, void* ws_dev, float* logits_dev, void* stream);
+
 /* Greedy generation on the device.  The `lean` page's GPU path picks the next
  * token on the GPU, so a step never waits for the logits to reach the host; the
  * LeanExe README's command-line host generates a continuation greedily and rejects

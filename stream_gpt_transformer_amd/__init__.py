@@ -45,6 +45,7 @@ SIGNATURES = {
     "gpt2_batched_cached_step": (_i, [_vp, _vp, _sz, _vp, _vp, _vp, _i, _vp, _vp, _vp]),
     "gpt2_infer": (_i, [_vp, _vp, _i, _vp, _vp, _vp]),
     "gpt2_generate": (_i, [_vp, _vp, _sz, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
+    "gpt2_prefill": (_i, [_vp, _vp, _i, _vp, _sz, _vp, _vp, _vp]),
     "gpt2_test_quantize": (_i, [_vp, _i, _vp, _vp, _vp]),
     "gpt2_test_gemm": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp]),
     "gpt2_test_gemm_bias": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]),
@@ -143,6 +144,12 @@ def gpt2_infer(model, tokens: Sequence[int], ws_dev, logits_dev, stream=0) -> in
     tk = _u32_array([t & 0xFFFFFFFF for t in tokens]) if len(tokens) else None
     return lib().gpt2_infer(model, ctypes.cast(tk, _vp) if tk is not None else None, len(tokens), ws_dev,
                             logits_dev, stream)
+
+
+def gpt2_prefill(model, tokens: Sequence[int], cache_dev, cache_capacity_nwords, ws_dev, logits_dev, stream=0) -> int:
+    tk = _u32_array([t & 0xFFFFFFFF for t in tokens]) if len(tokens) else None
+    return lib().gpt2_prefill(model, ctypes.cast(tk, _vp) if tk is not None else None, len(tokens), cache_dev,
+                              cache_capacity_nwords, ws_dev, logits_dev, stream)
 
 
 def gpt2_generate(model, cache_dev, cache_capacity_nwords, prompt: Sequence[int], n_gen, q8, ws_dev, logits_dev,
@@ -275,6 +282,13 @@ class Model:
                            self.ws.data_ptr(), logits.data_ptr(), tokens_out.data_ptr(), status.data_ptr(), _stream())
         if rc:
             raise Gpt2Error(rc, "gpt2_generate")
+
+    def prefill(self, tokens, cache, logits) -> None:
+        """gpt2_prefill: infer over tokens, also filling cache (device float32) for them."""
+        rc = gpt2_prefill(self.handle, list(tokens), cache.data_ptr(), cache.numel(), self.ws.data_ptr(),
+                          logits.data_ptr(), _stream())
+        if rc:
+            raise Gpt2Error(rc, "gpt2_prefill")
 
     def infer(self, tokens, logits) -> None:
         rc = gpt2_infer(self.handle, list(tokens), self.ws.data_ptr(), logits.data_ptr(), _stream())

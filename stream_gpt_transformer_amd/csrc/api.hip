@@ -185,6 +185,19 @@ int gpt2_batched_cached_step(const gpt2_model* m, float* caches, size_t stride, 
   return e == hipSuccess ? GPT2_OK : GPT2_EHIP;
 }
 
+int gpt2_prefill(const gpt2_model* m, const uint32_t* tokens, int n, float* cache, size_t cache_capacity_nwords,
+                 void* ws, float* logits, void* stream) {
+  if (!m) return GPT2_EARG;
+  if (!(m->flags & GPT2_PACK_F32)) return GPT2_ENOTPACKED;
+  if (!tokens || n < 1 || n > PMAX) return GPT2_ETOKEN;
+  for (int t = 0; t < n; ++t)
+    if (tokens[t] >= (uint32_t)V) return GPT2_ETOKEN;
+  if (!cache || !aligned16(cache) || cache_capacity_nwords < (size_t)n * CACHE_POS) return GPT2_ECACHE;
+  if (!ws || !aligned16(ws) || !logits || !aligned4(logits)) return GPT2_EARG;
+  const hipError_t e = launch_infer(m->w, work_ptrs(ws, MAX_BATCH), tokens, n, logits, (hipStream_t)stream, cache);
+  return e == hipSuccess ? GPT2_OK : GPT2_EHIP;
+}
+
 int gpt2_infer(const gpt2_model* m, const uint32_t* tokens, int n, void* ws, float* logits, void* stream) {
   if (!m) return GPT2_EARG;
   if (!(m->flags & GPT2_PACK_F32)) return GPT2_ENOTPACKED;

@@ -64,8 +64,10 @@ hipError_t launch_step_q8(const Weights& w, const Work& k, const Sessions& ss, f
                           float* logits, char* capture, hipStream_t s, const uint32_t* tokp = nullptr);
 hipError_t launch_argmax(const float* logits, uint32_t* next, uint32_t* tokens_out, int32_t* status, int step,
                          hipStream_t s);
+// cache (or null): the key/value rows of positions 0..n-1 are also written there
+// in the cachedStep layout.
 hipError_t launch_infer(const Weights& w, const Work& k, const uint32_t* toks, int n, float* logits,
-                        hipStream_t s);
+                        hipStream_t s, float* cache = nullptr);
 // device_token: a generation step, whose token is the workspace header's word
 // HDR_WORD_NEXT_TOKEN (a separate kernel instantiation; capture must be null).
 hipError_t launch_fused(bool q8, const Weights& w, const Work& k, uint32_t token, int32_t pos, float* cache,

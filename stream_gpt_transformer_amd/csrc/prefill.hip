@@ -156,10 +156,13 @@ struct G16 {
   static constexpr int UA = GM * CH / G16_NTH, U = UA + 1, NB = 16 * CH;
   static_assert(UA * G16_NTH == GM * CH && NB <= G16_NTH, "whole chunks per thread");
 };
+// kv (QKV projection handing the session to the cached step, or null): outputs
+// col >= 768 (keys, then values) of row t also go to kv[t * 12 * 1536 + col - 768],
+// the cachedStep layout of position t for the layer kv points at.
 template <int KS, bool GELU, int PF>
 __global__ __launch_bounds__(G16_NTH) void k_gemm16(const float* __restrict__ A, int lda, const float* __restrict__ W,
                                                    int ldw, int M, int K, const float* __restrict__ bias,
-                                                   float* __restrict__ C, int ldc) {
+                                                   float* __restrict__ C, int ldc, float* __restrict__ kv) {
   using G = G16<KS>;
   static_assert(PF % 2 == 0, "the LDS buffer of a stage follows from the unrolled pass");
   extern __shared__ __align__(16) char lds[];
@@ -239,6 +242,7 @@ __global__ __launch_bounds__(G16_NTH) void k_gemm16(const float* __restrict__ A,
     float y = (acc[0][r] + acc[1][r]) + bv;
     if (GELU) y = gelu_tanh(y);
     C[(size_t)row * ldc + col] = y;
+    if (kv && col >= D) kv[(size_t)row * CACHE_POS + col - D] = y;
   }
 }
 
@@ -246,7 +250,7 @@ __global__ __launch_bounds__(G16_NTH) void k_gemm16(const float* __restrict__ A,
 constexpr int G16_KS = 32;
 template <bool GELU>
 static hipError_t gemm16(const float* A, int lda, const float* W, int M, int N, int K, const float* bias, float* C,
-                         int ldc, hipStream_t s) {
+                         int ldc, hipStream_t s, float* kv = nullptr) {
   constexpr size_t lds = 2 * (size_t)G16<G16_KS>::BUF;
   static bool attr = false;
   if (!attr) {
@@ -255,7 +259,8 @@ static hipError_t gemm16(const float* A, int lda, const float* W, int M, int N, 
     if (e) return e;
     attr = true;
   }
-  hipLaunchKernelGGL((k_gemm16<G16_KS, GELU, 2>), dim3(N / 16), dim3(G16_NTH), lds, s, A, lda, W, K, M, K, bias, C, ldc);
+  hipLaunchKernelGGL((k_gemm16<G16_KS, GELU, 2>), dim3(N / 16), dim3(G16_NTH), lds, s, A, lda, W, K, M, K, bias, C, ldc,
+                     kv);
   return hipGetLastError();
 }
 
@@ -451,14 +456,15 @@ static void mm(const float* A, int lda, const float* W, int K, int M, int N, con
 }
 
 hipError_t launch_infer(const Weights& w, const Work& k, const uint32_t* toks, int n, float* logits,
-                        hipStream_t s) {
+                        hipStream_t s, float* cache) {
   Toks tk{};
   hipError_t e;
   for (int t = 0; t < n; ++t) tk.t[t] = toks[t];
   hipLaunchKernelGGL(k_pf_embed_ln, dim3(n), dim3(64), 0, s, w, tk, k.pf_x, small_p(w, 0, sp::LN1_G),
                      small_p(w, 0, sp::LN1_B), k.pf_h);
   for (int l = 0; l < L; ++l) {
-    if ((e = gemm16<false>(k.pf_h, D, f32_mat(w, l, M_QKV), n, D3, D, small_p(w, l, sp::B_QKV), k.pf_qkv, D3, s)))
+    if ((e = gemm16<false>(k.pf_h, D, f32_mat(w, l, M_QKV), n, D3, D, small_p(w, l, sp::B_QKV), k.pf_qkv, D3, s,
+                           cache ? cache + (size_t)l * KV_ROW : nullptr)))
       return e;
     hipLaunchKernelGGL(k_pf_attn, dim3(H, (n + PF_ROWS - 1) / PF_ROWS), dim3(PF_ATT_THREADS), 0, s, k.pf_qkv, n, k.pf_att);
     mm<EPI_PART>(k.pf_att, D, f32_mat(w, l, M_O), D, n, D, nullptr, k.pf_part, D, S_O, false, s);

@@ -95,5 +95,9 @@ def test_test_hook_validation():
     assert g.gpt2_test_layernorm_seq(0, 2, FAKE, FAKE, FAKE) == g.GPT2_EARG
 
 
+def test_prefill_validation_without_model():
+    assert g.gpt2_prefill(None, [1, 2], FAKE, 2 * g.GPT2_CACHE_WORDS_PER_POS, FAKE, FAKE) == g.GPT2_EARG
+
+
 def test_generate_validation_without_model():
     assert g.gpt2_generate(None, FAKE, 20 * g.GPT2_CACHE_WORDS_PER_POS, [1, 2], 4, 0, FAKE, FAKE, FAKE, FAKE) == g.GPT2_EARG

@@ -115,3 +115,39 @@ def test_batched_rejections():
     assert g.gpt2_batched_cached_step(h, c, st, [0] * 65, [0] * 65, [0] * 65, ws, l) == g.GPT2_EARG
     torch.cuda.synchronize()
     assert torch.all(lb == 7.0) and torch.all(caches == 0)
+
+
+def test_prefill_hands_the_session_to_the_cached_step():
+    """gpt2_prefill over the first 64 tokens of the 128-token session, then
+    cachedStep at positions 64..127: logits against the oracle's cached session at
+    every continued position (fp32 tolerance); the handed-over cache rows against
+    the oracle's; the prefill logits against the oracle's at position 63."""
+    need_gpu()
+    m = model()
+    T, P = 128, 64
+    toks = synth.make_tokens(synth.SEED_SESSION, T)
+    ref, ref_cache = oracle_session(0, tuple(int(t) for t in toks))
+    cache = m.new_cache(T)
+    lg = torch.empty(g.GPT2_VOCAB, dtype=torch.float32, device="cuda")
+    m.prefill(toks[:P], cache, lg)
+    torch.cuda.synchronize()
+    check_logits(lg.cpu().numpy(), ref[P - 1], TOL_F32, "prefill logits")
+    got = cache.cpu().numpy()[:P * PER]
+    assert np.abs(got - ref_cache[:P * PER]).max() <= 1e-3
+    out = torch.empty((T - P, g.GPT2_VOCAB), dtype=torch.float32, device="cuda")
+    for p in range(P, T):
+        m.step(cache, p, int(toks[p]), out[p - P])
+    torch.cuda.synchronize()
+    check_logits(out.cpu().numpy(), ref[P:], TOL_F32, "steps after prefill")
+
+
+def test_prefill_validation():
+    need_gpu()
+    m = model()
+    cache = m.new_cache(8)
+    lg = torch.empty(g.GPT2_VOCAB, dtype=torch.float32, device="cuda")
+    cap = cache.numel()
+    assert g.gpt2_prefill(m.handle, [1] * 9, cache.data_ptr(), cap, m.ws.data_ptr(), lg.data_ptr()) == g.GPT2_ECACHE
+    assert g.gpt2_prefill(m.handle, [], cache.data_ptr(), cap, m.ws.data_ptr(), lg.data_ptr()) == g.GPT2_ETOKEN
+    assert g.gpt2_prefill(m.handle, [g.GPT2_VOCAB], cache.data_ptr(), cap, m.ws.data_ptr(), lg.data_ptr()) == g.GPT2_ETOKEN
+    assert g.gpt2_prefill(m.handle, [1], 0, cap, m.ws.data_ptr(), lg.data_ptr()) == g.GPT2_ECACHE
