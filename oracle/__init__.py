@@ -67,6 +67,10 @@ def lib() -> ctypes.CDLL:
         "oracle_q8_quantize_weights": (ctypes.c_int, [_dp, _f32p, _sz, _i8p, _f32p]),
         "oracle_q8_cached_step": (ctypes.c_int, [_dp, _f32p, _sz, _i8p, _f32p, _f32p, _sz,
                                                  ctypes.c_uint32, ctypes.c_int32, _f32p]),
+        "oracle_f16_weights": (ctypes.c_int, [_dp, _f32p, _sz, _f32p]),
+        "oracle_f16_cached_step": (ctypes.c_int, [_dp, _f32p, _f32p, _sz, _f32p, _sz, ctypes.c_uint32,
+                                                  ctypes.c_int32, _f32p]),
+        "oracle_round_binary16": (None, [ctypes.c_longlong, _f32p, _f32p]),
         "oracle_layernorm": (None, [ctypes.c_int, _f32p, _f32p, _f32p, _f32p]),
         "oracle_linear": (None, [ctypes.c_int, ctypes.c_int, _f32p, _f32p, ctypes.c_void_p, _f32p]),
         "oracle_gelu": (None, [ctypes.c_int, _f32p, _f32p]),
@@ -141,21 +145,49 @@ def infer(d, w: np.ndarray, toks: np.ndarray) -> Tuple[int, np.ndarray]:
     return rc, logits
 
 
-def session(d, w: np.ndarray, toks: np.ndarray, q8: Optional[Tuple[np.ndarray, np.ndarray]] = None):
-    """Run cachedStep at positions 0..len(toks)-1 from an empty cache.
+def session(d, w: np.ndarray, toks: np.ndarray, q8: Optional[Tuple[np.ndarray, np.ndarray]] = None,
+            f16: Optional[np.ndarray] = None):
+    """Run cachedStep at positions 0..len(toks)-1 from an empty cache (int8 with
+    q8 = (codes, scales), binary16 storage with f16 = f16_weights(d, w)).
     Returns (logits [T][V], cache)."""
     T = len(toks)
     per = cache_words_per_pos(d)
     cache = np.zeros(T * per, np.float32)
     out = np.zeros((T, d.vocab), np.float32)
     for p in range(T):
-        if q8 is None:
-            rc, lg = cached_step(d, w, cache, p * per, int(toks[p]), p)
-        else:
+        if q8 is not None:
             rc, lg = q8_cached_step(d, w, q8[0], q8[1], cache, p * per, int(toks[p]), p)
+        elif f16 is not None:
+            rc, lg = f16_cached_step(d, w, f16, cache, p * per, int(toks[p]), p)
+        else:
+            rc, lg = cached_step(d, w, cache, p * per, int(toks[p]), p)
         assert rc == 0, rc
         out[p] = lg
     return out, cache
+
+
+def round_binary16(x: np.ndarray) -> np.ndarray:
+    """IEEE binary16 rounding (nearest, ties to even) of float32 values, as float32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty_like(x)
+    lib().oracle_round_binary16(x.size, x, y)
+    return y
+
+
+def f16_weights(d, w: np.ndarray) -> np.ndarray:
+    """Checkpoint copy with the block matrices and the token table (as the head)
+    rounded to binary16."""
+    w16 = np.empty_like(w)
+    rc = lib().oracle_f16_weights(ctypes.byref(dims(d)), w, w.size, w16)
+    assert rc == 0, rc
+    return w16
+
+
+def f16_cached_step(d, w, w16, cache, cache_words, tok, pos) -> Tuple[int, np.ndarray]:
+    logits = np.zeros(d.vocab, np.float32)
+    rc = lib().oracle_f16_cached_step(ctypes.byref(dims(d)), w, w16, w.size, cache, cache_words,
+                                      int(tok), int(pos), logits)
+    return rc, logits
 
 
 def q8_sizes(d) -> Tuple[int, int]:

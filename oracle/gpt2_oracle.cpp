@@ -370,6 +370,28 @@ int validate_step(const OracleDims* dm, size_t w_words, size_t cache_words, uint
   return ORACLE_OK;
 }
 
+// ---- binary16 weight storage (gpt2.s page, options: -h) ----------------------
+// The page keeps the 48 block matrices and the output head as half precision and
+// everything else (embeddings, biases, LayerNorm weights, products, sums) in
+// binary32.  It names no rounding rule for the conversion; the reading taken is
+// IEEE 754's default, round to nearest with ties to even, overflow to infinity.
+// binary16 has an 11-bit significand and exponents -14..15, so a finite nonzero x
+// with floor(log2|x|) = e (at least -14) lies on the grid of spacing 2^(e-10);
+// below 2^-14 the spacing stays 2^-24 (subnormals).  x / spacing is exact (a
+// power-of-two scale), nearbyint rounds it to an integer with ties to even (the
+// default rounding mode), and the product is exact again.
+float round_binary16(float x) {
+  if (!(x == x) || std::isinf(x) || x == 0.0f) return x;
+  int e2 = 0;
+  std::frexp(x, &e2);  // |x| = m 2^e2, 0.5 <= m < 1
+  int e = e2 - 1;
+  if (e < -14) e = -14;
+  const float spacing = std::ldexp(1.0f, e - 10);
+  const float r = std::nearbyint(x / spacing) * spacing;
+  if (std::fabs(r) > 65504.0f) return std::copysign(INFINITY, x);
+  return r;
+}
+
 // Per-projection hooks so the fp32 and the int8 forward share the block recurrence
 // but not the projection arithmetic.
 struct Proj {
@@ -584,6 +606,42 @@ int oracle_q8_quantize_weights(const OracleDims* dm, const float* w, size_t w_wo
       quant_group(wte + (size_t)v * D + g * 64, 64, codes + q.code_off[4] + (size_t)v * D + g * 64,
                   scales + q.scale_off[4] + (size_t)v * (D / 64) + g);
   return ORACLE_OK;
+}
+
+// binary16 weight storage: a copy of the checkpoint whose 48 block matrices and
+// token table are rounded to binary16 (round_binary16); every other word is copied
+// unchanged.  The copy's token table is the rounded output head only: the step
+// below still takes the embedding rows from the original checkpoint.
+int oracle_f16_weights(const OracleDims* dm, const float* w, size_t w_words, float* w16) {
+  if (!dims_ok(dm)) return ORACLE_EARG;
+  const OracleDims& d = *dm;
+  if (w_words != total_words(d)) return ORACLE_EWEIGHTS;
+  std::memcpy(w16, w, w_words * sizeof(float));
+  auto round_range = [&](size_t off, size_t n) {
+    for (size_t i = 0; i < n; ++i) w16[off + i] = round_binary16(w[off + i]);
+  };
+  round_range(wte_off(d), (size_t)d.vocab * d.d_model);
+  const int wt[4] = {T_ATTN_W, T_APROJ_W, T_FC_W, T_MPROJ_W};
+  for (int l = 0; l < d.n_layer; ++l)
+    for (int m = 0; m < 4; ++m) round_range(tensor_off(d, l, wt[m]), block_tensor_words(d, wt[m]));
+  return ORACLE_OK;
+}
+
+// cachedStep with binary16 weight storage: the projections (block matrices and the
+// head) read w16 from oracle_f16_weights, widened exactly to binary32, with the same
+// binary32 arithmetic as oracle_cached_step; embeddings, LayerNorm and biases come
+// from w.
+int oracle_f16_cached_step(const OracleDims* dm, const float* w, const float* w16, size_t w_words, float* cache,
+                           size_t cache_words, uint32_t tok, int32_t pos, float* logits) {
+  const int rc = validate_step(dm, w_words, cache_words, tok, pos);
+  if (rc) return rc;
+  ProjF32 p(*dm, w16);
+  step_body(*dm, w, p, cache, tok, pos, logits);
+  return ORACLE_OK;
+}
+
+void oracle_round_binary16(long long n, const float* x, float* y) {
+  for (long long i = 0; i < n; ++i) y[i] = round_binary16(x[i]);
 }
 
 // Quantized cachedStep: projections (the four block matrices and the tied head)

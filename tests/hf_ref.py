@@ -22,23 +22,30 @@ def _quiet() -> None:
         logging.getLogger(name).setLevel(logging.ERROR)
 
 
-def build(w: np.ndarray, d: synth.Dims):
+def build(w: np.ndarray, d: synth.Dims, f16: bool = False):
+    """f16: binary16 weight storage (gpt2.s page, options, -h) -- the four block
+    matrices and an untied output head are the checkpoint's values rounded to
+    binary16 by numpy's conversion, while the embedding table keeps the binary32
+    values."""
     _quiet()
     from transformers import GPT2Config, GPT2LMHeadModel
 
     cfg = GPT2Config(n_layer=d.n_layer, n_embd=d.d_model, n_head=d.n_head, n_inner=d.d_ff,
                      vocab_size=d.vocab, n_positions=d.n_pos_rows, activation_function="gelu_new",
                      resid_pdrop=0.0, embd_pdrop=0.0, attn_pdrop=0.0, layer_norm_epsilon=1e-5,
-                     bos_token_id=0, eos_token_id=0, tie_word_embeddings=True)
+                     bos_token_id=0, eos_token_id=0, tie_word_embeddings=not f16)
     cfg._attn_implementation = "eager"
     with torch.device("meta"):
         model = GPT2LMHeadModel(cfg)
     off = synth.offsets(d)
     D, F = d.d_model, d.d_ff
 
-    def t(name, shape):
+    def t(name, shape, half=False):
         o, n = off[name]
-        return torch.from_numpy(w[o:o + n].astype(np.float64).reshape(shape))
+        v = w[o:o + n]
+        if half:
+            v = v.astype(np.float16)
+        return torch.from_numpy(v.astype(np.float64).reshape(shape))
 
     sd = {"transformer.wte.weight": t("wte", (d.vocab, D)),
           "transformer.wpe.weight": t("wpe", (d.n_pos_rows, D)),
@@ -52,13 +59,14 @@ def build(w: np.ndarray, d: synth.Dims):
                 "mlpproj_w": ("mlp.c_proj.weight", (F, D)), "mlpproj_b": ("mlp.c_proj.bias", (D,))}
     for l in range(d.n_layer):
         for ours, (theirs, shape) in hf_names.items():
-            sd[f"transformer.h.{l}.{theirs}"] = t(f"h{l}.{ours}", shape)
-    sd["lm_head.weight"] = sd["transformer.wte.weight"]
+            sd[f"transformer.h.{l}.{theirs}"] = t(f"h{l}.{ours}", shape, half=f16 and ours.endswith("_w"))
+    sd["lm_head.weight"] = t("wte", (d.vocab, D), half=True) if f16 else sd["transformer.wte.weight"]
     model = model.to_empty(device="cpu").double()
     missing, unexpected = model.load_state_dict(sd, strict=False)
     bad = [m for m in missing if not m.endswith("attn.bias") and not m.endswith("masked_bias")]
     assert not bad and not unexpected, (bad, unexpected)
-    model.tie_weights()
+    if not f16:
+        model.tie_weights()
     model.eval()
     return model
 
