@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
-"""Bench: batch-1 cachedStep tokens/s of GPT-2 124M (fp32 and int8 group-64) on one
-MI355X, as absolute numbers and as a fraction of the HBM roofline, with the CPU
-oracle timed on the host beside it.
+"""Bench: batch-1 cachedStep tokens/s of GPT-2 124M (fp32, int8 group-64 and binary16
+weight storage) on one MI355X, as absolute numbers and as a fraction of the HBM
+roofline, with the CPU oracle timed on the host beside it.
 
 A step is one cachedStep call: one token through the 12 blocks and the tied head.
 The workload is the 128-position session (uniform-random token ids, seed 101) of
@@ -29,10 +29,13 @@ FP32_MFMA_PEAK_TF = 157.3  # MI355X dense fp32 matrix
 #         485,376 B + two embedding rows 6,144 B = 494,619,648 B;
 #   int8: codes 123,532,032 B + group scales 7,720,752 B + LayerNorm/bias 485,376 B
 #         + embedding rows 6,144 B = 131,744,304 B;
+#   binary16 storage: block matrices 169,869,312 B + head 77,194,752 B + LayerNorm/bias
+#         485,376 B + embedding rows (binary32) 6,144 B = 247,555,584 B;
 #   both: key/value rows read for positions 0..p (73,728 B each, the new one
 #         included) and 201,028 B of logits written.
 F32_FIXED = 494_619_648
 Q8_FIXED = 123_532_032 + 7_720_752 + 485_376 + 6_144
+F16_FIXED = 169_869_312 + 77_194_752 + 485_376 + 6_144
 KV_PER_POS = 73_728
 LOGITS = 201_028
 PREFILL_FLOP = 21_743_271_936 + 304_349_184  # block GEMMs + causal attention at T = 128
@@ -61,8 +64,9 @@ def kernel_sources_sha256() -> str:
     return hsh.hexdigest()
 
 
-def measured_traffic():
-    """Bytes per fp32 step launch from the committed counter summary, or None."""
+def measured_traffic(key: str = "traffic_bytes_per_launch"):
+    """Bytes per step launch (fp32 kernel; key ..._f16 for the binary16-weight kernel)
+    from the committed counter summary, or None."""
     try:
         with open(TRAFFIC_SUMMARY) as f:
             text = f.read()
@@ -76,7 +80,7 @@ def measured_traffic():
     if vals.get("sources_sha256") != kernel_sources_sha256():
         return None
     try:
-        return int(vals["traffic_bytes_per_launch"])
+        return int(vals[key])
     except (KeyError, ValueError):
         return None
 
@@ -89,7 +93,7 @@ def main() -> int:
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU-oracle baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--pmc-probe", action="store_true",
-                    help="for counter runs: 128 fp32 then 128 int8 steps (positions 0..127) and one "
+                    help="for counter runs: 128 fp32, 128 int8, then 128 binary16 steps (positions 0..127) and one "
                          "device copy of 256 MiB, nothing timed or printed")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -108,7 +112,7 @@ def main() -> int:
     w = synth.make_checkpoint(0, synth.GPT2)
     toks = synth.make_tokens(synth.SEED_SESSION, 128)
     ck = torch.from_numpy(w).to(dev)
-    m = g.Model(ck, g.GPT2_PACK_F32 | g.GPT2_PACK_Q8)
+    m = g.Model(ck, g.GPT2_PACK_F32 | g.GPT2_PACK_Q8 | g.GPT2_PACK_F16)
     torch.cuda.synchronize()
     del ck
     stream = torch.cuda.current_stream()
@@ -133,12 +137,14 @@ def main() -> int:
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
-        nbytes = sum(step_bytes(F32_FIXED if fn is g.gpt2_cached_step else Q8_FIXED, i % 128) for i in range(steps))
+        fixed = {g.gpt2_cached_step: F32_FIXED, g.gpt2_q8_cached_step: Q8_FIXED, g.gpt2_f16_cached_step: F16_FIXED}[fn]
+        nbytes = sum(step_bytes(fixed, i % 128) for i in range(steps))
         return ms, nbytes
 
     if args.pmc_probe:
         run(g.gpt2_cached_step, 128)
         run(g.gpt2_q8_cached_step, 128)
+        run(g.gpt2_f16_cached_step, 128)
         src = torch.ones(PMC_COPY_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
@@ -149,10 +155,13 @@ def main() -> int:
 
     ms32, b32 = timed(g.gpt2_cached_step, args.steps, args.warmup)
     ms8, b8 = timed(g.gpt2_q8_cached_step, args.steps, args.warmup)
+    ms16, b16 = timed(g.gpt2_f16_cached_step, args.steps, args.warmup)
     tok32 = args.steps / (ms32 * 1e-3)
     tok8 = args.steps / (ms8 * 1e-3)
+    tok16 = args.steps / (ms16 * 1e-3)
     gbs32 = b32 / (ms32 * 1e-3) / 1e9
     gbs8 = b8 / (ms8 * 1e-3) / 1e9
+    gbs16 = b16 / (ms16 * 1e-3) / 1e9
 
     # greedy generation on the device: an 8-token prompt and 120 chosen tokens
     # (127 steps and 120 on-device choices per call), median of 5 calls
@@ -224,6 +233,10 @@ def main() -> int:
         "int8_g64": {"value": round(tok8, 1), "unit": "tok/s", "ms_per_step": round(ms8 / args.steps, 5),
                      "roofline": {"bound": "hbm", "achieved": round(gbs8, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": round(gbs8 / HBM_PEAK_GBS, 4)}},
+        "f16_weights": {"value": round(tok16, 1), "unit": "tok/s", "ms_per_step": round(ms16 / args.steps, 5),
+                        "roofline": {"bound": "hbm", "achieved": round(gbs16, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                     "frac": round(gbs16 / HBM_PEAK_GBS, 4),
+                                     "traffic": measured_traffic("traffic_bytes_per_launch_f16")}},
         "generate": {"value": round(120 / (gms * 1e-3), 1), "unit": "tok/s", "ms_per_call": round(gms, 3),
                      "sample": "fp32 greedy, 8-token prompt + 120 tokens chosen on the GPU (127 steps)"},
         "prefill": {"value": round(128 / (pms * 1e-3), 1), "unit": "tok/s", "ms_median": round(pms, 4),

@@ -51,8 +51,12 @@ extern "C" {
 
 enum {
   GPT2_PACK_F32 = 1, /* binary32 [out][in] matrices for the fp32 step, infer and the batched step */
-  GPT2_PACK_Q8 = 2   /* int8 group-64 codes and scales for gpt2_q8_cached_step */
+  GPT2_PACK_Q8 = 2,  /* int8 group-64 codes and scales for gpt2_q8_cached_step */
+  GPT2_PACK_F16 = 4  /* binary16 [out][in] block matrices and head for gpt2_f16_cached_step */
 };
+
+/* Stored weight format of a step (gpt2_generate's `weights`). */
+enum { GPT2_WEIGHTS_F32 = 0, GPT2_WEIGHTS_Q8 = 1, GPT2_WEIGHTS_F16 = 2 };
 
 enum {
   GPT2_OK = 0,
@@ -89,10 +93,15 @@ size_t gpt2_workspace_nbytes(void);
  *                 mlp-projection weight [3072][768], its bias.
  *  ckpt_nbytes  : must be 497,759,232 (GPT2_EWEIGHTS otherwise).
  *  packed_dev   : >= gpt2_packed_nbytes(flags) bytes; written on `stream`.
- *  flags        : GPT2_PACK_F32 and/or GPT2_PACK_Q8.  The int8 form follows the
- *                 marXiv 2609.00018 abstract: every block matrix and the tied head,
- *                 per output row and per group of 64 inputs, scale = max|w|/127,
- *                 code = clamp(round-half-even(w/scale), -127, 127).
+ *  flags        : any nonzero OR of GPT2_PACK_F32, GPT2_PACK_Q8, GPT2_PACK_F16.  The
+ *                 int8 form follows the marXiv 2609.00018 abstract: every block
+ *                 matrix and the tied head, per output row and per group of 64
+ *                 inputs, scale = max|w|/127, code = clamp(round-half-even(w/scale),
+ *                 -127, 127).  The binary16 form (gpt2.s page, options, -h) rounds
+ *                 the 48 block matrices and the head (the token table read as the
+ *                 output matrix) to IEEE binary16, nearest with ties to even,
+ *                 overflow to infinity; the embedding lookup keeps the binary32
+ *                 table, which every form holds.
  *  out          : receives a host handle that refers to packed_dev (which must
  *                 stay allocated while the handle is used).  The checkpoint is
  *                 not referenced after the enqueued packing work completes.
@@ -128,6 +137,16 @@ int gpt2_cached_step(const gpt2_model* model, float* cache_dev, size_t cache_nwo
  * Same arguments and errors as gpt2_cached_step; needs GPT2_PACK_Q8. */
 int gpt2_q8_cached_step(const gpt2_model* model, float* cache_dev, size_t cache_nwords, uint32_t token,
                         int32_t position, void* ws_dev, float* logits_dev, void* stream);
+
+/* The cached step with binary16 weight storage (gpt2.s page, options, -h): the 48
+ * block matrices and the head are read as binary16 and widened exactly to binary32;
+ * embeddings, biases, LayerNorm parameters, every product and sum, attention,
+ * GELU, residuals and the cache stay binary32.  The result equals gpt2_cached_step
+ * on a checkpoint whose block matrices and head were rounded to binary16 while the
+ * embedding rows were not, bit for bit.  Same arguments and errors as
+ * gpt2_cached_step; needs GPT2_PACK_F16. */
+int gpt2_f16_cached_step(const gpt2_model* model, float* cache_dev, size_t cache_nwords, uint32_t token,
+                         int32_t position, void* ws_dev, float* logits_dev, void* stream);
 
 /* B independent sessions (1..64) advanced by one token each.
  *  caches_dev         : session b's cache starts at caches_dev + b*cache_stride_words;
@@ -192,8 +211,9 @@ int gpt2_prefill(const gpt2_model* model, const uint32_t* tokens, int n, float* 
  * then feeds each step the first maximum of the previous step's logits, until
  * n_gen tokens are chosen: tokens_out[i] (device, uint32[n_gen]) is the choice
  * made from the logits of position n_prompt-1+i, and the last choice is not
- * stepped, so positions 0..n_prompt+n_gen-2 are computed.  q8 = 0: fp32 steps
- * (GPT2_PACK_F32); q8 = 1: int8 steps (GPT2_PACK_Q8).  cache (device) holds at
+ * stepped, so positions 0..n_prompt+n_gen-2 are computed.  weights: GPT2_WEIGHTS_F32
+ * (gpt2_cached_step, GPT2_PACK_F32), GPT2_WEIGHTS_Q8 (gpt2_q8_cached_step,
+ * GPT2_PACK_Q8) or GPT2_WEIGHTS_F16 (gpt2_f16_cached_step, GPT2_PACK_F16).  cache (device) holds at
  * least (n_prompt+n_gen-1) * 18,432 words; it starts empty (position 0) and ends
  * holding those positions' rows.  logits receives the last step's logits.
  * *status (device int32) is 0 when every step's logits were finite, else k+1 for
@@ -204,7 +224,7 @@ int gpt2_prefill(const gpt2_model* model, const uint32_t* tokens, int n, float* 
  * n_prompt+n_gen-1 > 128 or a prompt token >= 50,257; GPT2_ECACHE for a short or
  * null cache; GPT2_ENOTPACKED; GPT2_EARG otherwise. */
 int gpt2_generate(const gpt2_model* model, float* cache_dev, size_t cache_capacity_nwords, const uint32_t* prompt,
-                  int n_prompt, int n_gen, int q8, void* ws_dev, float* logits_dev, uint32_t* tokens_out_dev,
+                  int n_prompt, int n_gen, int weights, void* ws_dev, float* logits_dev, uint32_t* tokens_out_dev,
                   int32_t* status_dev, void* stream);
 
 /* Group-64 quantizer alone: n (a multiple of 64) values -> codes [n], scales [n/64]. */

@@ -28,6 +28,8 @@ GPT2_CACHE_WORDS_PER_POS = 18_432
 GPT2_MAX_BATCH = 64
 GPT2_PACK_F32 = 1
 GPT2_PACK_Q8 = 2
+GPT2_PACK_F16 = 4
+GPT2_WEIGHTS_F32, GPT2_WEIGHTS_Q8, GPT2_WEIGHTS_F16 = 0, 1, 2
 GPT2_OK, GPT2_EWEIGHTS, GPT2_ETOKEN, GPT2_EPOSITION, GPT2_ECACHE, GPT2_ENOTPACKED, GPT2_EARG, GPT2_EHIP = \
     0, -1, -2, -3, -4, -5, -6, -7
 ERROR_NAMES = {0: "GPT2_OK", -1: "GPT2_EWEIGHTS", -2: "GPT2_ETOKEN", -3: "GPT2_EPOSITION",
@@ -42,6 +44,7 @@ SIGNATURES = {
     "gpt2_release": (None, [_vp]),
     "gpt2_cached_step": (_i, [_vp, _vp, _sz, _u32, ctypes.c_int32, _vp, _vp, _vp]),
     "gpt2_q8_cached_step": (_i, [_vp, _vp, _sz, _u32, ctypes.c_int32, _vp, _vp, _vp]),
+    "gpt2_f16_cached_step": (_i, [_vp, _vp, _sz, _u32, ctypes.c_int32, _vp, _vp, _vp]),
     "gpt2_batched_cached_step": (_i, [_vp, _vp, _sz, _vp, _vp, _vp, _i, _vp, _vp, _vp]),
     "gpt2_infer": (_i, [_vp, _vp, _i, _vp, _vp, _vp]),
     "gpt2_generate": (_i, [_vp, _vp, _sz, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
@@ -122,6 +125,11 @@ def gpt2_q8_cached_step(model, cache_dev, cache_nwords, token, position, ws_dev,
                                      logits_dev, stream)
 
 
+def gpt2_f16_cached_step(model, cache_dev, cache_nwords, token, position, ws_dev, logits_dev, stream=0) -> int:
+    return lib().gpt2_f16_cached_step(model, cache_dev, cache_nwords, token & 0xFFFFFFFF, position, ws_dev,
+                                      logits_dev, stream)
+
+
 def gpt2_q8_cached_step_capture(model, cache_dev, cache_nwords, token, position, ws_dev, logits_dev,
                                 capture_dev, stream=0) -> int:
     return lib().gpt2_q8_cached_step_capture(model, cache_dev, cache_nwords, token & 0xFFFFFFFF, position,
@@ -152,11 +160,11 @@ def gpt2_prefill(model, tokens: Sequence[int], cache_dev, cache_capacity_nwords,
                               cache_capacity_nwords, ws_dev, logits_dev, stream)
 
 
-def gpt2_generate(model, cache_dev, cache_capacity_nwords, prompt: Sequence[int], n_gen, q8, ws_dev, logits_dev,
+def gpt2_generate(model, cache_dev, cache_capacity_nwords, prompt: Sequence[int], n_gen, weights, ws_dev, logits_dev,
                   tokens_out_dev, status_dev, stream=0) -> int:
     tk = _u32_array([t & 0xFFFFFFFF for t in prompt]) if len(prompt) else None
     return lib().gpt2_generate(model, cache_dev, cache_capacity_nwords, ctypes.cast(tk, _vp) if tk is not None else None,
-                               len(prompt), n_gen, q8, ws_dev, logits_dev, tokens_out_dev, status_dev, stream)
+                               len(prompt), n_gen, weights, ws_dev, logits_dev, tokens_out_dev, status_dev, stream)
 
 
 def gpt2_test_quantize(x_dev, n, codes_dev, scales_dev, stream=0) -> int:
@@ -260,8 +268,8 @@ class Model:
         shape = (positions * GPT2_CACHE_WORDS_PER_POS,) if batch == 0 else (batch, positions * GPT2_CACHE_WORDS_PER_POS)
         return torch.zeros(shape, dtype=torch.float32, device=self.packed.device)
 
-    def step(self, cache, pos: int, token: int, logits, q8: bool = False) -> None:
-        fn = gpt2_q8_cached_step if q8 else gpt2_cached_step
+    def step(self, cache, pos: int, token: int, logits, q8: bool = False, f16: bool = False) -> None:
+        fn = gpt2_q8_cached_step if q8 else gpt2_f16_cached_step if f16 else gpt2_cached_step
         rc = fn(self.handle, cache.data_ptr(), pos * GPT2_CACHE_WORDS_PER_POS, token, pos, self.ws.data_ptr(),
                 logits.data_ptr(), _stream())
         if rc:
@@ -275,10 +283,12 @@ class Model:
         if rc:
             raise Gpt2Error(rc, "gpt2_batched_cached_step")
 
-    def generate(self, cache, prompt, n_gen: int, logits, tokens_out, status, q8: bool = False) -> None:
+    def generate(self, cache, prompt, n_gen: int, logits, tokens_out, status, q8: bool = False,
+                 f16: bool = False) -> None:
         """Greedy generation on the device (gpt2_generate): cache, logits, tokens_out
         (uint32 or int32, n_gen) and status (int32, 1) are device tensors."""
-        rc = gpt2_generate(self.handle, cache.data_ptr(), cache.numel(), list(prompt), n_gen, 1 if q8 else 0,
+        weights = GPT2_WEIGHTS_Q8 if q8 else GPT2_WEIGHTS_F16 if f16 else GPT2_WEIGHTS_F32
+        rc = gpt2_generate(self.handle, cache.data_ptr(), cache.numel(), list(prompt), n_gen, weights,
                            self.ws.data_ptr(), logits.data_ptr(), tokens_out.data_ptr(), status.data_ptr(), _stream())
         if rc:
             raise Gpt2Error(rc, "gpt2_generate")

@@ -56,7 +56,7 @@ static int step_checks(const gpt2_model* m, int need_flag, const float* cache, s
 extern "C" {
 
 size_t gpt2_packed_nbytes(int flags) {
-  if (flags < 1 || flags > 3) return 0;
+  if (flags < 1 || flags > PACK_FLAGS_ALL) return 0;
   return packed_layout(flags).total;
 }
 
@@ -64,7 +64,7 @@ size_t gpt2_workspace_nbytes(void) { return ws_layout(MAX_BATCH).total; }
 
 int gpt2_pack_weights(const void* ckpt_dev, size_t ckpt_nbytes, void* packed_dev, size_t packed_nbytes,
                       int flags, void* stream, gpt2_model** out) {
-  if (!out || flags < 1 || flags > 3) return GPT2_EARG;
+  if (!out || flags < 1 || flags > PACK_FLAGS_ALL) return GPT2_EARG;
   if (!ckpt_dev || ckpt_nbytes != (size_t)ck::WORDS * 4) return GPT2_EWEIGHTS;
   if (!aligned16(ckpt_dev)) return GPT2_EARG;
   if (!packed_dev || !aligned16(packed_dev) || packed_nbytes < packed_layout(flags).total) return GPT2_EARG;
@@ -84,6 +84,7 @@ int gpt2_pack_weights(const void* ckpt_dev, size_t ckpt_nbytes, void* packed_dev
   m->w.f32 = (flags & 1) ? (const float*)(p + pl.f32) : nullptr;
   m->w.q8c = (flags & 2) ? (const int8_t*)(p + pl.q8_codes) : nullptr;
   m->w.q8s = (flags & 2) ? (const float*)(p + pl.q8_scales) : nullptr;
+  m->w.f16 = (flags & 4) ? (const uint16_t*)(p + pl.f16) : nullptr;
   *out = m;
   return GPT2_OK;
 }
@@ -93,28 +94,37 @@ void gpt2_release(gpt2_model* model) { delete model; }
 // One validated batch-1 step: the single-launch kernel, or the per-phase kernels
 // where it cannot run.  tokp: read the token from device memory instead (it must be
 // the workspace header's word HDR_WORD_NEXT_TOKEN).
-static int enqueue_step(const gpt2_model* m, bool q8, float* cache, uint32_t token, const uint32_t* tokp,
+static int enqueue_step(const gpt2_model* m, WFmt f, float* cache, uint32_t token, const uint32_t* tokp,
                         int32_t pos, void* ws, float* logits, char* capture, hipStream_t s) {
   const Work k = work_ptrs(ws, MAX_BATCH);
   bool used = false;
   if (!g_force_phase_kernels &&
-      launch_fused(q8, m->w, k, token, pos, cache, logits, capture, s, &used, tokp != nullptr) != hipSuccess)
+      launch_fused(f, m->w, k, token, pos, cache, logits, capture, s, &used, tokp != nullptr) != hipSuccess)
     return GPT2_EHIP;
   if (used) return GPT2_OK;
   Sessions ss{};
   ss.B = 1;
   ss.tok[0] = token;
   ss.pos[0] = pos;
-  const hipError_t e = q8 ? launch_step_q8(m->w, k, ss, cache, logits, capture, s, tokp)
-                          : launch_step_f32(m->w, k, ss, cache, 0, logits, s, tokp);
+  const hipError_t e = f == WF_Q8 ? launch_step_q8(m->w, k, ss, cache, logits, capture, s, tokp)
+                                  : launch_step_f32(m->w, k, ss, cache, 0, logits, s, tokp, f == WF_F16);
   return e == hipSuccess ? GPT2_OK : GPT2_EHIP;
 }
+
+static int pack_flag(WFmt f) { return f == WF_Q8 ? GPT2_PACK_Q8 : f == WF_F16 ? GPT2_PACK_F16 : GPT2_PACK_F32; }
 
 int gpt2_cached_step(const gpt2_model* m, float* cache, size_t cache_nwords, uint32_t token, int32_t pos,
                      void* ws, float* logits, void* stream) {
   const int rc = step_checks(m, GPT2_PACK_F32, cache, cache_nwords, token, pos, ws, logits);
   if (rc) return rc;
-  return enqueue_step(m, false, cache, token, nullptr, pos, ws, logits, nullptr, (hipStream_t)stream);
+  return enqueue_step(m, WF_F32, cache, token, nullptr, pos, ws, logits, nullptr, (hipStream_t)stream);
+}
+
+int gpt2_f16_cached_step(const gpt2_model* m, float* cache, size_t cache_nwords, uint32_t token, int32_t pos,
+                         void* ws, float* logits, void* stream) {
+  const int rc = step_checks(m, GPT2_PACK_F16, cache, cache_nwords, token, pos, ws, logits);
+  if (rc) return rc;
+  return enqueue_step(m, WF_F16, cache, token, nullptr, pos, ws, logits, nullptr, (hipStream_t)stream);
 }
 
 static int q8_step(const gpt2_model* m, float* cache, size_t cache_nwords, uint32_t token, int32_t pos, void* ws,
@@ -122,14 +132,15 @@ static int q8_step(const gpt2_model* m, float* cache, size_t cache_nwords, uint3
   const int rc = step_checks(m, GPT2_PACK_Q8, cache, cache_nwords, token, pos, ws, logits);
   if (rc) return rc;
   if (capture && !aligned16(capture)) return GPT2_EARG;
-  return enqueue_step(m, true, cache, token, nullptr, pos, ws, logits, (char*)capture, (hipStream_t)stream);
+  return enqueue_step(m, WF_Q8, cache, token, nullptr, pos, ws, logits, (char*)capture, (hipStream_t)stream);
 }
 
 int gpt2_generate(const gpt2_model* m, float* cache, size_t cache_capacity_nwords, const uint32_t* prompt,
-                  int n_prompt, int n_gen, int q8, void* ws, float* logits, uint32_t* tokens_out, int32_t* status,
-                  void* stream) {
-  if (!m || (q8 != 0 && q8 != 1)) return GPT2_EARG;
-  if (!(m->flags & (q8 ? GPT2_PACK_Q8 : GPT2_PACK_F32))) return GPT2_ENOTPACKED;
+                  int n_prompt, int n_gen, int weights, void* ws, float* logits, uint32_t* tokens_out,
+                  int32_t* status, void* stream) {
+  if (!m || weights < GPT2_WEIGHTS_F32 || weights > GPT2_WEIGHTS_F16) return GPT2_EARG;
+  const WFmt f = (WFmt)weights;
+  if (!(m->flags & pack_flag(f))) return GPT2_ENOTPACKED;
   if (!prompt || n_prompt < 1 || n_gen < 1 || n_prompt + n_gen - 1 > PMAX) return GPT2_ETOKEN;
   for (int t = 0; t < n_prompt; ++t)
     if (prompt[t] >= (uint32_t)V) return GPT2_ETOKEN;
@@ -142,8 +153,7 @@ int gpt2_generate(const gpt2_model* m, float* cache, size_t cache_capacity_nword
   uint32_t* next = work_ptrs(ws, MAX_BATCH).header + HDR_WORD_NEXT_TOKEN;
   for (int p = 0; p < nsteps; ++p) {
     const bool fed = p >= n_prompt;
-    const int rc = enqueue_step(m, q8 != 0, cache, fed ? 0u : prompt[p], fed ? next : nullptr, p, ws, logits,
-                                nullptr, s);
+    const int rc = enqueue_step(m, f, cache, fed ? 0u : prompt[p], fed ? next : nullptr, p, ws, logits, nullptr, s);
     if (rc) return rc;
     if (p >= n_prompt - 1 && launch_argmax(logits, next, tokens_out, status, p - (n_prompt - 1), s) != hipSuccess)
       return GPT2_EHIP;

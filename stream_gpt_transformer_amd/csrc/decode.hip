@@ -21,6 +21,7 @@ struct ProjArgs {
   size_t cache_stride;  // words
   float* logits;        // [B][V]
   char* capture;        // int8 path capture buffer or null
+  const uint32_t* tokp; // session 0's token in device memory, or null
   int layer;
 };
 
@@ -29,7 +30,8 @@ __device__ __forceinline__ T nt_load(const T* p) {
   return __builtin_nontemporal_load(p);
 }
 
-// x += wte[tok] + wpe[pos]: one block of 192 threads per session.
+// x += wte[tok] + wpe[pos]: one block of 192 threads per session (the fp32 token
+// table for every weight format).
 __global__ __launch_bounds__(192) void k_embed(const Weights w, const Sessions ss, float* x, const uint32_t* tokp) {
   const int b = blockIdx.x, t = threadIdx.x;
   const uint32_t tok = b == 0 && tokp ? min(*tokp, (uint32_t)V - 1) : ss.tok[b];
@@ -113,8 +115,9 @@ __device__ __forceinline__ float proj_dot(const f4 (&w)[NI], const f4 (&x)[NI]) 
 // fp32 projection over B sessions.  Block = 4 waves; wave w owns RPW consecutive
 // output rows, whose weights it loads once; sessions are staged BT at a time in
 // LDS as (normalised) input fragments.  Output r of session b is
-// proj_dot(W_r, x_b) + bias_r — the same value for any B, RPW or BT.
-template <int MODE, int RPW, int BT>
+// proj_dot(W_r, x_b) + bias_r — the same value for any B, RPW or BT.  H16: the
+// weights are read as binary16 and widened (exact) when loaded.
+template <int MODE, int RPW, int BT, bool H16>
 __global__ __launch_bounds__(256) void k_proj(const ProjArgs a) {
   constexpr int NI = MODE == MODE_PR ? F / 256 : D / 256;
   constexpr int K = 256 * NI;
@@ -123,13 +126,18 @@ __global__ __launch_bounds__(256) void k_proj(const ProjArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row0 = (blockIdx.x * 4 + wave) * RPW;
   const float* W = MODE == MODE_HEAD ? a.w.wte : f32_mat(a.w, a.layer, MODE);
+  const uint16_t* W16 = H16 ? f16_mat(a.w, a.layer, MODE) : nullptr;
   f4 w[RPW][NI];
 #pragma unroll
   for (int rr = 0; rr < RPW; ++rr) {
     const int r = row0 + rr;
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      w[rr][i] = r < NROWS ? nt_load((const f4*)(W + (size_t)r * K + 256 * i + 4 * lane)) : f4{0, 0, 0, 0};
+    for (int i = 0; i < NI; ++i) {
+      const size_t e = (size_t)r * K + 256 * i + 4 * lane;
+      if (r >= NROWS) w[rr][i] = f4{0, 0, 0, 0};
+      else if constexpr (H16) w[rr][i] = widen(nt_load((const h4*)(W16 + e)));
+      else w[rr][i] = nt_load((const f4*)(W + e));
+    }
   }
   float bias[RPW];
 #pragma unroll
@@ -345,29 +353,30 @@ __global__ __launch_bounds__(256) void k_special_bits(int kind, uint32_t first, 
 
 // ---- launchers ---------------------------------------------------------------
 
-template <int MODE, int RPW, int BT>
+template <int MODE, int RPW, int BT, bool H16>
 static void launch_proj(const ProjArgs& a, hipStream_t s) {
   const int rows = MODE == MODE_QKV ? D3 : MODE == MODE_FC ? F : MODE == MODE_HEAD ? V : D;
   const int nblk = (rows + 4 * RPW - 1) / (4 * RPW);
-  hipLaunchKernelGGL((k_proj<MODE, RPW, BT>), dim3(nblk), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_proj<MODE, RPW, BT, H16>), dim3(nblk), dim3(256), 0, s, a);
 }
 
-template <int RPW, int BT768, int BT3072>
+template <int RPW, int BT768, int BT3072, bool H16>
 static void launch_layers(ProjArgs& a, hipStream_t s) {
   const int B = a.ss.B;
+  hipLaunchKernelGGL(k_embed, dim3(B), dim3(192), 0, s, a.w, a.ss, a.k.x, a.tokp);
   for (int l = 0; l < L; ++l) {
     a.layer = l;
-    launch_proj<MODE_QKV, RPW, BT768>(a, s);
+    launch_proj<MODE_QKV, RPW, BT768, H16>(a, s);
     hipLaunchKernelGGL(k_attn<false>, dim3(H, B), dim3(128), 0, s, a);
-    launch_proj<MODE_O, RPW, BT768>(a, s);
-    launch_proj<MODE_FC, RPW, BT768>(a, s);
-    launch_proj<MODE_PR, RPW, BT3072>(a, s);
+    launch_proj<MODE_O, RPW, BT768, H16>(a, s);
+    launch_proj<MODE_FC, RPW, BT768, H16>(a, s);
+    launch_proj<MODE_PR, RPW, BT3072, H16>(a, s);
   }
-  launch_proj<MODE_HEAD, RPW, BT768>(a, s);
+  launch_proj<MODE_HEAD, RPW, BT768, H16>(a, s);
 }
 
 hipError_t launch_step_f32(const Weights& w, const Work& k, const Sessions& ss, float* caches,
-                           size_t cache_stride, float* logits, hipStream_t s, const uint32_t* tokp) {
+                           size_t cache_stride, float* logits, hipStream_t s, const uint32_t* tokp, bool h16) {
   ProjArgs a{};
   a.w = w;
   a.k = k;
@@ -376,11 +385,15 @@ hipError_t launch_step_f32(const Weights& w, const Work& k, const Sessions& ss, 
   a.cache_stride = cache_stride;
   a.logits = logits;
   a.capture = nullptr;
-  hipLaunchKernelGGL(k_embed, dim3(ss.B), dim3(192), 0, s, w, ss, k.x, tokp);
-  if (ss.B == 1)
-    launch_layers<2, 1, 1>(a, s);
-  else
-    launch_layers<4, 16, 4>(a, s);
+  a.tokp = tokp;
+  if (h16) {
+    if (ss.B != 1) return hipErrorInvalidValue;
+    launch_layers<2, 1, 1, true>(a, s);
+  } else if (ss.B == 1) {
+    launch_layers<2, 1, 1, false>(a, s);
+  } else {
+    launch_layers<4, 16, 4, false>(a, s);
+  }
   return hipGetLastError();
 }
 
@@ -421,7 +434,7 @@ hipError_t launch_head_f32(const Weights& w, const float* x_row, float* logits, 
   a.k.x = const_cast<float*>(x_row);
   a.ss.B = 1;
   a.logits = logits;
-  launch_proj<MODE_HEAD, 2, 1>(a, s);
+  launch_proj<MODE_HEAD, 2, 1, false>(a, s);
   return hipGetLastError();
 }
 

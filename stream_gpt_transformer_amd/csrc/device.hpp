@@ -19,6 +19,11 @@ namespace g2 {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef int i4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+
+// Four binary16 weights widened to binary32 (exact: every binary16 value is a
+// binary32 value).
+__device__ __forceinline__ f4 widen(const h4 h) { return __builtin_convertvector(h, f4); }
 
 // ---- cross-lane reductions on DPP ---------------------------------------------
 // Lane moves inside one VALU instruction (GFX9 data-parallel primitives), with no

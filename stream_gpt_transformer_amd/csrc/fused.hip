@@ -158,6 +158,8 @@ __device__ __forceinline__ uint32_t epoch_of(u64 w) { return (uint32_t)(w >> 32)
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 // Order a wave's LDS writes before its later LDS reads by other lanes.
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// vmcnt(0): every global access this wave issued, its stores included, has completed.
+__device__ __forceinline__ void wave_vmem_sync() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
 __device__ __forceinline__ uint32_t xcc_id() {
   uint32_t v;
@@ -267,23 +269,48 @@ __device__ __forceinline__ float rs_sum(const float* scratch) {
 // int8 (int4 slots): QKV rows 0..3, FC rows 4..7, MLP units 8..11; head units:
 // output-projection half dot k -> slots 2k, 2k+1 and scale sc[k]; head rows: slot s.  sc[] is the lane's weight scale
 // for its slot.
+// binary16 weights (H16, the block matrices and the head; the embedding rows stay
+// fp32): the fp32 slot numbering with four halves per slot, widened to fp32 where
+// they are used, so the values and the order of operations are those of the fp32
+// step on the same (binary16-representable) weights.
 //
 // Units a wave does not own load a valid row in their place and store to a sink
 // word, so every wave of a role issues the same memory-instruction stream and the
 // compiler's wait counts stay exact.
-template <bool Q8>
+template <bool Q8, bool H16 = false>
 struct WRegs;
 template <>
-struct WRegs<false> {
+struct WRegs<false, false> {
   f4 r[24];
   float b[8];  // bias of QKV rows 0..3, FC rows 0..3
 };
 template <>
-struct WRegs<true> {
+struct WRegs<false, true> {
+  h4 r[24];
+  float b[8];
+};
+template <>
+struct WRegs<true, false> {
   i4 c[12];
   float sc[12];
   float b[8];
 };
+// fp32 weight slot s (H16: widened)
+template <bool H16>
+__device__ __forceinline__ f4 wslot(const WRegs<false, H16>& R, int s) {
+  if constexpr (H16) return widen(R.r[s]);
+  else return R.r[s];
+}
+// dot_frag of the 768-weight row in slots s..s+2 with x
+template <bool H16>
+__device__ __forceinline__ float dot_slots(WRegs<false, H16>& R, int s, const f4 (&x)[3]) {
+  if constexpr (H16) {
+    const f4 wv[3] = {widen(R.r[s]), widen(R.r[s + 1]), widen(R.r[s + 2])};
+    return dot_frag<3>(wv, x);
+  } else {
+    return dot_frag<3>(*reinterpret_cast<f4(*)[3]>(&R.r[s]), x);
+  }
+}
 
 // QKV row n of XCD X (n < 192 per head): head hh = n/192, part (q,k,v) = n%192/64,
 // coordinate n%64.
@@ -303,10 +330,17 @@ __device__ __forceinline__ void ld_row3(f4* dst, const float* row) {
 #pragma unroll
   for (int i = 0; i < 3; ++i) dst[i] = __builtin_nontemporal_load((const f4*)(row + 256 * i + 4 * lane));
 }
+__device__ __forceinline__ void ld_row3_h(h4* dst, const uint16_t* row) {
+  const int lane = lane_id_fresh();
+#pragma unroll
+  for (int i = 0; i < 3; ++i) dst[i] = __builtin_nontemporal_load((const h4*)(row + 256 * i + 4 * lane));
+}
 
-template <bool Q8>
-__device__ __forceinline__ void load_row768(WRegs<Q8>& R, int slot, const Weights& w, int l, int m, int r) {
-  if constexpr (!Q8) {
+template <bool Q8, bool H16>
+__device__ __forceinline__ void load_row768(WRegs<Q8, H16>& R, int slot, const Weights& w, int l, int m, int r) {
+  if constexpr (H16) {
+    ld_row3_h(&R.r[3 * slot], f16_mat(w, l, m) + (size_t)r * D);
+  } else if constexpr (!Q8) {
     ld_row3(&R.r[3 * slot], f32_mat(w, l, m) + (size_t)r * D);
   } else {
     i4 t[1];
@@ -324,30 +358,51 @@ static_assert(sizeof(PrLds) >= (size_t)FT * 128, "head units stage their output-
 __device__ __forceinline__ const f4& pr_w(const PrLds& P, int wave, int k, int p) {
   return P.w[wave - 1][k][p][lane_id()];
 }
+// binary16: a unit's 12 group dots of 64 halves sit contiguously at the start of its
+// fp32 space (group dot kk at byte 128 kk), so pass p of lane (qq, j) reads the 8
+// bytes at 512 p + 8 lane.
+__device__ __forceinline__ char* pr_unit(PrLds& P, int wave, int k) { return (char*)&P.w[wave - 1][k][0][0]; }
+__device__ __forceinline__ f4 pr_w16(PrLds& P, int wave, int k, int p) {
+  return widen(*(const h4*)(pr_unit(P, wave, k) + 512 * p + 8 * lane_id()));
+}
 
 // All units of a regular compute wave for block l.
-template <bool Q8>
-__device__ __forceinline__ void load_block(WRegs<Q8>& R, PrLds& P, const Weights& w, int l, const Units& U,
+template <bool Q8, bool H16>
+__device__ __forceinline__ void load_block(WRegs<Q8, H16>& R, PrLds& P, const Weights& w, int l, const Units& U,
                                            int wave) {
   const int lane = lane_id_fresh();
 #pragma unroll
   for (int k = 0; k < UPW; ++k) {
     const int r = qkv_row(U.X, min(U.qkv(k), 192 * U.nh - 1));
-    load_row768<Q8>(R, k, w, l, M_QKV, r);
+    load_row768<Q8, H16>(R, k, w, l, M_QKV, r);
     R.b[k] = small_p(w, l, sp::B_QKV)[r];
   }
 #pragma unroll
   for (int k = 0; k < UPW; ++k) {
     const int r = GS * U.X + min(U.cw + U.cwn * k, GS - 1);
-    load_row768<Q8>(R, UPW + k, w, l, M_FC, r);
+    load_row768<Q8, H16>(R, UPW + k, w, l, M_FC, r);
     R.b[UPW + k] = small_p(w, l, sp::B_FC)[r];
   }
   // MLP projection.  fp32: row pair u (< 384) = rows 2u, 2u+1 over the XCD's slice;
   // pass p, quarter qq takes group dot kk = 4p+qq: row 2u + kk/6, slice group kk%6.
+  // binary16: the same group dots, 1536 bytes per unit: one 16-byte copy per lane for
+  // kk < 8 (8 lanes a group dot), then two 4-byte copies for kk = 8, 9 and 10, 11
+  // (32 lanes a group dot).
   // int8: unit n = 16u + lane/4 (< 6*768): output n/6, group 6X + n%6.
 #pragma unroll
   for (int k = 0; k < UPW; ++k) {
-    if constexpr (!Q8) {
+    if constexpr (H16) {
+      const int u = min(U.cw + U.cwn * k, D / 2 - 1);
+      const uint16_t* W = f16_mat(w, l, M_PR);
+      auto gd = [&](int kk) { return W + (size_t)(2 * u + kk / GPS) * F + 64 * (GPS * U.X + kk % GPS); };
+      char* dst = pr_unit(P, wave, k);
+      __builtin_amdgcn_global_load_lds((const void*)(gd(lane / 8) + 8 * (lane % 8)),
+                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        __builtin_amdgcn_global_load_lds((const void*)(gd(8 + 2 * b + lane / 32) + 2 * (lane % 32)),
+                                         (__attribute__((address_space(3))) void*)(dst + 1024 + 256 * b), 4, 0, 0);
+    } else if constexpr (!Q8) {
       const int u = min(U.cw + U.cwn * k, D / 2 - 1);
       const float* W = f32_mat(w, l, M_PR);
       const int qq = lane / 16, j = lane % 16;
@@ -372,20 +427,21 @@ __device__ __forceinline__ void load_block(WRegs<Q8>& R, PrLds& P, const Weights
 // 8k..8k+7; int8: i4 slots 2k, 2k+1 and the output's group scale sc[k].
 // Loading: for each k the 256 rows' 64 head columns are copied into LDS with
 // coalesced direct loads (rows are contiguous 256 / 64-byte segments), then each
-// thread reads its 128 / 32 contiguous bytes from there (a thread's half dot is
+// thread reads its 128 / 32 contiguous bytes (binary16: 64) from there (a thread's half dot is
 // one row segment, which a per-lane global load would fetch as scattered 16-byte
 // pieces).  Uses `stage` (>= 64 KB of LDS) as scratch; every thread must call it.
 __device__ __forceinline__ int o_half(int k) { return (int)threadIdx.x + FT * k; }
-template <bool Q8>
-__device__ __forceinline__ void load_o_head(WRegs<Q8>& R, char* stage, const Weights& w, int l, int h) {
-  constexpr int SEG = Q8 ? 32 : 128;              // bytes of one half dot
+template <bool Q8, bool H16>
+__device__ __forceinline__ void load_o_head(WRegs<Q8, H16>& R, char* stage, const Weights& w, int l, int h) {
+  constexpr int ELEM = Q8 ? 1 : H16 ? 2 : 4;      // bytes of one weight
+  constexpr int SEG = 32 * ELEM;                  // bytes of one half dot
   constexpr int CHUNK = (FT / 2) * 2 * SEG;       // 256 rows x 64 columns
   constexpr int ITERS = CHUNK / (FT * 16);
   static_assert(ITERS * FT * 16 == CHUNK, "chunk");
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int lane = lane_id_fresh();
-  const char* base = Q8 ? (const char*)q8_codes(w, l, M_O) : (const char*)f32_mat(w, l, M_O);
-  constexpr int ELEM = Q8 ? 1 : 4;
+  const char* base = Q8 ? (const char*)q8_codes(w, l, M_O)
+                    : H16 ? (const char*)f16_mat(w, l, M_O) : (const char*)f32_mat(w, l, M_O);
 #pragma unroll
   for (int k = 0; k < O_HALF_PER_THREAD; ++k) {
 #pragma unroll
@@ -398,7 +454,10 @@ __device__ __forceinline__ void load_o_head(WRegs<Q8>& R, char* stage, const Wei
     }
     __syncthreads();  // every wave's copies have landed
     const char* mine = stage + (size_t)threadIdx.x * SEG;
-    if constexpr (!Q8) {
+    if constexpr (H16) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) R.r[8 * k + j] = *(const h4*)(mine + 8 * j);
+    } else if constexpr (!Q8) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) R.r[8 * k + j] = *(const f4*)(mine + 16 * j);
     } else {
@@ -412,10 +471,12 @@ __device__ __forceinline__ void load_o_head(WRegs<Q8>& R, char* stage, const Wei
 }
 
 // Head row r (clamped to the last row) into head slot s.
-template <bool Q8>
-__device__ __forceinline__ void load_head(WRegs<Q8>& R, const Weights& w, int s, int r) {
+template <bool Q8, bool H16>
+__device__ __forceinline__ void load_head(WRegs<Q8, H16>& R, const Weights& w, int s, int r) {
   r = min(r, V - 1);
-  if constexpr (!Q8) {
+  if constexpr (H16) {
+    ld_row3_h(&R.r[3 * s], f16_mat(w, 0, M_HEAD) + (size_t)r * D);
+  } else if constexpr (!Q8) {
     ld_row3(&R.r[3 * s], w.wte + (size_t)r * D);
   } else {
     i4 t[1];
@@ -423,10 +484,10 @@ __device__ __forceinline__ void load_head(WRegs<Q8>& R, const Weights& w, int s,
     R.c[s] = t[0];
   }
 }
-template <bool Q8>
-__device__ __forceinline__ void load_head_slots(WRegs<Q8>& R, const Weights& w, int hw) {
+template <bool Q8, bool H16>
+__device__ __forceinline__ void load_head_slots(WRegs<Q8, H16>& R, const Weights& w, int hw) {
 #pragma unroll
-  for (int s = 0; s < nhs<Q8>(); ++s) load_head<Q8>(R, w, s, hw + s * HEAD_STRIDE);
+  for (int s = 0; s < nhs<Q8>(); ++s) load_head<Q8, H16>(R, w, s, hw + s * HEAD_STRIDE);
 }
 
 // int8 group accumulator of a quad: lanes 4k..4k+3 each hold 16 codes of one group.
@@ -588,8 +649,8 @@ __device__ __forceinline__ void capture_input(const FusedArgs& a, FusedSmem& S, 
 // Head rows of wave hw (rows hw + k*HEAD_STRIDE): the first NS slots were loaded
 // ahead; each slot is refilled with the row NS further on as soon as it has been
 // used.  Rows past the vocabulary compute on the last row and store to the sink.
-template <bool Q8, bool CAP>
-__device__ __forceinline__ void head_rows(const FusedArgs a, FusedSmem& S, WRegs<Q8>& R, int hw, float* sinkf) {
+template <bool Q8, bool CAP, bool H16>
+__device__ __forceinline__ void head_rows(const FusedArgs a, FusedSmem& S, WRegs<Q8, H16>& R, int hw, float* sinkf) {
   const int lane = lane_id();
   constexpr int NS = nhs<Q8>();
   f4 x[3];
@@ -605,7 +666,7 @@ __device__ __forceinline__ void head_rows(const FusedArgs a, FusedSmem& S, WRegs
     const int s = k % NS;
     float y;
     if constexpr (!Q8) {
-      y = dot_frag<3>(*reinterpret_cast<f4(*)[3]>(&R.r[3 * s]), x);
+      y = dot_slots(R, 3 * s, x);
     } else {
       int32_t* ca = CAP && r < V ? (int32_t*)(a.capture + cap_offset(0, M_HEAD) + cap_item(M_HEAD).acc) + (size_t)r * 12
                                  : nullptr;
@@ -613,7 +674,7 @@ __device__ __forceinline__ void head_rows(const FusedArgs a, FusedSmem& S, WRegs
       if (CAP && r < V && lane == 0) ((float*)(a.capture + cap_offset(0, M_HEAD) + cap_item(M_HEAD).y))[r] = y;
     }
     *(r < V ? a.logits + r : sinkf) = y;
-    if (k + NS < HEAD_MAX_ROWS) load_head<Q8>(R, a.w, s, r + NS * HEAD_STRIDE);
+    if (k + NS < HEAD_MAX_ROWS) load_head<Q8, H16>(R, a.w, s, r + NS * HEAD_STRIDE);
   }
 }
 
@@ -621,7 +682,7 @@ __device__ __forceinline__ void head_rows(const FusedArgs a, FusedSmem& S, WRegs
 // Wave 0 receives (reduce-scatters, all-gathers, the int8 LayerNorm) and holds no
 // weights; waves 1..7 compute from registers (and the fp32 MLP weights from LDS).
 // The two roles meet at the same sequence of workgroup barriers.
-template <bool Q8, bool CAP, bool TOKP>
+template <bool Q8, bool CAP, bool TOKP, bool H16>
 __device__ __forceinline__ void regular_io(const FusedArgs& a, FusedSmem& S, const Ctx& c) {
   const int lane = lane_id();
   uint32_t* hdr = a.header;
@@ -699,8 +760,9 @@ __device__ __forceinline__ void regular_io(const FusedArgs& a, FusedSmem& S, con
   if (lane == 0) stamp(a.trace, 49);
 }
 
-template <bool Q8, bool CAP>
-__device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S, const Ctx& c, WRegs<Q8>& R, int wave) {
+template <bool Q8, bool CAP, bool H16>
+__device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S, const Ctx& c, WRegs<Q8, H16>& R,
+                                                int wave) {
   const int lane = lane_id();
   const uint32_t E = c.E;
   u64* sinkw = a.sinkw + ((size_t)blockIdx.x * 8 + wave) * 16;
@@ -712,7 +774,7 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
   U.cw = (wave - 1) * (NQ - c.nh) + (c.q - c.nh);
   const int l0 = c.set;
   defer_set1(c, a.header);
-  load_block<Q8>(R, S.pr, a.w, l0, U, wave);
+  load_block<Q8, H16>(R, S.pr, a.w, l0, U, wave);
   wg_barrier();  // B0
   for (int l = l0; l < L; l += 2) {
     u64* loc = loc_of(c, l);
@@ -739,7 +801,7 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
         const int r = qkv_row(U.X, own ? n : 0);
         float y;
         if constexpr (!Q8) {
-          y = dot_frag<3>(*reinterpret_cast<f4(*)[3]>(&R.r[3 * k]), x);
+          y = dot_slots(R, 3 * k, x);
         } else {
           int32_t* ca = CAP && own ? (int32_t*)(a.capture + cap_offset(l, M_QKV) + cap_item(M_QKV).acc) + (size_t)r * 12
                                    : nullptr;
@@ -772,7 +834,7 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
         const int r = GS * U.X + (own ? n : 0);
         float y;
         if constexpr (!Q8) {
-          y = dot_frag<3>(*reinterpret_cast<f4(*)[3]>(&R.r[3 * (UPW + k)]), x);
+          y = dot_slots(R, 3 * (UPW + k), x);
         } else {
           int32_t* ca = CAP && own ? (int32_t*)(a.capture + cap_offset(l, M_FC) + cap_item(M_FC).acc) + (size_t)r * 12
                                    : nullptr;
@@ -802,7 +864,8 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
         for (int p = 0; p < 3; ++p) {
           const int kk = 4 * p + qq;
           const f4 xv = *(const f4*)(S.xg + 64 * (kk % GPS) + 4 * j);
-          qv[p] = dot_q16(pr_w(S.pr, wave, k, p), xv);
+          if constexpr (H16) qv[p] = dot_q16(pr_w16(S.pr, wave, k, p), xv);
+          else qv[p] = dot_q16(pr_w(S.pr, wave, k, p), xv);
         }
         auto val = [&](int kk) { return lane_val(qv[kk / 4], 16 * (kk % 4)); };
         float p0 = val(0), p1 = val(GPS);
@@ -831,9 +894,12 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
     }
     if (wave == 1) dstamp(a.trace, l, 63);
     if (FUSED_DELAY && l + 2 < L) wg_barrier();  // BD: the other set has its block input
-    // this block is done: the weights of the set's next block (or the first head rows)
-    if (l + 2 < L) load_block<Q8>(R, S.pr, a.w, l + 2, U, wave);
-    else load_head_slots<Q8>(R, a.w, wave * GRID + (int)blockIdx.x);
+    // this block is done: the weights of the set's next block (or the first head rows).
+    // The MLP terms have reached memory before that stream starts: stores still queued
+    // behind a wave's weight loads would hold up the other set's reduce-scatter.
+    wave_vmem_sync();
+    if (l + 2 < L) load_block<Q8, H16>(R, S.pr, a.w, l + 2, U, wave);
+    else load_head_slots<Q8, H16>(R, a.w, wave * GRID + (int)blockIdx.x);
   }
   if (c.set == 0) rs_pr_poll<Q8>(a, S, c, L - 1, wave);
   wg_barrier();  // BT
@@ -850,8 +916,9 @@ __device__ __forceinline__ void stage_kv(const FusedArgs& a, FusedSmem& S, int l
   attn_stage_rows(S.at, [&](int j) { return cl + (size_t)j * CACHE_POS; }, 0, a.pos, 0, FT);
 }
 
-template <bool Q8, bool CAP, bool TOKP>
-__device__ __forceinline__ void head_unit(const FusedArgs& a, FusedSmem& S, const Ctx& c, WRegs<Q8>& R, int wave) {
+template <bool Q8, bool CAP, bool TOKP, bool H16>
+__device__ __forceinline__ void head_unit(const FusedArgs& a, FusedSmem& S, const Ctx& c, WRegs<Q8, H16>& R,
+                                          int wave) {
   const int lane = lane_id();
   uint32_t* hdr = a.header;
   const uint32_t E = c.E;
@@ -863,7 +930,7 @@ __device__ __forceinline__ void head_unit(const FusedArgs& a, FusedSmem& S, cons
   float bo = 0.0f, bpr = 0.0f, xr = 0.0f;
   if (wave == 0) defer_set1(c, hdr);
   wg_barrier();
-  load_o_head<Q8>(R, (char*)&S.pr, a.w, l0, h);
+  load_o_head<Q8, H16>(R, (char*)&S.pr, a.w, l0, h);
   stage_kv(a, S, l0, h);
   if (wave == 0) {
     stage_vec(S.lnf[0], a.w.small + sp::LNF_G);
@@ -924,7 +991,7 @@ __device__ __forceinline__ void head_unit(const FusedArgs& a, FusedSmem& S, cons
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const f4 x = *(const f4*)(av + 4 * j);
-          const f4 wv4 = R.r[8 * k + j];
+          const f4 wv4 = wslot(R, 8 * k + j);
           float acc = 0.0f;
           acc = fmaf(wv4.x, x.x, acc);
           acc = fmaf(wv4.y, x.y, acc);
@@ -968,10 +1035,10 @@ __device__ __forceinline__ void head_unit(const FusedArgs& a, FusedSmem& S, cons
       wg_barrier();
     }
     if (ln < L) {
-      load_o_head<Q8>(R, (char*)&S.pr, a.w, ln, h);
+      load_o_head<Q8, H16>(R, (char*)&S.pr, a.w, ln, h);
       stage_kv(a, S, ln, h);
     } else {
-      load_head_slots<Q8>(R, a.w, wave * GRID + (int)blockIdx.x);
+      load_head_slots<Q8, H16>(R, a.w, wave * GRID + (int)blockIdx.x);
     }
     if (wave == 0) {
       if (ln < L) bo = small_p(a.w, ln, sp::B_O)[o];
@@ -988,7 +1055,7 @@ __device__ __forceinline__ void head_unit(const FusedArgs& a, FusedSmem& S, cons
   }
 }
 
-template <bool Q8, bool CAP, bool TOKP>
+template <bool Q8, bool CAP, bool TOKP, bool H16>
 __global__ __launch_bounds__(FT, 1) void k_fused(const FusedArgs a) {
   extern __shared__ __align__(16) char smem_raw[];
   FusedSmem& S = *(FusedSmem*)smem_raw;
@@ -1012,21 +1079,21 @@ __global__ __launch_bounds__(FT, 1) void k_fused(const FusedArgs a) {
   float* sinkf = (float*)(a.sinkw + ((size_t)blockIdx.x * 8 + wave) * 16 + 8);
   const int hw = wave * GRID + (int)blockIdx.x;  // first head row of this wave
 
-  WRegs<Q8> R;
-  if (c.head) head_unit<Q8, CAP, TOKP>(a, S, c, R, wave);
-  else if (wave == 0) regular_io<Q8, CAP, TOKP>(a, S, c);
-  else regular_compute<Q8, CAP>(a, S, c, R, wave);
+  WRegs<Q8, H16> R;
+  if (c.head) head_unit<Q8, CAP, TOKP, H16>(a, S, c, R, wave);
+  else if (wave == 0) regular_io<Q8, CAP, TOKP, H16>(a, S, c);
+  else regular_compute<Q8, CAP, H16>(a, S, c, R, wave);
 
   // ---- the tied head: every wave takes its head rows (the first ones are in its
   // registers already, except on wave 0 of a regular unit)
-  if (!c.head && wave == 0) load_head_slots<Q8>(R, a.w, hw);
+  if (!c.head && wave == 0) load_head_slots<Q8, H16>(R, a.w, hw);
   wg_barrier();  // x12 is in LDS
   if constexpr (Q8) {
     layernorm_seq_wg<2>(S.xs, S.lnf[0], S.lnf[1], S.xn, S.lntmp, seq_tab(S), S.xc, S.xsc);
     wg_barrier();
     if (CAP && blockIdx.x == 0 && wave == 0) capture_input(a, S, 0, M_HEAD, S.xn, 0, D, lane, 64);
   }
-  head_rows<Q8, CAP>(a, S, R, hw, sinkf);
+  head_rows<Q8, CAP, H16>(a, S, R, hw, sinkf);
   if (lane == 0 && wave == 1) stamp(a.trace, 50);
 
   // Epilogue: the last workgroup to finish checks the placement (XCD(b) - b one
@@ -1069,11 +1136,11 @@ __global__ __launch_bounds__(FT, 1) void k_fused(const FusedArgs a) {
 struct FusedConfig {
   int ok;  // 1 usable, 0 not yet probed, -1 unusable (fall back to per-phase kernels)
 };
-static FusedConfig g_cfg[5][64];
+static FusedConfig g_cfg[7][64];
 uint64_t* g_fused_trace = nullptr;  // timeline test hook
 int g_fused_plain_launch = 1;       // 1: ordinary launch (default), 0: cooperative launch
 
-template <bool Q8, bool CAP, bool TOKP>
+template <bool Q8, bool CAP, bool TOKP, bool H16>
 static hipError_t fused_config(FusedConfig& c) {
   if (c.ok) return hipSuccess;
   int dev = 0, cus = 0;
@@ -1081,25 +1148,25 @@ static hipError_t fused_config(FusedConfig& c) {
   if ((e = hipGetDevice(&dev))) return e;
   if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev))) return e;
   const size_t lds = sizeof(FusedSmem);
-  if ((e = hipFuncSetAttribute((const void*)k_fused<Q8, CAP, TOKP>, hipFuncAttributeMaxDynamicSharedMemorySize,
+  if ((e = hipFuncSetAttribute((const void*)k_fused<Q8, CAP, TOKP, H16>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)lds)))
     return e;
   int per_cu = 0;
-  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_fused<Q8, CAP, TOKP>, FT, lds))) return e;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_fused<Q8, CAP, TOKP, H16>, FT, lds))) return e;
   // One workgroup per compute unit, 32 per XCD: the grid is the whole chip.
   c.ok = (cus == GRID && per_cu >= 1) ? 1 : -1;
   return hipSuccess;
 }
 
-template <bool Q8, bool CAP, bool TOKP>
+template <bool Q8, bool CAP, bool TOKP, bool H16>
 static hipError_t launch_fused_t(const Weights& w, const Work& k, uint32_t token, int32_t pos, float* cache,
                                  float* logits, char* capture, hipStream_t s, bool* used) {
   *used = false;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e) return e;
-  FusedConfig& c = g_cfg[TOKP ? (Q8 ? 4 : 3) : Q8 ? (CAP ? 2 : 1) : 0][dev & 63];
-  if ((e = fused_config<Q8, CAP, TOKP>(c))) return e;
+  FusedConfig& c = g_cfg[H16 ? (TOKP ? 6 : 5) : TOKP ? (Q8 ? 4 : 3) : Q8 ? (CAP ? 2 : 1) : 0][dev & 63];
+  if ((e = fused_config<Q8, CAP, TOKP, H16>(c))) return e;
   if (c.ok != 1) return hipSuccess;
   FusedArgs a{};
   a.w = w;
@@ -1114,24 +1181,27 @@ static hipError_t launch_fused_t(const Weights& w, const Work& k, uint32_t token
   a.pos = pos;
   void* args[] = {&a};
   if (g_fused_plain_launch)
-    e = hipLaunchKernel((const void*)k_fused<Q8, CAP, TOKP>, dim3(GRID), dim3(FT), args, sizeof(FusedSmem), s);
+    e = hipLaunchKernel((const void*)k_fused<Q8, CAP, TOKP, H16>, dim3(GRID), dim3(FT), args, sizeof(FusedSmem), s);
   else
-    e = hipLaunchCooperativeKernel((const void*)k_fused<Q8, CAP, TOKP>, dim3(GRID), dim3(FT), args, sizeof(FusedSmem),
-                                   s);
+    e = hipLaunchCooperativeKernel((const void*)k_fused<Q8, CAP, TOKP, H16>, dim3(GRID), dim3(FT), args,
+                                   sizeof(FusedSmem), s);
   if (e == hipSuccess) *used = true;
   return e;
 }
 
-hipError_t launch_fused(bool q8, const Weights& w, const Work& k, uint32_t token, int32_t pos, float* cache,
+hipError_t launch_fused(WFmt f, const Weights& w, const Work& k, uint32_t token, int32_t pos, float* cache,
                         float* logits, char* capture, hipStream_t s, bool* used, bool device_token) {
-  if (device_token) {
-    if (capture) return hipErrorInvalidValue;
-    return q8 ? launch_fused_t<true, false, true>(w, k, token, pos, cache, logits, nullptr, s, used)
-              : launch_fused_t<false, false, true>(w, k, token, pos, cache, logits, nullptr, s, used);
-  }
-  if (!q8) return launch_fused_t<false, false, false>(w, k, token, pos, cache, logits, nullptr, s, used);
-  if (capture) return launch_fused_t<true, true, false>(w, k, token, pos, cache, logits, capture, s, used);
-  return launch_fused_t<true, false, false>(w, k, token, pos, cache, logits, nullptr, s, used);
+  if (capture && (f != WF_Q8 || device_token)) return hipErrorInvalidValue;
+  if (f == WF_F16)
+    return device_token ? launch_fused_t<false, false, true, true>(w, k, token, pos, cache, logits, nullptr, s, used)
+                        : launch_fused_t<false, false, false, true>(w, k, token, pos, cache, logits, nullptr, s, used);
+  const bool q8 = f == WF_Q8;
+  if (device_token)
+    return q8 ? launch_fused_t<true, false, true, false>(w, k, token, pos, cache, logits, nullptr, s, used)
+              : launch_fused_t<false, false, true, false>(w, k, token, pos, cache, logits, nullptr, s, used);
+  if (!q8) return launch_fused_t<false, false, false, false>(w, k, token, pos, cache, logits, nullptr, s, used);
+  if (capture) return launch_fused_t<true, true, false, false>(w, k, token, pos, cache, logits, capture, s, used);
+  return launch_fused_t<true, false, false, false>(w, k, token, pos, cache, logits, nullptr, s, used);
 }
 
 }  // namespace g2

@@ -16,6 +16,7 @@ struct Weights {
   const float* f32;    // per-layer [out][in] fp32 matrices, or null
   const int8_t* q8c;   // per-layer [out][in] int8 codes, then the head [V][D], or null
   const float* q8s;    // per-layer [out][in/64] scales, then the head [V][D/64], or null
+  const uint16_t* f16; // per-layer [out][in] binary16 matrices, then the token table [V][D], or null
 };
 
 __host__ __device__ inline const float* f32_mat(const Weights& w, int layer, int m) {
@@ -26,6 +27,9 @@ __host__ __device__ inline const int8_t* q8_codes(const Weights& w, int layer, i
 }
 __host__ __device__ inline const float* q8_scales(const Weights& w, int layer, int m) {
   return m == M_HEAD ? w.q8s + (size_t)L * LAYER_SCALES : w.q8s + (size_t)layer * LAYER_SCALES + mat_scale_off(m);
+}
+__host__ __device__ inline const uint16_t* f16_mat(const Weights& w, int layer, int m) {
+  return m == M_HEAD ? w.f16 + (size_t)L * LAYER_ELEMS : w.f16 + (size_t)layer * LAYER_ELEMS + mat_elem_off(m);
 }
 __host__ __device__ inline const float* small_p(const Weights& w, int layer, int off) {
   return w.small + (size_t)layer * sp::PER_LAYER + off;
@@ -56,10 +60,14 @@ hipError_t launch_pack(const float* ckpt, char* packed, int flags, hipStream_t s
 // (written by k_argmax, read by the step's embedding).
 constexpr int HDR_WORD_NEXT_TOKEN = 3;
 
+// Stored weight format of a step: fp32, int8 group-64, or binary16 (computed in fp32).
+enum WFmt { WF_F32 = 0, WF_Q8 = 1, WF_F16 = 2 };
+
 // tokp: when given, session 0's token is read from device memory at run time
-// instead of ss.tok[0] / token.
+// instead of ss.tok[0] / token.  h16: the binary16 weights (batch 1 only).
 hipError_t launch_step_f32(const Weights& w, const Work& k, const Sessions& ss, float* caches,
-                           size_t cache_stride, float* logits, hipStream_t s, const uint32_t* tokp = nullptr);
+                           size_t cache_stride, float* logits, hipStream_t s, const uint32_t* tokp = nullptr,
+                           bool h16 = false);
 hipError_t launch_step_q8(const Weights& w, const Work& k, const Sessions& ss, float* cache,
                           float* logits, char* capture, hipStream_t s, const uint32_t* tokp = nullptr);
 hipError_t launch_argmax(const float* logits, uint32_t* next, uint32_t* tokens_out, int32_t* status, int step,
@@ -70,7 +78,7 @@ hipError_t launch_infer(const Weights& w, const Work& k, const uint32_t* toks, i
                         hipStream_t s, float* cache = nullptr);
 // device_token: a generation step, whose token is the workspace header's word
 // HDR_WORD_NEXT_TOKEN (a separate kernel instantiation; capture must be null).
-hipError_t launch_fused(bool q8, const Weights& w, const Work& k, uint32_t token, int32_t pos, float* cache,
+hipError_t launch_fused(WFmt f, const Weights& w, const Work& k, uint32_t token, int32_t pos, float* cache,
                         float* logits, char* capture, hipStream_t s, bool* used, bool device_token = false);
 extern bool g_force_phase_kernels;
 extern uint64_t* g_fused_trace;

@@ -69,22 +69,25 @@ constexpr int LNF_G = L * PER_LAYER, LNF_B = LNF_G + D, TOTAL = LNF_B + D;
 constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct PackedLayout {
-  size_t wte, wpe, small, f32, q8_codes, q8_scales, total;
+  size_t wte, wpe, small, f32, q8_codes, q8_scales, f16, total;
 };
 
-// flags: bit 0 = fp32 matrices, bit 1 = int8 group-64 matrices.
+// flags: bit 0 = fp32 matrices, bit 1 = int8 group-64 matrices, bit 2 = binary16
+// matrices and token-embedding table.
+constexpr int PACK_FLAGS_ALL = 7;
 inline PackedLayout packed_layout(int flags) {
   PackedLayout p{};
   size_t off = 0;
   p.wte = off; off = align256(off + (size_t)V * D * 4);
   p.wpe = off; off = align256(off + (size_t)PMAX * D * 4);
   p.small = off; off = align256(off + (size_t)sp::TOTAL * 4);
-  p.f32 = p.q8_codes = p.q8_scales = 0;
+  p.f32 = p.q8_codes = p.q8_scales = p.f16 = 0;
   if (flags & 1) { p.f32 = off; off = align256(off + (size_t)L * LAYER_ELEMS * 4); }
   if (flags & 2) {
     p.q8_codes = off; off = align256(off + (size_t)L * LAYER_ELEMS + (size_t)V * D);
     p.q8_scales = off; off = align256(off + ((size_t)L * LAYER_SCALES + (size_t)V * (D / 64)) * 4);
   }
+  if (flags & 4) { p.f16 = off; off = align256(off + ((size_t)L * LAYER_ELEMS + (size_t)V * D) * 2); }
   p.total = off;
   return p;
 }

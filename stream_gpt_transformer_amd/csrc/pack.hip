@@ -1,8 +1,12 @@
 // One-time packing of the checkpoint into the device layout (gpt2.s page, weight
 // tiling paragraph: the program re-lays the [input][output] block matrices once at
 // startup so the matrix kernel streams them in order; here the re-layout is to
-// [output][input] rows for wavefront-wide coalesced row reads), and int8 group-64
-// quantization of the projection weights (marXiv 2609.00018 abstract).
+// [output][input] rows for wavefront-wide coalesced row reads), int8 group-64
+// quantization of the projection weights (marXiv 2609.00018 abstract), and the
+// binary16 storage form (gpt2.s page, options: weights kept as half precision and
+// widened to binary32 for the arithmetic).
+#include <hip/hip_fp16.h>
+
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -22,6 +26,28 @@ __global__ __launch_bounds__(256) void k_transpose(const float* __restrict__ src
     const int nn = i >> 6, kk = i & 63;
     dst[(size_t)(n0 + nn) * K + k0 + kk] = tile[kk][nn];
   }
+}
+
+// binary16 dst[N][K] of src[K][N] (round to nearest even, overflow to infinity).
+__global__ __launch_bounds__(256) void k_transpose_f16(const float* __restrict__ src, uint16_t* __restrict__ dst,
+                                                       int K, int N) {
+  __shared__ float tile[64][65];
+  const int n0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int kk = i >> 6, nn = i & 63;
+    tile[kk][nn] = src[(size_t)(k0 + kk) * N + n0 + nn];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int nn = i >> 6, kk = i & 63;
+    dst[(size_t)(n0 + nn) * K + k0 + kk] = __half_as_ushort(__float2half_rn(tile[kk][nn]));
+  }
+}
+
+// binary16 copy of n values (the token table).
+__global__ __launch_bounds__(256) void k_to_f16(const float* __restrict__ src, uint16_t* __restrict__ dst, size_t n) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dst[i] = __half_as_ushort(__float2half_rn(src[i]));
 }
 
 // int8 codes [N][K] and scales [N][K/64] of a checkpoint matrix src[K][N]: group g of
@@ -93,12 +119,21 @@ hipError_t launch_pack(const float* ck_, char* packed, int flags, hipStream_t s)
         float* dst = (float*)(packed + pl.f32) + (size_t)l * LAYER_ELEMS + mat_elem_off(m);
         hipLaunchKernelGGL(k_transpose, dim3(N / 64, K / 64), dim3(256), 0, s, src, dst, K, N);
       }
+      if (flags & 4) {
+        uint16_t* dst = (uint16_t*)(packed + pl.f16) + (size_t)l * LAYER_ELEMS + mat_elem_off(m);
+        hipLaunchKernelGGL(k_transpose_f16, dim3(N / 64, K / 64), dim3(256), 0, s, src, dst, K, N);
+      }
       if (flags & 2) {
         int8_t* codes = (int8_t*)(packed + pl.q8_codes) + (size_t)l * LAYER_ELEMS + mat_elem_off(m);
         float* scales = (float*)(packed + pl.q8_scales) + (size_t)l * LAYER_SCALES + mat_scale_off(m);
         hipLaunchKernelGGL(k_quant_in_out, dim3(N / 64, K / 64), dim3(256), 0, s, src, codes, scales, K, N);
       }
     }
+  }
+  if (flags & 4) {
+    const size_t n = (size_t)V * D;
+    hipLaunchKernelGGL(k_to_f16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ck_ + ck::WTE,
+                       (uint16_t*)(packed + pl.f16) + (size_t)L * LAYER_ELEMS, n);
   }
   if (flags & 2) {
     int8_t* codes = (int8_t*)(packed + pl.q8_codes) + (size_t)L * LAYER_ELEMS;

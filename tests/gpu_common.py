@@ -54,13 +54,21 @@ def oracle_session(seed: int, toks_key: tuple, q8: bool = False, robust: bool = 
     return oracle.session(D, checkpoint(seed, robust), toks, q8=oracle_q8(seed, robust) if q8 else None)
 
 
-def gpu_session(m: g.Model, toks, q8: bool = False):
+@functools.lru_cache(maxsize=None)
+def oracle_session_f16(seed: int, toks_key: tuple, robust: bool = False):
+    toks = np.array(toks_key, dtype=np.uint32)
+    oracle.set_threads(16)
+    w = checkpoint(seed, robust)
+    return oracle.session(D, w, toks, f16=oracle.f16_weights(D, w))
+
+
+def gpu_session(m: g.Model, toks, q8: bool = False, f16: bool = False):
     """cachedStep at positions 0..T-1 from an empty cache; returns (logits [T][V], cache)."""
     T = len(toks)
     cache = m.new_cache(T)
     out = torch.empty((T, g.GPT2_VOCAB), dtype=torch.float32, device="cuda")
     for p in range(T):
-        m.step(cache, p, int(toks[p]), out[p], q8=q8)
+        m.step(cache, p, int(toks[p]), out[p], q8=q8, f16=f16)
     torch.cuda.synchronize()
     assert m.status() == 0, f"workspace error {m.status()}"
     return out.cpu().numpy(), cache.cpu().numpy()

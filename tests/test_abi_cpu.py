@@ -35,8 +35,13 @@ def test_every_declared_symbol_is_exported_and_bound():
 
 
 def test_sizes():
-    assert g.gpt2_packed_nbytes(0) == 0 and g.gpt2_packed_nbytes(4) == 0
+    assert g.gpt2_packed_nbytes(0) == 0 and g.gpt2_packed_nbytes(8) == 0
     f32 = g.gpt2_packed_nbytes(g.GPT2_PACK_F32)
+    f16 = g.gpt2_packed_nbytes(g.GPT2_PACK_F16)
+    # binary16: the block matrices and the token table at two bytes each (besides the
+    # fp32 token table and position rows every form keeps)
+    assert 0 <= f16 - (f32 - 12 * 7_077_888 * 4) - (12 * 7_077_888 + 50257 * 768) * 2 < 4096
+    assert g.gpt2_packed_nbytes(7) > g.gpt2_packed_nbytes(3)
     q8 = g.gpt2_packed_nbytes(g.GPT2_PACK_Q8)
     both = g.gpt2_packed_nbytes(3)
     # fp32 [out][in] block matrices: 12 x 7,077,888 words; int8: the same count of bytes

@@ -129,9 +129,9 @@ def test_generate_validation():
     out = torch.empty(64, dtype=torch.int32, device="cuda")
     st = torch.empty(1, dtype=torch.int32, device="cuda")
 
-    def call(prompt=(1, 2, 3), n_gen=4, q8=0, cap_words=cap, cache_p=None, out_p=None):
+    def call(prompt=(1, 2, 3), n_gen=4, weights=0, cap_words=cap, cache_p=None, out_p=None):
         return g.gpt2_generate(m.handle, cache.data_ptr() if cache_p is None else cache_p, cap_words, list(prompt),
-                               n_gen, q8, m.ws.data_ptr(), lg.data_ptr(),
+                               n_gen, weights, m.ws.data_ptr(), lg.data_ptr(),
                                out.data_ptr() if out_p is None else out_p, st.data_ptr())
 
     assert call(prompt=()) == g.GPT2_ETOKEN
@@ -141,7 +141,9 @@ def test_generate_validation():
     assert call(cap_words=5 * PER) == g.GPT2_ECACHE                 # needs 6 positions
     assert call(cache_p=0) == g.GPT2_ECACHE
     assert call(out_p=0) == g.GPT2_EARG
-    assert call(q8=2) == g.GPT2_EARG
+    assert call(weights=3) == g.GPT2_EARG
+    assert call(weights=-1) == g.GPT2_EARG
+    assert call(weights=g.GPT2_WEIGHTS_F16) == g.GPT2_ENOTPACKED     # packed fp32 + int8 only
     torch.cuda.synchronize()
     mf = model(flags=g.GPT2_PACK_F32)
     assert g.gpt2_generate(mf.handle, cache.data_ptr(), cap, [1], 2, 1, mf.ws.data_ptr(), lg.data_ptr(),
