@@ -71,6 +71,13 @@ def lib() -> ctypes.CDLL:
         "oracle_f16_cached_step": (ctypes.c_int, [_dp, _f32p, _f32p, _sz, _f32p, _sz, ctypes.c_uint32,
                                                   ctypes.c_int32, _f32p]),
         "oracle_round_binary16": (None, [ctypes.c_longlong, _f32p, _f32p]),
+        "oracle_qv_sizes": (ctypes.c_int, [_dp, ctypes.c_int, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
+        "oracle_qv_quantize_weights": (ctypes.c_int, [_dp, _f32p, _sz, ctypes.c_int, _i8p, _f32p]),
+        "oracle_qv_cached_step": (ctypes.c_int, [_dp, _f32p, _sz, ctypes.c_int, ctypes.c_int, _i8p, _f32p,
+                                                 _f32p, _sz, ctypes.c_uint32, ctypes.c_int32, _f32p]),
+        "oracle_qv_linear": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _f32p, ctypes.c_int, _i8p, _f32p,
+                                            ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, _f32p]),
         "oracle_layernorm": (None, [ctypes.c_int, _f32p, _f32p, _f32p, _f32p]),
         "oracle_linear": (None, [ctypes.c_int, ctypes.c_int, _f32p, _f32p, ctypes.c_void_p, _f32p]),
         "oracle_gelu": (None, [ctypes.c_int, _f32p, _f32p]),
@@ -188,6 +195,65 @@ def f16_cached_step(d, w, w16, cache, cache_words, tok, pos) -> Tuple[int, np.nd
     rc = lib().oracle_f16_cached_step(ctypes.byref(dims(d)), w, w16, w.size, cache, cache_words,
                                       int(tok), int(pos), logits)
     return rc, logits
+
+
+# ---- quantizer granularity variants: weight groups gw, input groups gx (0 = whole row)
+
+def qv_sizes(d, gw: int) -> Tuple[int, int]:
+    c, s = _sz(), _sz()
+    rc = lib().oracle_qv_sizes(ctypes.byref(dims(d)), gw, ctypes.byref(c), ctypes.byref(s))
+    assert rc == 0, rc
+    return int(c.value), int(s.value)
+
+
+def qv_quantize_weights(d, w: np.ndarray, gw: int) -> Tuple[np.ndarray, np.ndarray]:
+    nc, ns = qv_sizes(d, gw)
+    codes = np.zeros(nc, np.int8)
+    scales = np.zeros(ns, np.float32)
+    rc = lib().oracle_qv_quantize_weights(ctypes.byref(dims(d)), w, w.size, gw, codes, scales)
+    assert rc == 0, rc
+    return codes, scales
+
+
+def qv_cached_step(d, w, gw, gx, codes, scales, cache, cache_words, tok, pos) -> Tuple[int, np.ndarray]:
+    logits = np.zeros(d.vocab, np.float32)
+    rc = lib().oracle_qv_cached_step(ctypes.byref(dims(d)), w, w.size, gw, gx, codes, scales, cache,
+                                     cache_words, int(tok), int(pos), logits)
+    return rc, logits
+
+
+def qv_session(d, w, toks, gw: int, gx: int, q=None):
+    """Variant cachedStep at positions 0..T-1 from an empty cache; q = qv_quantize_weights(d, w, gw)."""
+    codes, scales = q if q is not None else qv_quantize_weights(d, w, gw)
+    T = len(toks)
+    per = cache_words_per_pos(d)
+    cache = np.zeros(T * per, np.float32)
+    out = np.zeros((T, d.vocab), np.float32)
+    for p in range(T):
+        rc, out[p] = qv_cached_step(d, w, gw, gx, codes, scales, cache, p * per, int(toks[p]), p)
+        assert rc == 0, rc
+    return out, cache
+
+
+def qv_linear(x, gx: int, wc, ws, gw: int, b=None):
+    """Returns (codes, input scales, accumulators [N][K/gcd], y) of one variant projection."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    wc = np.ascontiguousarray(wc, dtype=np.int8)
+    ws = np.ascontiguousarray(ws, dtype=np.float32)
+    N, K = wc.shape
+    GX = K if gx == 0 else gx
+    GW = K if gw == 0 else gw
+    import math
+    GM = math.gcd(GX, GW)
+    xc = np.zeros(K, np.int8)
+    xs = np.zeros(K // GX, np.float32)
+    acc = np.zeros((N, K // GM), np.int32)
+    y = np.zeros(N, np.float32)
+    bb = None if b is None else np.ascontiguousarray(b, dtype=np.float32)
+    rc = lib().oracle_qv_linear(K, N, x, gx, wc, ws, gw, None if bb is None else bb.ctypes.data,
+                                xc.ctypes.data, xs.ctypes.data, acc.ctypes.data, y)
+    assert rc == 0, rc
+    return xc, xs, acc, y
 
 
 def q8_sizes(d) -> Tuple[int, int]:

@@ -359,6 +359,66 @@ void quant_matrix_in_out(int K, int N, const float* W, int8_t* codes, float* sca
   }
 }
 
+// ---- quantizer granularity variants (marXiv 2609.00018 abstract) ------------
+// The abstract's first design used one scale per activation row, its deployed one
+// a scale per 64 consecutive coordinates, and its 74.3 % storage figure matches
+// one weight scale per output row.  Generalised here: a weight scale per group of
+// gw consecutive inputs of an output row and an input scale per group of gx
+// consecutive coordinates, each group size a multiple of 64 dividing the row
+// length K, or 0 for the whole row.  Scale choice, rounding and saturation are
+// quant_group's.  The integer sums run over the groups on which both scales are
+// constant (gcd(gx, gw) consecutive coordinates, since both partitions start at
+// 0), and the rescale keeps the fixed order: y = 0; y = y + ((float)acc_h * sw) *
+// sx for those groups h ascending; y = y + b.
+int group_len(int g, int K) { return g == 0 ? K : g; }
+bool group_ok(int g, int K) { return g == 0 || (g > 0 && g % 64 == 0 && K % g == 0); }
+int gcd_int(int a, int b) { return b == 0 ? a : gcd_int(b, a % b); }
+
+void qv_quantize_input(int K, const float* x, int gx, int8_t* xc, float* xs) {
+  const int G = group_len(gx, K);
+  for (int g = 0; g < K / G; ++g) quant_group(x + g * G, G, xc + g * G, &xs[g]);
+}
+
+// Row j: K codes wc[j][*] and K/gw scales ws[j][*]; the input: codes xc, K/gx scales xs.
+void qv_linear_codes(int K, int N, const int8_t* xc, const float* xs, int gx, const int8_t* wc,
+                     const float* ws, int gw, const float* b, int32_t* acc_out, float* y) {
+  const int GX = group_len(gx, K), GW = group_len(gw, K), GM = gcd_int(GX, GW);
+  const int NW = K / GW, NH = K / GM;
+#pragma omp parallel for schedule(static)
+  for (int j = 0; j < N; ++j) {
+    const int8_t* row = wc + (size_t)j * K;
+    float yj = 0.0f;
+    for (int h = 0; h < NH; ++h) {
+      int32_t acc = 0;
+      for (int i = h * GM; i < (h + 1) * GM; ++i) acc += (int32_t)row[i] * (int32_t)xc[i];
+      if (acc_out) acc_out[(size_t)j * NH + h] = acc;
+      yj = yj + ((float)acc * ws[(size_t)j * NW + h * GM / GW]) * xs[h * GM / GX];
+    }
+    y[j] = b ? yj + b[j] : yj;
+  }
+}
+
+// Oracle-side store of a variant: the Q8Layout order with K/gw scales per row.
+Q8Layout qv_layout(const OracleDims& d, int gw) {
+  Q8Layout q{};
+  const size_t D = d.d_model, F = d.d_ff;
+  const size_t rows[4] = {3 * D, D, F, D}, cols[4] = {D, D, D, F};
+  size_t c = 0, s = 0;
+  for (int m = 0; m < 4; ++m) {
+    q.code_off[m] = c;
+    q.scale_off[m] = s;
+    c += rows[m] * cols[m];
+    s += rows[m] * (cols[m] / group_len(gw, (int)cols[m]));
+  }
+  q.layer_codes = c;
+  q.layer_scales = s;
+  q.code_off[4] = c * d.n_layer;
+  q.scale_off[4] = s * d.n_layer;
+  q.n_codes = q.code_off[4] + (size_t)d.vocab * D;
+  q.n_scales = q.scale_off[4] + (size_t)d.vocab * (D / group_len(gw, (int)D));
+  return q;
+}
+
 int validate_step(const OracleDims* dm, size_t w_words, size_t cache_words, uint32_t tok,
                   int32_t pos) {
   if (!dims_ok(dm)) return ORACLE_EARG;
@@ -432,6 +492,29 @@ struct ProjQ8 : Proj {
     const size_t sb = m == 4 ? q.scale_off[4] : l * q.layer_scales + q.scale_off[m];
     const float* b = m == 4 ? nullptr : w + tensor_off(d, l, bt[m]);
     q8_linear(K[m], N[m], x, codes + cb, scales + sb, b, y);
+  }
+};
+
+struct ProjQv : Proj {
+  const OracleDims& d;
+  const float* w;
+  const int8_t* codes;
+  const float* scales;
+  int gw, gx;
+  Q8Layout q;
+  ProjQv(const OracleDims& d_, const float* w_, const int8_t* c_, const float* s_, int gw_, int gx_)
+      : d(d_), w(w_), codes(c_), scales(s_), gw(gw_), gx(gx_), q(qv_layout(d_, gw_)) {}
+  void run(int l, int m, const float* x, float* y) const override {
+    const int D = d.d_model, F = d.d_ff;
+    const int K[5] = {D, D, D, F, D}, N[5] = {3 * D, D, F, D, d.vocab};
+    const int bt[4] = {T_ATTN_B, T_APROJ_B, T_FC_B, T_MPROJ_B};
+    const size_t cb = m == 4 ? q.code_off[4] : l * q.layer_codes + q.code_off[m];
+    const size_t sb = m == 4 ? q.scale_off[4] : l * q.layer_scales + q.scale_off[m];
+    const float* b = m == 4 ? nullptr : w + tensor_off(d, l, bt[m]);
+    std::vector<int8_t> xc(K[m]);
+    std::vector<float> xs(K[m] / group_len(gx, K[m]));
+    qv_quantize_input(K[m], x, gx, xc.data(), xs.data());
+    qv_linear_codes(K[m], N[m], xc.data(), xs.data(), gx, codes + cb, scales + sb, gw, b, nullptr, y);
   }
 };
 
@@ -655,6 +738,75 @@ int oracle_q8_cached_step(const OracleDims* dm, const float* w, size_t w_words,
   if (rc) return rc;
   ProjQ8 p(*dm, w, codes, scales);
   step_body(*dm, w, p, cache, tok, pos, logits);
+  return ORACLE_OK;
+}
+
+// Quantizer granularity variants (see qv_linear_codes).  Group sizes must be 0
+// or multiples of 64 dividing both d_model and d_ff.
+static bool qv_groups_ok(const OracleDims& d, int g) { return group_ok(g, d.d_model) && group_ok(g, d.d_ff); }
+
+int oracle_qv_sizes(const OracleDims* d, int gw, size_t* n_codes, size_t* n_scales) {
+  if (!dims_ok(d) || !qv_groups_ok(*d, gw)) return ORACLE_EARG;
+  const Q8Layout q = qv_layout(*d, gw);
+  *n_codes = q.n_codes;
+  *n_scales = q.n_scales;
+  return ORACLE_OK;
+}
+
+int oracle_qv_quantize_weights(const OracleDims* dm, const float* w, size_t w_words, int gw, int8_t* codes,
+                               float* scales) {
+  if (!dims_ok(dm) || !qv_groups_ok(*dm, gw)) return ORACLE_EARG;
+  const OracleDims& d = *dm;
+  if (w_words != total_words(d)) return ORACLE_EWEIGHTS;
+  const Q8Layout q = qv_layout(d, gw);
+  const int D = d.d_model, F = d.d_ff;
+  const int wt[4] = {T_ATTN_W, T_APROJ_W, T_FC_W, T_MPROJ_W};
+  const int K[4] = {D, D, D, F}, N[4] = {3 * D, D, F, D};
+  for (int l = 0; l < d.n_layer; ++l)
+    for (int m = 0; m < 4; ++m) {
+      const float* W = w + tensor_off(d, l, wt[m]);  // [K][N]
+      int8_t* c = codes + l * q.layer_codes + q.code_off[m];
+      float* s = scales + l * q.layer_scales + q.scale_off[m];
+      const int G = group_len(gw, K[m]), NG = K[m] / G;
+#pragma omp parallel for schedule(static)
+      for (int j = 0; j < N[m]; ++j) {
+        std::vector<float> col(K[m]);
+        for (int i = 0; i < K[m]; ++i) col[i] = W[(size_t)i * N[m] + j];
+        for (int g = 0; g < NG; ++g)
+          quant_group(col.data() + g * G, G, c + (size_t)j * K[m] + g * G, s + (size_t)j * NG + g);
+      }
+    }
+  const float* wte = w + wte_off(d);
+  const int G = group_len(gw, D), NG = D / G;
+  for (int v = 0; v < d.vocab; ++v)
+    for (int g = 0; g < NG; ++g)
+      quant_group(wte + (size_t)v * D + g * G, G, codes + q.code_off[4] + (size_t)v * D + g * G,
+                  scales + q.scale_off[4] + (size_t)v * NG + g);
+  return ORACLE_OK;
+}
+
+int oracle_qv_cached_step(const OracleDims* dm, const float* w, size_t w_words, int gw, int gx,
+                          const int8_t* codes, const float* scales, float* cache, size_t cache_words, uint32_t tok,
+                          int32_t pos, float* logits) {
+  if (!dims_ok(dm) || !qv_groups_ok(*dm, gw) || !qv_groups_ok(*dm, gx)) return ORACLE_EARG;
+  const int rc = validate_step(dm, w_words, cache_words, tok, pos);
+  if (rc) return rc;
+  ProjQv p(*dm, w, codes, scales, gw, gx);
+  step_body(*dm, w, p, cache, tok, pos, logits);
+  return ORACLE_OK;
+}
+
+// One variant projection from binary32 input x: codes xc_out [K], input scales
+// xs_out [K/gx], accumulators acc_out [N][K/gcd] (each optional), outputs y [N].
+int oracle_qv_linear(int K, int N, const float* x, int gx, const int8_t* wc, const float* ws, int gw,
+                     const float* b, int8_t* xc_out, float* xs_out, int32_t* acc_out, float* y) {
+  if (K <= 0 || N < 0 || !group_ok(gx, K) || !group_ok(gw, K)) return ORACLE_EARG;
+  std::vector<int8_t> xc(K);
+  std::vector<float> xs(K / group_len(gx, K));
+  qv_quantize_input(K, x, gx, xc.data(), xs.data());
+  if (xc_out) std::memcpy(xc_out, xc.data(), K);
+  if (xs_out) std::memcpy(xs_out, xs.data(), xs.size() * sizeof(float));
+  qv_linear_codes(K, N, xc.data(), xs.data(), gx, wc, ws, gw, b, acc_out, y);
   return ORACLE_OK;
 }
 
