@@ -163,6 +163,47 @@ def main() -> int:
     gbs8 = b8 / (ms8 * 1e-3) / 1e9
     gbs16 = b16 / (ms16 * 1e-3) / 1e9
 
+    # int8 quantizer granularity variants (weight-scale group, input-scale group; 0 =
+    # the whole row): ms/step over the 128-position session and the logits' deviation
+    # from the fp32 step's on the same tokens (synthetic weights: a size of the
+    # quantization error, not an accuracy claim)
+    ref = torch.empty((128, g.GPT2_VOCAB), dtype=torch.float32, device=dev)
+    vcache = m.new_cache(128)
+    for p in range(128):
+        g.gpt2_cached_step(h, vcache.data_ptr(), p * PER, int(toks[p]), p, ws, ref[p].data_ptr(), s)
+    vout = torch.empty_like(ref)
+    variants = []
+    for gw, gx in ((64, 64), (0, 64), (64, 0), (0, 0), (128, 128), (256, 256)):
+        if gw == 64:
+            mv = m
+        else:
+            ckv = torch.from_numpy(w).to(dev)
+            mv = g.Model(ckv, g.GPT2_PACK_Q8, q8_weight_group=gw)
+            del ckv
+        vts = []
+        for rep in range(2):
+            vcache.zero_()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for p in range(128):
+                rc = g.gpt2_q8_cached_step_grouped(mv.handle, gx, vcache.data_ptr(), p * PER, int(toks[p]), p,
+                                                   mv.ws.data_ptr(), vout[p].data_ptr(), s)
+                if rc:
+                    raise g.Gpt2Error(rc, "gpt2_q8_cached_step_grouped")
+            e1.record(stream)
+            torch.cuda.synchronize()
+            vts.append(e0.elapsed_time(e1) / 128)
+        dl = (vout - ref).abs()
+        variants.append({"weight_group": gw or "row", "input_group": gx or "row",
+                         "ms_per_step": round(min(vts), 4),
+                         "kernel": "single launch" if gx == 64 else "per phase",
+                         "max_abs_dlogit_vs_fp32": round(float(dl.max()), 5),
+                         "mean_abs_dlogit_vs_fp32": round(float(dl.mean()), 6)})
+        if mv is not m:
+            mv.close()
+            del mv
+
     # greedy generation on the device: an 8-token prompt and 120 chosen tokens
     # (127 steps and 120 on-device choices per call), median of 5 calls
     gprompt = toks[:8].tolist()
@@ -237,6 +278,7 @@ def main() -> int:
                         "roofline": {"bound": "hbm", "achieved": round(gbs16, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                      "frac": round(gbs16 / HBM_PEAK_GBS, 4),
                                      "traffic": measured_traffic("traffic_bytes_per_launch_f16")}},
+        "q8_variants": {"session": "128 positions, seed-101 tokens, seed-0 checkpoint", "rows": variants},
         "generate": {"value": round(120 / (gms * 1e-3), 1), "unit": "tok/s", "ms_per_call": round(gms, 3),
                      "sample": "fp32 greedy, 8-token prompt + 120 tokens chosen on the GPU (127 steps)"},
         "prefill": {"value": round(128 / (pms * 1e-3), 1), "unit": "tok/s", "ms_median": round(pms, 4),

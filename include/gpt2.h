@@ -109,6 +109,23 @@ size_t gpt2_workspace_nbytes(void);
 int gpt2_pack_weights(const void* ckpt_dev, size_t ckpt_nbytes, void* packed_dev, size_t packed_nbytes,
                       int flags, void* stream, gpt2_model** out);
 
+/* gpt2_pack_weights with a chosen int8 weight-scale granularity (marXiv 2609.00018
+ * abstract: its deployed model's 74.3 % smaller checkpoint matches one weight scale
+ * per output row; its group-64 scales are the default).
+ *  q8_weight_group : 64 (gpt2_pack_weights), 128, 192, 256, 384, 768, or 0 for one
+ *                    scale per output row (768 inputs, 3,072 for the MLP projection).
+ *                    Each output row's consecutive groups of that many inputs get
+ *                    scale = max|w|/127 and codes clamp(round-half-even(w/scale),
+ *                    -127, 127), 0 for an all-zero group.  The device form still
+ *                    holds one scale per 64 inputs (the group's, repeated), so
+ *                    every int8 entry point runs unchanged on it.
+ * Other arguments and errors as gpt2_pack_weights; GPT2_EARG for another group. */
+int gpt2_pack_weights_grouped(const void* ckpt_dev, size_t ckpt_nbytes, void* packed_dev, size_t packed_nbytes,
+                              int flags, int q8_weight_group, void* stream, gpt2_model** out);
+
+/* The int8 weight-scale group a model was packed with (0 = per row), -1 for null. */
+int gpt2_q8_weight_group(const gpt2_model* model);
+
 /* Free the host handle (device memory is the caller's). */
 void gpt2_release(gpt2_model* model);
 
@@ -147,6 +164,20 @@ int gpt2_q8_cached_step(const gpt2_model* model, float* cache_dev, size_t cache_
  * gpt2_cached_step; needs GPT2_PACK_F16. */
 int gpt2_f16_cached_step(const gpt2_model* model, float* cache_dev, size_t cache_nwords, uint32_t token,
                          int32_t position, void* ws_dev, float* logits_dev, void* stream);
+
+/* The int8 cached step with input scales per `input_group` consecutive coordinates
+ * of each projection input (marXiv 2609.00018 abstract: its first design took one
+ * scale per activation row, i.e. input_group = 0; its deployed one 64).
+ *  input_group : 64, 128, 192, 256, 384, 768, or 0 for one scale per input vector.
+ * With weight groups gw (gpt2_pack_weights_grouped) and input groups gx, the exact
+ * int32 sums run over the gcd(gx, gw) consecutive coordinates on which both scales
+ * are constant, and y = 0; y = y + ((float)acc_h * sw_h) * sx_h for those groups h
+ * ascending; y = y + bias.  Scale and code rules as gpt2_q8_cached_step, which is
+ * this call with input_group 64.  Input groups other than 64 run as one kernel per
+ * phase.  Same arguments and errors as gpt2_cached_step, plus GPT2_EARG for another
+ * group; needs GPT2_PACK_Q8. */
+int gpt2_q8_cached_step_grouped(const gpt2_model* model, int input_group, float* cache_dev, size_t cache_nwords,
+                                uint32_t token, int32_t position, void* ws_dev, float* logits_dev, void* stream);
 
 /* B independent sessions (1..64) advanced by one token each.
  *  caches_dev         : session b's cache starts at caches_dev + b*cache_stride_words;

@@ -45,6 +45,9 @@ SIGNATURES = {
     "gpt2_cached_step": (_i, [_vp, _vp, _sz, _u32, ctypes.c_int32, _vp, _vp, _vp]),
     "gpt2_q8_cached_step": (_i, [_vp, _vp, _sz, _u32, ctypes.c_int32, _vp, _vp, _vp]),
     "gpt2_f16_cached_step": (_i, [_vp, _vp, _sz, _u32, ctypes.c_int32, _vp, _vp, _vp]),
+    "gpt2_q8_cached_step_grouped": (_i, [_vp, _i, _vp, _sz, _u32, ctypes.c_int32, _vp, _vp, _vp]),
+    "gpt2_pack_weights_grouped": (_i, [_vp, _sz, _vp, _sz, _i, _i, _vp, ctypes.POINTER(_vp)]),
+    "gpt2_q8_weight_group": (_i, [_vp]),
     "gpt2_batched_cached_step": (_i, [_vp, _vp, _sz, _vp, _vp, _vp, _i, _vp, _vp, _vp]),
     "gpt2_infer": (_i, [_vp, _vp, _i, _vp, _vp, _vp]),
     "gpt2_generate": (_i, [_vp, _vp, _sz, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
@@ -109,6 +112,24 @@ def gpt2_pack_weights(ckpt_dev: int, ckpt_nbytes: int, packed_dev: int, packed_n
     h = ctypes.c_void_p()
     rc = lib().gpt2_pack_weights(ckpt_dev, ckpt_nbytes, packed_dev, packed_nbytes, flags, stream, ctypes.byref(h))
     return rc, (h.value if rc == 0 else None)
+
+
+def gpt2_pack_weights_grouped(ckpt_dev: int, ckpt_nbytes: int, packed_dev: int, packed_nbytes: int, flags: int,
+                              q8_weight_group: int, stream: int = 0) -> Tuple[int, Optional[int]]:
+    h = ctypes.c_void_p()
+    rc = lib().gpt2_pack_weights_grouped(ckpt_dev, ckpt_nbytes, packed_dev, packed_nbytes, flags, q8_weight_group,
+                                         stream, ctypes.byref(h))
+    return rc, (h.value if rc == 0 else None)
+
+
+def gpt2_q8_weight_group(model) -> int:
+    return lib().gpt2_q8_weight_group(model)
+
+
+def gpt2_q8_cached_step_grouped(model, input_group, cache_dev, cache_nwords, token, position, ws_dev, logits_dev,
+                                stream=0) -> int:
+    return lib().gpt2_q8_cached_step_grouped(model, input_group, cache_dev, cache_nwords, token & 0xFFFFFFFF,
+                                             position, ws_dev, logits_dev, stream)
 
 
 def gpt2_release(model: int) -> None:
@@ -236,16 +257,17 @@ def _stream() -> int:
 class Model:
     """A packed model whose device memory (packed weights, workspace) torch owns."""
 
-    def __init__(self, ckpt_dev, flags: int = GPT2_PACK_F32):
+    def __init__(self, ckpt_dev, flags: int = GPT2_PACK_F32, q8_weight_group: int = 64):
+        """q8_weight_group: the int8 weight-scale group (gpt2_pack_weights_grouped)."""
         import torch
         self.flags = flags
         n = gpt2_packed_nbytes(flags)
         self.packed = torch.empty(n, dtype=torch.uint8, device=ckpt_dev.device)
         self.ws = torch.zeros(gpt2_workspace_nbytes(), dtype=torch.uint8, device=ckpt_dev.device)
-        rc, h = gpt2_pack_weights(ckpt_dev.data_ptr(), ckpt_dev.numel() * ckpt_dev.element_size(),
-                                  self.packed.data_ptr(), n, flags, _stream())
+        rc, h = gpt2_pack_weights_grouped(ckpt_dev.data_ptr(), ckpt_dev.numel() * ckpt_dev.element_size(),
+                                          self.packed.data_ptr(), n, flags, q8_weight_group, _stream())
         if rc:
-            raise Gpt2Error(rc, "gpt2_pack_weights")
+            raise Gpt2Error(rc, "gpt2_pack_weights_grouped")
         self.handle = h
 
     def close(self) -> None:
@@ -268,7 +290,16 @@ class Model:
         shape = (positions * GPT2_CACHE_WORDS_PER_POS,) if batch == 0 else (batch, positions * GPT2_CACHE_WORDS_PER_POS)
         return torch.zeros(shape, dtype=torch.float32, device=self.packed.device)
 
-    def step(self, cache, pos: int, token: int, logits, q8: bool = False, f16: bool = False) -> None:
+    def step(self, cache, pos: int, token: int, logits, q8: bool = False, f16: bool = False,
+             input_group: int = 64) -> None:
+        """One cached step (int8 with q8; input_group: its input-scale group)."""
+        if q8 and input_group != 64:
+            rc = gpt2_q8_cached_step_grouped(self.handle, input_group, cache.data_ptr(),
+                                             pos * GPT2_CACHE_WORDS_PER_POS, token, pos, self.ws.data_ptr(),
+                                             logits.data_ptr(), _stream())
+            if rc:
+                raise Gpt2Error(rc, "gpt2_q8_cached_step_grouped")
+            return
         fn = gpt2_q8_cached_step if q8 else gpt2_f16_cached_step if f16 else gpt2_cached_step
         rc = fn(self.handle, cache.data_ptr(), pos * GPT2_CACHE_WORDS_PER_POS, token, pos, self.ws.data_ptr(),
                 logits.data_ptr(), _stream())

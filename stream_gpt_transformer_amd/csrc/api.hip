@@ -11,6 +11,7 @@ using namespace g2;
 struct gpt2_model {
   Weights w;
   int flags;
+  int q8_group;  // int8 weight-scale group (coordinates; 0 = the whole row)
   const void* packed;
 };
 
@@ -62,21 +63,33 @@ size_t gpt2_packed_nbytes(int flags) {
 
 size_t gpt2_workspace_nbytes(void) { return ws_layout(MAX_BATCH).total; }
 
+// Scale-group sizes of the int8 granularity variants: 64, larger multiples of 64
+// dividing 768 (so also 3,072), or 0 for the whole row.
+static bool q8_group_ok(int g) { return g == 0 || (g > 0 && g % 64 == 0 && D % g == 0); }
+static int q8_group_units(int g) { return g / 64; }  // 0 stays 0 (the whole row)
+
 int gpt2_pack_weights(const void* ckpt_dev, size_t ckpt_nbytes, void* packed_dev, size_t packed_nbytes,
                       int flags, void* stream, gpt2_model** out) {
-  if (!out || flags < 1 || flags > PACK_FLAGS_ALL) return GPT2_EARG;
+  return gpt2_pack_weights_grouped(ckpt_dev, ckpt_nbytes, packed_dev, packed_nbytes, flags, 64, stream, out);
+}
+
+int gpt2_pack_weights_grouped(const void* ckpt_dev, size_t ckpt_nbytes, void* packed_dev, size_t packed_nbytes,
+                              int flags, int q8_weight_group, void* stream, gpt2_model** out) {
+  if (!out || flags < 1 || flags > PACK_FLAGS_ALL || !q8_group_ok(q8_weight_group)) return GPT2_EARG;
   if (!ckpt_dev || ckpt_nbytes != (size_t)ck::WORDS * 4) return GPT2_EWEIGHTS;
   if (!aligned16(ckpt_dev)) return GPT2_EARG;
   if (!packed_dev || !aligned16(packed_dev) || packed_nbytes < packed_layout(flags).total) return GPT2_EARG;
   gpt2_model* m = new (std::nothrow) gpt2_model();
   if (!m) return GPT2_EARG;
-  if (launch_pack((const float*)ckpt_dev, (char*)packed_dev, flags, (hipStream_t)stream) != hipSuccess) {
+  if (launch_pack((const float*)ckpt_dev, (char*)packed_dev, flags, (hipStream_t)stream, q8_weight_group) !=
+      hipSuccess) {
     delete m;
     return GPT2_EHIP;
   }
   const PackedLayout pl = packed_layout(flags);
   const char* p = (const char*)packed_dev;
   m->flags = flags;
+  m->q8_group = q8_weight_group;
   m->packed = packed_dev;
   m->w.wte = (const float*)(p + pl.wte);
   m->w.wpe = (const float*)(p + pl.wpe);
@@ -94,11 +107,14 @@ void gpt2_release(gpt2_model* model) { delete model; }
 // One validated batch-1 step: the single-launch kernel, or the per-phase kernels
 // where it cannot run.  tokp: read the token from device memory instead (it must be
 // the workspace header's word HDR_WORD_NEXT_TOKEN).
+// qx: the int8 input-scale group in units of 64 (0 = the whole row).  Only
+// 64-coordinate input groups run in the single-launch kernel (which reads one
+// weight scale per 64 inputs, replicated at packing for larger weight groups).
 static int enqueue_step(const gpt2_model* m, WFmt f, float* cache, uint32_t token, const uint32_t* tokp,
-                        int32_t pos, void* ws, float* logits, char* capture, hipStream_t s) {
+                        int32_t pos, void* ws, float* logits, char* capture, hipStream_t s, int qx = 1) {
   const Work k = work_ptrs(ws, MAX_BATCH);
   bool used = false;
-  if (!g_force_phase_kernels &&
+  if (!g_force_phase_kernels && qx == 1 &&
       launch_fused(f, m->w, k, token, pos, cache, logits, capture, s, &used, tokp != nullptr) != hipSuccess)
     return GPT2_EHIP;
   if (used) return GPT2_OK;
@@ -106,8 +122,9 @@ static int enqueue_step(const gpt2_model* m, WFmt f, float* cache, uint32_t toke
   ss.B = 1;
   ss.tok[0] = token;
   ss.pos[0] = pos;
-  const hipError_t e = f == WF_Q8 ? launch_step_q8(m->w, k, ss, cache, logits, capture, s, tokp)
-                                  : launch_step_f32(m->w, k, ss, cache, 0, logits, s, tokp, f == WF_F16);
+  const hipError_t e = f == WF_Q8
+                           ? launch_step_q8(m->w, k, ss, cache, logits, capture, s, tokp, qx, q8_group_units(m->q8_group))
+                           : launch_step_f32(m->w, k, ss, cache, 0, logits, s, tokp, f == WF_F16);
   return e == hipSuccess ? GPT2_OK : GPT2_EHIP;
 }
 
@@ -165,6 +182,17 @@ int gpt2_q8_cached_step(const gpt2_model* m, float* cache, size_t cache_nwords, 
                         void* ws, float* logits, void* stream) {
   return q8_step(m, cache, cache_nwords, token, pos, ws, logits, nullptr, stream);
 }
+
+int gpt2_q8_cached_step_grouped(const gpt2_model* m, int input_group, float* cache, size_t cache_nwords,
+                                uint32_t token, int32_t pos, void* ws, float* logits, void* stream) {
+  if (!q8_group_ok(input_group)) return GPT2_EARG;
+  const int rc = step_checks(m, GPT2_PACK_Q8, cache, cache_nwords, token, pos, ws, logits);
+  if (rc) return rc;
+  return enqueue_step(m, WF_Q8, cache, token, nullptr, pos, ws, logits, nullptr, (hipStream_t)stream,
+                      q8_group_units(input_group));
+}
+
+int gpt2_q8_weight_group(const gpt2_model* m) { return m ? m->q8_group : -1; }
 
 int gpt2_q8_cached_step_capture(const gpt2_model* m, float* cache, size_t cache_nwords, uint32_t token,
                                 int32_t pos, void* ws, float* logits, void* capture, void* stream) {

@@ -23,6 +23,7 @@ struct ProjArgs {
   char* capture;        // int8 path capture buffer or null
   const uint32_t* tokp; // session 0's token in device memory, or null
   int layer;
+  int qx, qw;           // int8 input / weight scale groups in units of 64 (0 = the whole row)
 };
 
 template <class T>
@@ -191,6 +192,35 @@ __global__ __launch_bounds__(128) void k_attn(const ProjArgs a) {
 // and two exact integer butterfly steps give the group accumulator.  The rescale
 // runs in one fixed order: y = 0; y = y + ((float)acc_g * sw_g) * sx_g for
 // g = 0..G-1; y = y + bias.
+// Granularity variants (qx, qw other than 64-coordinate groups; marXiv 2609.00018
+// abstract): an input group takes the largest magnitude of its 64-coordinate
+// pieces (an exact maximum) and quant_lane's scale and code rules; the exact group
+// accumulators of the gm = gcd(gx, gw) coordinates on which both scales are
+// constant are integer sums of the 64-coordinate ones, and y = 0; y = y +
+// ((float)acc_h * sw_h) * sx_h for h ascending; y = y + bias.
+__device__ __forceinline__ int gcd_int(int a, int b) {
+  while (b) {
+    const int t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+template <int K>
+__device__ __forceinline__ float q8_dot_groups(const i4 (&wc)[(K + 1023) / 1024], float swl, const int8_t* xc,
+                                               const float* xsc, int qm) {
+  constexpr int G = K / 64;
+  const int accg = q8_group_acc<K>(wc, xc, lane_id());
+  float y = 0.0f;
+  for (int h = 0; h < G / qm; ++h) {
+    int acc = 0;
+    for (int t = 0; t < qm; ++t) acc += __builtin_amdgcn_readlane(accg, h * qm + t);
+    const float sw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(swl), h * qm));
+    y = y + ((float)acc * sw) * xsc[h * qm];
+  }
+  return y;
+}
+
 template <int MODE, int RPW>
 __global__ __launch_bounds__(256) void k_q8proj(const ProjArgs a) {
   constexpr int K = MODE == MODE_PR ? F : D;
@@ -202,7 +232,9 @@ __global__ __launch_bounds__(256) void k_q8proj(const ProjArgs a) {
   __shared__ __align__(16) float lntmp[mode_ln<MODE>() ? D : 1];
   __shared__ __align__(16) int8_t xc[K];
   __shared__ float xsc[G];
+  __shared__ float xm[G];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int qx = a.qx == 0 ? G : a.qx, qm = gcd_int(qx, a.qw == 0 ? G : a.qw);
   const CapLayout cl = cap_item(MODE);
   char* cap = a.capture ? a.capture + cap_offset(a.layer, MODE) : nullptr;
 
@@ -216,11 +248,27 @@ __global__ __launch_bounds__(256) void k_q8proj(const ProjArgs a) {
     if (wave == 0) layernorm_seq(xf, ln_gamma<MODE>(a), ln_beta<MODE>(a), xf, lntmp);
     __syncthreads();
   }
-  for (int g = wave; g < G; g += 4) {
-    float s;
-    const int c = quant_lane(xf[g * 64 + lane], s);
-    xc[g * 64 + lane] = (int8_t)c;
-    if (lane == 0) xsc[g] = s;
+  if (qx == 1) {
+    for (int g = wave; g < G; g += 4) {
+      float s;
+      const int c = quant_lane(xf[g * 64 + lane], s);
+      xc[g * 64 + lane] = (int8_t)c;
+      if (lane == 0) xsc[g] = s;
+    }
+  } else {
+    for (int g = wave; g < G; g += 4) {
+      const float m = wave_max(fabsf(xf[g * 64 + lane]));
+      if (lane == 0) xm[g] = m;
+    }
+    __syncthreads();
+    for (int g = wave; g < G; g += 4) {
+      const int g0 = g - g % qx;
+      float m = 0.0f;
+      for (int t = 0; t < qx; ++t) m = fmaxf(m, xm[g0 + t]);
+      const float sc = m == 0.0f ? 0.0f : m / 127.0f;
+      xc[g * 64 + lane] = m == 0.0f ? 0 : (int8_t)quant_code(xf[g * 64 + lane], sc);
+      if (lane == 0) xsc[g] = sc;
+    }
   }
   __syncthreads();
   if (cap && blockIdx.x == 0) {
@@ -242,7 +290,7 @@ __global__ __launch_bounds__(256) void k_q8proj(const ProjArgs a) {
     float swl;
     q8_load_row<K>(wc, swl, codes, scales, r);
     int32_t* ca = cap ? (int32_t*)(cap + cl.acc) + (size_t)r * G : nullptr;
-    float y = q8_dot<K>(wc, swl, xc, xsc, ca);
+    float y = qm == 1 ? q8_dot<K>(wc, swl, xc, xsc, ca) : q8_dot_groups<K>(wc, swl, xc, xsc, qm);
     y = y + proj_bias<MODE>(a, r);
     if (cap && lane == 0) ((float*)(cap + cl.y))[r] = y;
     if (lane == 0) proj_store<MODE>(a, 0, r, y);
@@ -405,7 +453,7 @@ static void launch_q8(const ProjArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_step_q8(const Weights& w, const Work& k, const Sessions& ss, float* cache,
-                          float* logits, char* capture, hipStream_t s, const uint32_t* tokp) {
+                          float* logits, char* capture, hipStream_t s, const uint32_t* tokp, int qx, int qw) {
   ProjArgs a{};
   a.w = w;
   a.k = k;
@@ -414,6 +462,8 @@ hipError_t launch_step_q8(const Weights& w, const Work& k, const Sessions& ss, f
   a.cache_stride = 0;
   a.logits = logits;
   a.capture = capture;
+  a.qx = qx;
+  a.qw = qw;
   hipLaunchKernelGGL(k_embed, dim3(1), dim3(192), 0, s, w, ss, k.x, tokp);
   for (int l = 0; l < L; ++l) {
     a.layer = l;

@@ -734,11 +734,10 @@ __device__ __forceinline__ int quant_lane(float x, float& s_out) {
 //   t[g] = ((float)acc[g] * sw[g]) * sx[g] in lane g;
 //   y = 0; y = y + t[g] for g = 0..K/64-1  (fixed order, through readlane).
 // cap_acc (may be null) receives acc[0..K/64-1].  Bias excluded.
+// q8_group_acc alone: acc[lane] in lane < K/64 (lane = lane_id()).
 template <int K>
-__device__ __forceinline__ float q8_dot(const i4 (&wc)[(K + 1023) / 1024], float swl, const int8_t* xc,
-                                        const float* xsc, int32_t* cap_acc) {
-  constexpr int NCH = (K + 1023) / 1024, G = K / 64;
-  const int lane = lane_id();
+__device__ __forceinline__ int q8_group_acc(const i4 (&wc)[(K + 1023) / 1024], const int8_t* xc, int lane) {
+  constexpr int NCH = (K + 1023) / 1024;
   int accg = 0;  // acc[lane] for lane < G
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
@@ -755,6 +754,14 @@ __device__ __forceinline__ float q8_dot(const i4 (&wc)[(K + 1023) / 1024], float
     const int gi = __shfl(p, 4 * (lane & 15));  // group 16*i + (lane & 15)
     if ((lane >> 4) == i) accg = gi;
   }
+  return accg;
+}
+template <int K>
+__device__ __forceinline__ float q8_dot(const i4 (&wc)[(K + 1023) / 1024], float swl, const int8_t* xc,
+                                        const float* xsc, int32_t* cap_acc) {
+  constexpr int G = K / 64;
+  const int lane = lane_id();
+  const int accg = q8_group_acc<K>(wc, xc, lane);
   if (cap_acc && lane < G) cap_acc[lane] = accg;
   const float t = lane < G ? ((float)accg * swl) * xsc[lane] : 0.0f;
   float y = 0.0f;

@@ -55,7 +55,7 @@ struct Work {
 
 Work work_ptrs(void* ws, int max_batch);
 
-hipError_t launch_pack(const float* ckpt, char* packed, int flags, hipStream_t s);
+hipError_t launch_pack(const float* ckpt, char* packed, int flags, hipStream_t s, int q8_group = 64);
 // Header word of the workspace that carries the token a generation step is fed
 // (written by k_argmax, read by the step's embedding).
 constexpr int HDR_WORD_NEXT_TOKEN = 3;
@@ -68,8 +68,11 @@ enum WFmt { WF_F32 = 0, WF_Q8 = 1, WF_F16 = 2 };
 hipError_t launch_step_f32(const Weights& w, const Work& k, const Sessions& ss, float* caches,
                            size_t cache_stride, float* logits, hipStream_t s, const uint32_t* tokp = nullptr,
                            bool h16 = false);
+// qx, qw: the input- and weight-scale groups in units of 64 coordinates (64*q
+// dividing 768, or 0 for the whole row); the weights must have been packed with qw.
 hipError_t launch_step_q8(const Weights& w, const Work& k, const Sessions& ss, float* cache,
-                          float* logits, char* capture, hipStream_t s, const uint32_t* tokp = nullptr);
+                          float* logits, char* capture, hipStream_t s, const uint32_t* tokp = nullptr, int qx = 1,
+                          int qw = 1);
 hipError_t launch_argmax(const float* logits, uint32_t* next, uint32_t* tokens_out, int32_t* status, int step,
                          hipStream_t s);
 // cache (or null): the key/value rows of positions 0..n-1 are also written there

@@ -83,7 +83,56 @@ __global__ __launch_bounds__(256) void k_quant_rows(const float* __restrict__ sr
   if (lane == 0) scales[(size_t)r * G + g] = s;
 }
 
-hipError_t launch_pack(const float* ck_, char* packed, int flags, hipStream_t s) {
+// Weight-scale groups of gw inputs (gw a multiple of 64 dividing K; the marXiv
+// 2609.00018 abstract's granularity variants): output n, group j of a checkpoint
+// matrix src[K][N] gets scale (max |w| over the group)/127 and codes
+// clamp(rint(w/scale), -127, 127) (0 for an all-zero group), as quant_lane does
+// for 64 inputs.  The scale is written to each 64-input slot of the group, so the
+// int8 kernels read one scale per 64 inputs whatever gw is.  Thread = (output n,
+// group blockIdx.y); one-time work.
+__global__ __launch_bounds__(256) void k_quant_in_out_g(const float* __restrict__ src, int8_t* __restrict__ codes,
+                                                        float* __restrict__ scales, int K, int N, int gw) {
+  const int n = blockIdx.x * 256 + threadIdx.x, j = blockIdx.y;
+  if (n >= N) return;
+  const float* col = src + (size_t)j * gw * N + n;
+  float m = 0.0f;
+  for (int i = 0; i < gw; ++i) m = fmaxf(m, fabsf(col[(size_t)i * N]));
+  const float sc = m == 0.0f ? 0.0f : m / 127.0f;
+  int8_t* c = codes + (size_t)n * K + (size_t)j * gw;
+  for (int i = 0; i < gw; i += 4) {
+    int packed = 0;
+    if (m != 0.0f)
+      for (int e = 0; e < 4; ++e) packed |= (quant_code(col[(size_t)(i + e) * N], sc) & 0xff) << (8 * e);
+    *(int*)(c + i) = packed;
+  }
+  for (int t = 0; t < gw / 64; ++t) scales[(size_t)n * (K / 64) + (size_t)j * (gw / 64) + t] = sc;
+}
+
+// The same for rows already stored [rows][K] (the tied head: wte rows).  Thread =
+// (row, group).
+__global__ __launch_bounds__(256) void k_quant_rows_g(const float* __restrict__ src, int8_t* __restrict__ codes,
+                                                      float* __restrict__ scales, int rows, int K, int gw) {
+  const long long item = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int ng = K / gw;
+  if (item >= (long long)rows * ng) return;
+  const int r = (int)(item / ng), j = (int)(item % ng);
+  const float* x = src + (size_t)r * K + (size_t)j * gw;
+  float m = 0.0f;
+  for (int i = 0; i < gw; ++i) m = fmaxf(m, fabsf(x[i]));
+  const float sc = m == 0.0f ? 0.0f : m / 127.0f;
+  int8_t* c = codes + (size_t)r * K + (size_t)j * gw;
+  for (int i = 0; i < gw; i += 4) {
+    int packed = 0;
+    if (m != 0.0f)
+      for (int e = 0; e < 4; ++e) packed |= (quant_code(x[i + e], sc) & 0xff) << (8 * e);
+    *(int*)(c + i) = packed;
+  }
+  for (int t = 0; t < gw / 64; ++t) scales[(size_t)r * (K / 64) + (size_t)j * (gw / 64) + t] = sc;
+}
+
+// q8_group: the int8 weight-scale group (64, a larger multiple of 64 dividing 768,
+// or 0 for one scale per output row).
+hipError_t launch_pack(const float* ck_, char* packed, int flags, hipStream_t s, int q8_group) {
   const PackedLayout pl = packed_layout(flags);
   float* wte = (float*)(packed + pl.wte);
   float* wpe = (float*)(packed + pl.wpe);
@@ -126,7 +175,13 @@ hipError_t launch_pack(const float* ck_, char* packed, int flags, hipStream_t s)
       if (flags & 2) {
         int8_t* codes = (int8_t*)(packed + pl.q8_codes) + (size_t)l * LAYER_ELEMS + mat_elem_off(m);
         float* scales = (float*)(packed + pl.q8_scales) + (size_t)l * LAYER_SCALES + mat_scale_off(m);
-        hipLaunchKernelGGL(k_quant_in_out, dim3(N / 64, K / 64), dim3(256), 0, s, src, codes, scales, K, N);
+        if (q8_group == 64) {
+          hipLaunchKernelGGL(k_quant_in_out, dim3(N / 64, K / 64), dim3(256), 0, s, src, codes, scales, K, N);
+        } else {
+          const int gw = q8_group == 0 ? K : q8_group;
+          hipLaunchKernelGGL(k_quant_in_out_g, dim3((N + 255) / 256, K / gw), dim3(256), 0, s, src, codes, scales,
+                             K, N, gw);
+        }
       }
     }
   }
@@ -138,8 +193,15 @@ hipError_t launch_pack(const float* ck_, char* packed, int flags, hipStream_t s)
   if (flags & 2) {
     int8_t* codes = (int8_t*)(packed + pl.q8_codes) + (size_t)L * LAYER_ELEMS;
     float* scales = (float*)(packed + pl.q8_scales) + (size_t)L * LAYER_SCALES;
-    const int items = V * (D / 64);
-    hipLaunchKernelGGL(k_quant_rows, dim3((items + 3) / 4), dim3(256), 0, s, ck_ + ck::WTE, codes, scales, V, D);
+    if (q8_group == 64) {
+      const int items = V * (D / 64);
+      hipLaunchKernelGGL(k_quant_rows, dim3((items + 3) / 4), dim3(256), 0, s, ck_ + ck::WTE, codes, scales, V, D);
+    } else {
+      const int gw = q8_group == 0 ? D : q8_group;
+      const long long items = (long long)V * (D / gw);
+      hipLaunchKernelGGL(k_quant_rows_g, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, ck_ + ck::WTE, codes,
+                         scales, V, D, gw);
+    }
   }
   return hipGetLastError();
 }

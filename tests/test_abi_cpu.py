@@ -80,8 +80,16 @@ def test_pack_validation():
 
 
 def test_step_validation_without_model():
-    for fn in (g.gpt2_cached_step, g.gpt2_q8_cached_step):
+    for fn in (g.gpt2_cached_step, g.gpt2_q8_cached_step, g.gpt2_f16_cached_step):
         assert fn(None, FAKE, 0, 0, 0, FAKE, FAKE) == g.GPT2_EARG
+    for grp in (64, 0, 384):
+        assert g.gpt2_q8_cached_step_grouped(None, grp, FAKE, 0, 0, 0, FAKE, FAKE) == g.GPT2_EARG
+    assert g.gpt2_q8_cached_step_grouped(None, 96, FAKE, 0, 0, 0, FAKE, FAKE) == g.GPT2_EARG
+    assert g.gpt2_q8_weight_group(None) == -1
+    # an invalid weight group is rejected before any device work
+    for grp in (32, 96, 1536, 3072, -64):
+        rc, h = g.gpt2_pack_weights_grouped(FAKE, g.GPT2_CKPT_BYTES, FAKE, 1 << 40, g.GPT2_PACK_Q8, grp)
+        assert rc == g.GPT2_EARG and h is None
     assert g.gpt2_infer(None, [1, 2], FAKE, FAKE) == g.GPT2_EARG
     assert g.gpt2_batched_cached_step(None, FAKE, 18432, [0], [0], [0], FAKE, FAKE) == g.GPT2_EARG
 
