@@ -612,7 +612,6 @@ __device__ __forceinline__ void attn_stage(AttnSmem& sm, RowPtr kv, int npos, co
 // synchronises the block through LDS-only barriers.
 __device__ __forceinline__ float attn_compute(AttnSmem& sm, int npos, int nthr) {
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
-  const bool act = t < 128;
   // scores: unit u = 4*key + quarter, a lane quad per key
   for (int u = t; u < 4 * PMAX; u += nthr) {
     const int key = u >> 2, r = u & 3;
@@ -629,18 +628,20 @@ __device__ __forceinline__ float attn_compute(AttnSmem& sm, int npos, int nthr) 
     if (r == 0 && key < npos) sm.w[key] = P * 0.125f;
   }
   lds_barrier();
-  const float s = (act && t < npos) ? sm.w[t] : -INFINITY;
-  const float mw = wave_max(s);
-  if (act && lane == 0) sm.red[wv] = mw;
-  lds_barrier();
-  const float m = fmaxf(sm.red[0], sm.red[1]);
-  const float e = (act && t < npos) ? exp_spec(s - m) : 0.0f;
-  const float zw = wave_sum(e);
-  lds_barrier();  // everyone has read red[0..1]
-  if (act && lane == 0) sm.red[2 + wv] = zw;
-  lds_barrier();
-  const float Z = sm.red[2] + sm.red[3];
-  if (act) sm.w[t] = e / Z;
+  // Softmax by wave 0 alone over both halves of the 128 score slots: the maximum is
+  // the fmaxf of the two wave maxima over slots 0..63 and 64..127, and Z the sum of
+  // the two wave sums, the same trees and order as with one wave per half, so no
+  // other wave takes part and no exchange between waves is needed.
+  if (wv == 0) {
+    const float s0 = lane < npos ? sm.w[lane] : -INFINITY;
+    const float s1 = 64 + lane < npos ? sm.w[64 + lane] : -INFINITY;
+    const float m = fmaxf(wave_max(s0), wave_max(s1));
+    const float e0 = lane < npos ? exp_spec(s0 - m) : 0.0f;
+    const float e1 = 64 + lane < npos ? exp_spec(s1 - m) : 0.0f;
+    const float Z = wave_sum(e0) + wave_sum(e1);
+    sm.w[lane] = e0 / Z;
+    sm.w[64 + lane] = e1 / Z;
+  }
   lds_barrier();
   for (int b = wv; b < ATT_VB; b += nthr / 64) {
     float p = 0.0f;
