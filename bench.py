@@ -245,13 +245,16 @@ def main() -> int:
         ocache = np.zeros(128 * PER, np.float32)
         t0 = time.perf_counter()
         n = 0
-        while n < 128 and time.perf_counter() - t0 < args.cpu_seconds:
-            rc, _ = oracle.cached_step(synth.GPT2, w, ocache, n * PER, int(toks[n]), n)
+        # the session's positions in order, starting over from an empty cache after 127,
+        # until the time budget is spent (at least one step)
+        while n == 0 or time.perf_counter() - t0 < args.cpu_seconds:
+            p = n % 128
+            rc, _ = oracle.cached_step(synth.GPT2, w, ocache, p * PER, int(toks[p]), p)
             assert rc == 0
             n += 1
         el = time.perf_counter() - t0
         cpu = {"value": round(n / el, 3), "unit": "tok/s", "cores": oracle.max_threads(), "kind": "oracle",
-               "sample": f"fp32 cachedStep positions 0..{n - 1} of the same 128-token session "
+               "sample": f"{n} fp32 cachedStep calls cycling positions 0..127 of the same 128-token session "
                          f"({el:.1f} s, OpenMP over independent outputs)"}
 
     out = {
