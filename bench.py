@@ -39,6 +39,11 @@ F16_FIXED = 169_869_312 + 77_194_752 + 485_376 + 6_144
 KV_PER_POS = 73_728
 LOGITS = 201_028
 PREFILL_FLOP = 21_743_271_936 + 304_349_184  # block GEMMs + causal attention at T = 128
+# Batched step, 64 sessions: 2 FLOP per weight and session over the 48 block matrices and
+# the head (123,532,032 weights), i.e. 15,812,100,096 FLOP per step; fp32 vector FMA peak.
+BATCH = 64
+BATCH_FLOP = 2 * BATCH * 123_532_032
+FP32_VECTOR_PEAK_TF = 157.3
 
 
 def step_bytes(fixed: int, p: int) -> int:
@@ -222,6 +227,30 @@ def main() -> int:
     assert int(gst.item()) == 0
     gms = statistics.median(gts)
 
+    # batched step: 64 sessions (seeded token streams 1000..1063) advanced together over
+    # positions 0..127, after a warm-up pass over positions 0..15; per batched step
+    btoks = np.stack([synth.make_tokens(synth.SEED_BATCH_BASE + b, 128) for b in range(BATCH)])
+    bcaches = torch.zeros((BATCH, 128 * PER), dtype=torch.float32, device=dev)
+    blog = torch.empty((BATCH, g.GPT2_VOCAB), dtype=torch.float32, device=dev)
+
+    def bstep(p):
+        rc = g.gpt2_batched_cached_step(h, bcaches.data_ptr(), 128 * PER, [p * PER] * BATCH,
+                                        btoks[:, p].tolist(), [p] * BATCH, ws, blog.data_ptr(), s)
+        if rc:
+            raise g.Gpt2Error(rc, "gpt2_batched_cached_step")
+
+    for p in range(16):
+        bstep(p)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for p in range(128):
+        bstep(p)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    bms = e0.elapsed_time(e1) / 128
+    del bcaches, blog
+
     # prefill: median of 20 infer(128) calls after warm-up
     ptoks = synth.make_tokens(synth.SEED_PREFILL, 128).tolist()
     for _ in range(3):
@@ -282,6 +311,11 @@ def main() -> int:
                                      "frac": round(gbs16 / HBM_PEAK_GBS, 4),
                                      "traffic": measured_traffic("traffic_bytes_per_launch_f16")}},
         "q8_variants": {"session": "128 positions, seed-101 tokens, seed-0 checkpoint", "rows": variants},
+        "batched": {"value": round(BATCH / (bms * 1e-3), 1), "unit": "tok/s", "ms_per_step": round(bms, 4),
+                    "sample": "64 sessions advanced together, positions 0..127 (fp32)",
+                    "roofline": {"bound": "alu", "achieved": round(BATCH_FLOP / (bms * 1e-3) / 1e12, 2),
+                                 "peak": FP32_VECTOR_PEAK_TF, "unit": "TFLOP/s",
+                                 "frac": round(BATCH_FLOP / (bms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TF, 4)}},
         "generate": {"value": round(120 / (gms * 1e-3), 1), "unit": "tok/s", "ms_per_call": round(gms, 3),
                      "sample": "fp32 greedy, 8-token prompt + 120 tokens chosen on the GPU (127 steps)"},
         "prefill": {"value": round(128 / (pms * 1e-3), 1), "unit": "tok/s", "ms_median": round(pms, 4),

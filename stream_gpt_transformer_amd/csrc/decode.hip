@@ -24,6 +24,8 @@ struct ProjArgs {
   const uint32_t* tokp; // session 0's token in device memory, or null
   int layer;
   int qx, qw;           // int8 input / weight scale groups in units of 64 (0 = the whole row)
+  int sb;               // k_proj: sessions per workgroup (blockIdx.y takes sessions sb*y ..)
+  int preln;            // k_proj: LayerNorm inputs already normalised in k.att (k_bln)
 };
 
 template <class T>
@@ -116,8 +118,9 @@ __device__ __forceinline__ float proj_dot(const f4 (&w)[NI], const f4 (&x)[NI]) 
 // fp32 projection over B sessions.  Block = 4 waves; wave w owns RPW consecutive
 // output rows, whose weights it loads once; sessions are staged BT at a time in
 // LDS as (normalised) input fragments.  Output r of session b is
-// proj_dot(W_r, x_b) + bias_r — the same value for any B, RPW or BT.  H16: the
-// weights are read as binary16 and widened (exact) when loaded.
+// proj_dot(W_r, x_b) + bias_r — the same value for any B, RPW, BT or session split
+// (blockIdx.y takes sessions a.sb*y .. a.sb*y + a.sb - 1).  H16: the weights are read
+// as binary16 and widened (exact) when loaded.
 template <int MODE, int RPW, int BT, bool H16>
 __global__ __launch_bounds__(256) void k_proj(const ProjArgs a) {
   constexpr int NI = MODE == MODE_PR ? F / 256 : D / 256;
@@ -143,12 +146,14 @@ __global__ __launch_bounds__(256) void k_proj(const ProjArgs a) {
   float bias[RPW];
 #pragma unroll
   for (int rr = 0; rr < RPW; ++rr) bias[rr] = row0 + rr < NROWS ? proj_bias<MODE>(a, row0 + rr) : 0.0f;
-  for (int b0 = 0; b0 < a.ss.B; b0 += BT) {
-    const int nb = min(BT, a.ss.B - b0);
+  const int sb1 = min(a.ss.B, (int)(blockIdx.y + 1) * a.sb);
+  for (int b0 = blockIdx.y * a.sb; b0 < sb1; b0 += BT) {
+    const int nb = min(BT, sb1 - b0);
     __syncthreads();
     for (int s = wave; s < nb; s += 4) {
       f4 x[NI];
-      proj_input<MODE, NI>(a, b0 + s, x);
+      if (mode_ln<MODE>() && a.preln) load_frag<NI>(x, a.k.att + (size_t)(b0 + s) * D);
+      else proj_input<MODE, NI>(a, b0 + s, x);
       store_frag<NI>(&xs[s][0], x);
     }
     __syncthreads();
@@ -164,6 +169,16 @@ __global__ __launch_bounds__(256) void k_proj(const ProjArgs a) {
       }
     }
   }
+}
+
+// The LayerNorm input of a batched projection, once per session (proj_input's
+// values), into the attention-output buffer, which is free at that point of the
+// block: k_proj then reads it instead of normalising in every workgroup.
+template <int MODE>
+__global__ __launch_bounds__(64) void k_bln(const ProjArgs a) {
+  f4 x[3];
+  proj_input<MODE, 3>(a, blockIdx.x, x);
+  store_frag<3>(a.k.att + (size_t)blockIdx.x * D, x);
 }
 
 // Attention of head blockIdx.x for session blockIdx.y over its positions 0..pos,
@@ -401,26 +416,48 @@ __global__ __launch_bounds__(256) void k_special_bits(int kind, uint32_t first, 
 
 // ---- launchers ---------------------------------------------------------------
 
+// Batched step (B > 1) launch shape: rows per wave, sessions staged per pass for the
+// 768- and 3,072-input projections, sessions per workgroup (grid.y = B / BATCH_SB).
+#ifndef BATCH_RPW
+#define BATCH_RPW 2
+#endif
+#ifndef BATCH_BT768
+#define BATCH_BT768 8
+#endif
+#ifndef BATCH_BT3072
+#define BATCH_BT3072 4
+#endif
+#ifndef BATCH_SB
+#define BATCH_SB 8
+#endif
+
 template <int MODE, int RPW, int BT, bool H16>
 static void launch_proj(const ProjArgs& a, hipStream_t s) {
   const int rows = MODE == MODE_QKV ? D3 : MODE == MODE_FC ? F : MODE == MODE_HEAD ? V : D;
   const int nblk = (rows + 4 * RPW - 1) / (4 * RPW);
-  hipLaunchKernelGGL((k_proj<MODE, RPW, BT, H16>), dim3(nblk), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_proj<MODE, RPW, BT, H16>), dim3(nblk, (a.ss.B + a.sb - 1) / a.sb), dim3(256), 0, s, a);
 }
 
+// With a.preln (batched step), the LayerNorm inputs are normalised once per session
+// first (k_bln) and the projections read them.
+template <int MODE, int RPW, int BT, bool H16>
+static void launch_proj_ln(const ProjArgs& a, hipStream_t s) {
+  if (a.preln) hipLaunchKernelGGL(k_bln<MODE>, dim3(a.ss.B), dim3(64), 0, s, a);
+  launch_proj<MODE, RPW, BT, H16>(a, s);
+}
 template <int RPW, int BT768, int BT3072, bool H16>
 static void launch_layers(ProjArgs& a, hipStream_t s) {
   const int B = a.ss.B;
   hipLaunchKernelGGL(k_embed, dim3(B), dim3(192), 0, s, a.w, a.ss, a.k.x, a.tokp);
   for (int l = 0; l < L; ++l) {
     a.layer = l;
-    launch_proj<MODE_QKV, RPW, BT768, H16>(a, s);
+    launch_proj_ln<MODE_QKV, RPW, BT768, H16>(a, s);
     hipLaunchKernelGGL(k_attn<false>, dim3(H, B), dim3(128), 0, s, a);
     launch_proj<MODE_O, RPW, BT768, H16>(a, s);
-    launch_proj<MODE_FC, RPW, BT768, H16>(a, s);
+    launch_proj_ln<MODE_FC, RPW, BT768, H16>(a, s);
     launch_proj<MODE_PR, RPW, BT3072, H16>(a, s);
   }
-  launch_proj<MODE_HEAD, RPW, BT768, H16>(a, s);
+  launch_proj_ln<MODE_HEAD, RPW, BT768, H16>(a, s);
 }
 
 hipError_t launch_step_f32(const Weights& w, const Work& k, const Sessions& ss, float* caches,
@@ -434,13 +471,15 @@ hipError_t launch_step_f32(const Weights& w, const Work& k, const Sessions& ss, 
   a.logits = logits;
   a.capture = nullptr;
   a.tokp = tokp;
+  a.sb = ss.B == 1 ? 1 : BATCH_SB;
   if (h16) {
     if (ss.B != 1) return hipErrorInvalidValue;
     launch_layers<2, 1, 1, true>(a, s);
   } else if (ss.B == 1) {
     launch_layers<2, 1, 1, false>(a, s);
   } else {
-    launch_layers<4, 16, 4, false>(a, s);
+    a.preln = 1;
+    launch_layers<BATCH_RPW, BATCH_BT768, BATCH_BT3072, false>(a, s);
   }
   return hipGetLastError();
 }
@@ -464,6 +503,7 @@ hipError_t launch_step_q8(const Weights& w, const Work& k, const Sessions& ss, f
   a.capture = capture;
   a.qx = qx;
   a.qw = qw;
+  a.sb = 1;
   hipLaunchKernelGGL(k_embed, dim3(1), dim3(192), 0, s, w, ss, k.x, tokp);
   for (int l = 0; l < L; ++l) {
     a.layer = l;
@@ -483,6 +523,7 @@ hipError_t launch_head_f32(const Weights& w, const float* x_row, float* logits, 
   a.w = w;
   a.k.x = const_cast<float*>(x_row);
   a.ss.B = 1;
+  a.sb = 1;
   a.logits = logits;
   launch_proj<MODE_HEAD, 2, 1, false>(a, s);
   return hipGetLastError();
