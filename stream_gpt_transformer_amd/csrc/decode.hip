@@ -430,6 +430,16 @@ __global__ __launch_bounds__(256) void k_special_bits(int kind, uint32_t first, 
 #ifndef BATCH_SB
 #define BATCH_SB 8
 #endif
+// the head (50,257 rows): more rows and sessions per workgroup, fewer input re-reads
+#ifndef BATCH_HEAD_RPW
+#define BATCH_HEAD_RPW 4
+#endif
+#ifndef BATCH_HEAD_SB
+#define BATCH_HEAD_SB 32
+#endif
+#ifndef BATCH_HEAD_BT
+#define BATCH_HEAD_BT 16
+#endif
 
 template <int MODE, int RPW, int BT, bool H16>
 static void launch_proj(const ProjArgs& a, hipStream_t s) {
@@ -457,7 +467,13 @@ static void launch_layers(ProjArgs& a, hipStream_t s) {
     launch_proj_ln<MODE_FC, RPW, BT768, H16>(a, s);
     launch_proj<MODE_PR, RPW, BT3072, H16>(a, s);
   }
-  launch_proj_ln<MODE_HEAD, RPW, BT768, H16>(a, s);
+  if (a.preln) {
+    ProjArgs ah = a;
+    ah.sb = BATCH_HEAD_SB;
+    launch_proj_ln<MODE_HEAD, BATCH_HEAD_RPW, BATCH_HEAD_BT, H16>(ah, s);
+  } else {
+    launch_proj_ln<MODE_HEAD, RPW, BT768, H16>(a, s);
+  }
 }
 
 hipError_t launch_step_f32(const Weights& w, const Work& k, const Sessions& ss, float* caches,
