@@ -503,8 +503,8 @@ __device__ __forceinline__ int quad_acc(const i4 wc, const i4 xc) {
 struct FusedSmem {
   float xs[D];          // block input x (all-gather), x12 for the head
   float x1s[D];         // x1 (all-gather; a buffer of its own: waves 1..7 may still read xs)
-  float xn[D];          // int8 path: LayerNorm output
-  float lntmp[D];       // int8 path: LayerNorm scratch
+  float xn[D];          // LayerNorm output (fp32: of x; int8: of x or x1)
+  float lntmp[D];       // fp32: LayerNorm output of x1; int8: LayerNorm scratch
   float att[DH];        // attention output of a head unit
   float xg[GS];         // the XCD's GELU slice
   float rs[NG_PR * RSN];  // reduce-scatter terms
@@ -679,9 +679,11 @@ __device__ __forceinline__ void head_rows(const FusedArgs a, FusedSmem& S, WRegs
 }
 
 // ---- regular units -------------------------------------------------------------
-// Wave 0 receives (reduce-scatters, all-gathers, the int8 LayerNorm) and holds no
-// weights; waves 1..7 compute from registers (and the fp32 MLP weights from LDS).
-// The two roles meet at the same sequence of workgroup barriers.
+// Wave 0 receives (reduce-scatters, all-gathers) and holds no weights; it also
+// takes the block's two LayerNorms once for the workgroup (fp32: layernorm_lds into
+// xn and lntmp; int8: with the whole workgroup, layernorm_seq_wg).  Waves 1..7
+// compute from registers (and the fp32 MLP weights from LDS).  The two roles meet
+// at the same sequence of workgroup barriers.
 template <bool Q8, bool CAP, bool TOKP, bool H16>
 __device__ __forceinline__ void regular_io(const FusedArgs& a, FusedSmem& S, const Ctx& c) {
   const int lane = lane_id();
@@ -715,6 +717,8 @@ __device__ __forceinline__ void regular_io(const FusedArgs& a, FusedSmem& S, con
     if constexpr (Q8) {
       wg_barrier();  // the block input is in LDS
       layernorm_seq_wg<1>(S.xs, S.lnp[0], S.lnp[1], S.xn, S.lntmp, seq_tab(S), S.xc, S.xsc);
+    } else {
+      layernorm_lds(S.xs, S.lnp[0], S.lnp[1], S.xn);  // once for the workgroup
     }
     wg_barrier();  // B1: QKV (int8: its input codes are in LDS)
     if constexpr (Q8) {
@@ -727,6 +731,8 @@ __device__ __forceinline__ void regular_io(const FusedArgs& a, FusedSmem& S, con
     if constexpr (Q8) {
       wg_barrier();  // x1 is in LDS
       layernorm_seq_wg<1>(S.x1s, S.lnp[2], S.lnp[3], S.xn, S.lntmp, seq_tab(S), S.xc, S.xsc);
+    } else {
+      layernorm_lds(S.x1s, S.lnp[2], S.lnp[3], S.lntmp);
     }
     wg_barrier();  // B3: FC (int8: its input codes are in LDS)
     if constexpr (Q8) {
@@ -789,10 +795,7 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
     if (wave == 1) dstamp(a.trace, l, 59);
     {
       f4 x[3];
-      if constexpr (!Q8) {
-        load_frag<3>(x, S.xs);
-        layernorm_frag(x, S.lnp[0], S.lnp[1]);
-      }
+      if constexpr (!Q8) load_frag<3>(x, S.xn);
       if (wave == 1) dstamp(a.trace, l, 60);
 #pragma unroll
       for (int k = 0; k < UPW; ++k) {
@@ -823,10 +826,7 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
     wg_barrier();  // B3: FC
     {
       f4 x[3];
-      if constexpr (!Q8) {
-        load_frag<3>(x, S.x1s);
-        layernorm_frag(x, S.lnp[2], S.lnp[3]);
-      }
+      if constexpr (!Q8) load_frag<3>(x, S.lntmp);
 #pragma unroll
       for (int k = 0; k < UPW; ++k) {
         const int n = U.cw + U.cwn * k;
