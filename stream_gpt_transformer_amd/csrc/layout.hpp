@@ -111,8 +111,8 @@ constexpr int FX_LOC_PER_LAYER = 384 + 128 + D + 384 + D;
 constexpr int FX_GLB_PER_LAYER = (H + F / 64) * D;
 constexpr size_t FX_WORDS = (size_t)FX_NXCC * L * FX_LOC_PER_LAYER + (size_t)L * FX_GLB_PER_LAYER + 256 + 256 * 8 * 16;
 // Split-K partial sums of one prefill projection: at most S x 128 rows x N with
-// S*N <= 12 * 768 (QKV 4 x 2304, FC 3 x 3072, O and PR 12 x 768).
-constexpr size_t PF_PART_WORDS = (size_t)8 * PMAX * D;
+// S*N <= 12 * 768 (QKV 3 x 2304, O and MLP projection 8 x 768).
+constexpr size_t PF_PART_WORDS = (size_t)12 * PMAX * D;
 
 inline WsLayout ws_layout(int max_batch) {
   WsLayout w{};

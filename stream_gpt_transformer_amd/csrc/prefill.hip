@@ -2,15 +2,15 @@
 // as row batches through the 12 blocks; only the final row reaches the tied head.
 //
 // The block projections are dense T x K by K x N contractions on the fp32 matrix
-// cores (v_mfma_f32_32x32x2_f32).  With T <= 128 rows every projection is short
-// and wide: a workgroup owns all rows and 16, 32 or 64 output columns, stages both
-// operands through LDS, and launches about 150-200 workgroups, one per compute
-// unit.  The wide projections (QKV, FC) run over all of K in 16-column tiles with
-// the bias (and GELU) in the epilogue; the 768-output ones (O, MLP projection)
-// split K, and their partial sums are added in a fixed order by the kernel that
-// applies the residual and the LayerNorm that follows it, so results do not
-// depend on timing.  Causal attention stages each head's key/value rows in LDS once per
-// eight query rows.
+// cores (v_mfma_f32_32x32x2_f32 and _16x16x4_f32).  With T <= 128 rows every
+// projection is short and wide: a workgroup owns all rows and 16 or 32 output
+// columns, stages both operands through LDS, and the launches have 192-216
+// workgroups, about one per compute unit.  FC runs over all of K in 16-column tiles
+// with the bias and GELU in its epilogue.  QKV, O and the MLP projection split K;
+// their partial sums are added in split order by the kernel that consumes them
+// (attention for QKV, which also adds the bias; the residual-and-LayerNorm kernel
+// for the other two), so results do not depend on timing.  Causal attention stages
+// each head's key/value rows in LDS once per eight query rows.
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -20,112 +20,97 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 enum Epi { EPI_STORE = 0, EPI_PART = 1 };
 
-// Tile geometry of k_gemm.  A workgroup owns all GM = 128 rows of the row batch
-// and NT output columns (NT = 64: eight waves, NT = 32: four), over one slice of
-// K.  The slice is streamed in stages of GK = 32 elements: the 128 activation
-// rows and NT weight rows of a stage (128 bytes each) are loaded with coalesced
-// 16-byte reads (eight consecutive threads read one row), held in registers PF
-// stages ahead, and written to one of two LDS buffers.  Chunk c (16 bytes) of
-// staged row r sits at LDS slot c ^ (r % 8) of that row, so that the eight lanes
-// of an MFMA operand read, which take the same chunk of eight consecutive rows,
-// hit distinct banks.
+// C = A[M][K] * W[N][K]^T over the K range [z*klen, (z+1)*klen) (z = blockIdx.y) for
+// the workgroup's 32 output columns n0 = 32*blockIdx.x.  Four waves; wave w computes
+// rows 32w..32w+31 with v_mfma_f32_32x32x2_f32: lane l supplies A[l%32][k] and
+// B[k][l%32] for k = l/32, and result register r of lane l is
+// C[8(r/4) + 4(l/32) + r%4][l%32].
+// K is streamed in stages of GK = 32 elements.  A stage (the GM = 128 activation rows
+// and the 32 weight rows, 128 bytes each: 20 KB) is copied from memory straight into
+// one of NBUF LDS buffers by 16-byte direct-to-LDS loads, NBUF-1 stages ahead of the
+// one being multiplied, so no registers and no LDS store instructions carry the
+// operands.  A 1 KB region of a buffer holds eight rows, chunk c of row r at slot
+// c ^ (r % 8), so that the eight lanes of an MFMA operand read, which take the same
+// chunk of eight consecutive rows, hit distinct banks.  Each wave copies five of the
+// 20 regions; it waits until its own copies of a stage have landed, and a workgroup
+// barrier then makes the whole stage visible (and frees the buffer of the stage
+// before, which the copies of stage t+NBUF-1 overwrite).
+// Within a stage, lane half h = l/32 reads chunk 2q + h (q < 4) of its operand rows,
+// and sub-step s of that chunk feeds element 8q + 4h + s, so the 32 elements are
+// consumed once each; even and odd q accumulate into separate registers, added at the
+// end.  Rows at or past M read row M-1 and store nothing.  Past the last stage the
+// copies re-read it into a buffer no later stage uses, so every wave issues the same
+// copies and the wait counts stay exact.
+// EPI_STORE: C = acc + bias (bias may be null); EPI_PART: part[z][row][col] = acc.
 constexpr int GK = 32;
 constexpr int GM = 128;
-template <int NT>
-struct GemmCfg {
-  static constexpr int NW = 4 * NT / 32;        // waves: row quarter x column half
-  static constexpr int NTH = 64 * NW;
-  static constexpr int ROWS = GM + NT;          // staged rows per stage
-  static constexpr int U = ROWS * 8 / NTH;      // 16-byte chunks per thread per stage
-  static constexpr int UA = GM * 8 / NTH;       // of which activation chunks (u < UA)
-  static constexpr int BUF = ROWS * GK * 4;     // bytes of one LDS buffer
-  static_assert(U * NTH == ROWS * 8, "whole chunks per thread");
-};
-
-// C = A[M][K] * W[N][K]^T over the K range [z*klen, (z+1)*klen) (z = blockIdx.y).
-// Wave w computes rows 32(w%4)..+31 and columns n0 + 32(w/4)..+31 with
-// v_mfma_f32_32x32x2_f32: lane l supplies A[l%32][k] and B[k][l%32] for
-// k = l/32, and result register r of lane l is C[8(r/4) + 4(l/32) + r%4][l%32].
-// Within a stage, lane half h = l/32 reads chunk 2q + h (q < 4) of its operand
-// rows, and sub-step s of that chunk feeds element 8q + 4h + s, so the 32
-// elements of a stage are consumed once each; even and odd q accumulate into
-// separate registers, added at the end.  Rows at or past M read row M-1 and store
-// nothing.  Every loop pass issues the same loads (past the last stage they
-// re-read it), so the compiler's wait counts stay exact.
-// EPI_STORE: C = acc + bias (bias may be null); EPI_PART: part[z][row][col] = acc.
-template <int NT, int EPI, int PF>
-__global__ __launch_bounds__(GemmCfg<NT>::NTH) void k_gemm(const float* __restrict__ A, int lda,
-                                                          const float* __restrict__ W, int ldw, int M,
-                                                          const float* __restrict__ bias, float* __restrict__ C,
-                                                          int ldc, int klen) {
-  using G = GemmCfg<NT>;
-  static_assert(PF % 2 == 0, "the LDS buffer of a stage follows from the unrolled pass");
-  __shared__ __align__(16) char lds[2 * G::BUF];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n0 = NT * blockIdx.x, kbeg = blockIdx.y * klen;
+constexpr int MM_NBUF = 4;                              // stage buffers in LDS
+constexpr int MM_ROWS = GM + 32;                        // staged rows per stage
+constexpr int MM_BUF = MM_ROWS * GK * 4;                // bytes of one stage buffer
+constexpr int MM_PERW = MM_ROWS / 8 / 4;                // 1 KB regions copied per wave per stage
+constexpr int MM_LDS = MM_NBUF * MM_BUF;
+static_assert(MM_PERW * 4 * 8 == MM_ROWS, "whole regions per wave");
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm(const float* __restrict__ A, int lda, const float* __restrict__ W,
+                                              int ldw, int M, const float* __restrict__ bias, float* __restrict__ C,
+                                              int ldc, int klen) {
+  extern __shared__ __align__(16) char lds[];
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n0 = 32 * blockIdx.x, kbeg = blockIdx.y * klen;
   const int nsteps = klen / GK;
-  const float* src[G::U];
-  int dst[G::U];
+  const float* src[MM_PERW];
 #pragma unroll
-  for (int u = 0; u < G::U; ++u) {
-    const int idx = (int)threadIdx.x + G::NTH * u, rr = idx >> 3, c = idx & 7;
-    src[u] = (u < G::UA ? A + (size_t)min(rr, M - 1) * lda : W + (size_t)(n0 + rr - GM) * ldw) + kbeg + 4 * c;
-    dst[u] = rr * (GK * 4) + 16 * (c ^ (rr & 7));
+  for (int i = 0; i < MM_PERW; ++i) {
+    const int row = 8 * (wave + 4 * i) + lane / 8, c = (lane % 8) ^ (lane / 8);
+    src[i] = (row < GM ? A + (size_t)min(row, M - 1) * lda : W + (size_t)(n0 + row - GM) * ldw) + kbeg + 4 * c;
   }
-  f4 pre[PF][G::U];
-  auto gload = [&](int slot, int t) {
+  auto copy_stage = [&](int t) {
     const int o = GK * min(t, nsteps - 1);
+    char* buf = lds + (t % MM_NBUF) * MM_BUF;
 #pragma unroll
-    for (int u = 0; u < G::U; ++u)  // weights are read once: no cache residency
-      pre[slot][u] = u < G::UA ? *(const f4*)(src[u] + o) : __builtin_nontemporal_load((const f4*)(src[u] + o));
+    for (int i = 0; i < MM_PERW; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src[i] + o),
+                                       (__attribute__((address_space(3))) void*)(buf + 1024 * (wave + 4 * i)), 16, 0, 0);
   };
-  auto lstore = [&](int slot, int buf) {
-#pragma unroll
-    for (int u = 0; u < G::U; ++u) *(f4*)(lds + buf * G::BUF + dst[u]) = pre[slot][u];
-  };
-  const int wr = wave & 3, wc = wave >> 2, h = lane >> 5, sw = lane & 7;
-  const int aoff = (32 * wr + (lane & 31)) * (GK * 4), boff = (GM + 32 * wc + (lane & 31)) * (GK * 4);
+  const int h = lane >> 5, sw = lane & 7;
+  const int aoff = (32 * wave + (lane & 31)) * (GK * 4), boff = (GM + (lane & 31)) * (GK * 4);
   f32x16 acc[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[j][e] = 0.0f;
-
 #pragma unroll
-  for (int p = 0; p < PF; ++p) gload(p, p);
-  lstore(0, 0);
-  gload(0, PF);
-  __syncthreads();
-  for (int t0 = 0; t0 < nsteps; t0 += PF) {
+  for (int p = 0; p < MM_NBUF - 1; ++p) copy_stage(p);
+  // s_waitcnt with vmcnt = (NBUF-2) copies-per-stage still in flight, expcnt and
+  // lgkmcnt left at their maxima
+  constexpr int WAITN = (MM_NBUF - 2) * MM_PERW;
+  constexpr int WAIT_STAGE = (WAITN & 15) | ((WAITN >> 4) << 14) | 0x70 | 0xF00;
+  for (int t = 0; t < nsteps; ++t) {
+    __builtin_amdgcn_s_waitcnt(WAIT_STAGE);  // this wave's copies of stage t have landed
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();            // and every wave's; stage t-1's buffer is free
+    asm volatile("" ::: "memory");
+    const char* b = lds + (t % MM_NBUF) * MM_BUF;
+    f4 fa[4], fb[4];
 #pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      if (t0 + p < nsteps) {
-        const char* b = lds + (p & 1) * G::BUF;
-        f4 fa[4], fb[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int slot = 16 * ((2 * q + h) ^ sw);
-          fa[q] = *(const f4*)(b + aoff + slot);
-          fb[q] = *(const f4*)(b + boff + slot);
-        }
-        __builtin_amdgcn_sched_barrier(0);  // all reads of the stage in flight before the first product
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            acc[q & 1] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[q][s], fb[q][s], acc[q & 1], 0, 0, 0);
-      }
-      const int nx = (p + 1) % PF;
-      lstore(nx, (p + 1) & 1);
-      gload(nx, t0 + p + 1 + PF);
-      __syncthreads();
+    for (int q = 0; q < 4; ++q) {
+      const int slot = 16 * ((2 * q + h) ^ sw);
+      fa[q] = *(const f4*)(b + aoff + slot);
+      fb[q] = *(const f4*)(b + boff + slot);
     }
+    copy_stage(t + MM_NBUF - 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc[q & 1] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[q][s], fb[q][s], acc[q & 1], 0, 0, 0);
   }
-  const int col = n0 + 32 * wc + (lane & 31);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // no copy in flight when the workgroup ends
+  const int col = n0 + (lane & 31);
   const float bv = (EPI == EPI_STORE && bias) ? bias[col] : 0.0f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int row = 32 * wr + 8 * (r >> 2) + 4 * h + (r & 3);
+    const int row = 32 * wave + 8 * (r >> 2) + 4 * h + (r & 3);
     if (row >= M) continue;
     const float v = acc[0][r] + acc[1][r];
     if constexpr (EPI == EPI_PART)
@@ -135,7 +120,7 @@ __global__ __launch_bounds__(GemmCfg<NT>::NTH) void k_gemm(const float* __restri
   }
 }
 
-// Narrow full-K variant for the wide projections (QKV, FC): a workgroup owns all
+// Narrow full-K variant for the MLP's first projection (FC): a workgroup owns all
 // 128 rows and 16 output columns over the whole of K, so no split partial sums
 // and no reduction launch are needed; the epilogue adds the bias (and applies
 // GELU).  Eight waves, wave w computing rows 16w..16w+15 with
@@ -156,13 +141,10 @@ struct G16 {
   static constexpr int UA = GM * CH / G16_NTH, U = UA + 1, NB = 16 * CH;
   static_assert(UA * G16_NTH == GM * CH && NB <= G16_NTH, "whole chunks per thread");
 };
-// kv (QKV projection handing the session to the cached step, or null): outputs
-// col >= 768 (keys, then values) of row t also go to kv[t * 12 * 1536 + col - 768],
-// the cachedStep layout of position t for the layer kv points at.
 template <int KS, bool GELU, int PF>
 __global__ __launch_bounds__(G16_NTH) void k_gemm16(const float* __restrict__ A, int lda, const float* __restrict__ W,
                                                    int ldw, int M, int K, const float* __restrict__ bias,
-                                                   float* __restrict__ C, int ldc, float* __restrict__ kv) {
+                                                   float* __restrict__ C, int ldc) {
   using G = G16<KS>;
   static_assert(PF % 2 == 0, "the LDS buffer of a stage follows from the unrolled pass");
   extern __shared__ __align__(16) char lds[];
@@ -242,7 +224,6 @@ __global__ __launch_bounds__(G16_NTH) void k_gemm16(const float* __restrict__ A,
     float y = (acc[0][r] + acc[1][r]) + bv;
     if (GELU) y = gelu_tanh(y);
     C[(size_t)row * ldc + col] = y;
-    if (kv && col >= D) kv[(size_t)row * CACHE_POS + col - D] = y;
   }
 }
 
@@ -250,7 +231,7 @@ __global__ __launch_bounds__(G16_NTH) void k_gemm16(const float* __restrict__ A,
 constexpr int G16_KS = 32;
 template <bool GELU>
 static hipError_t gemm16(const float* A, int lda, const float* W, int M, int N, int K, const float* bias, float* C,
-                         int ldc, hipStream_t s, float* kv = nullptr) {
+                         int ldc, hipStream_t s) {
   constexpr size_t lds = 2 * (size_t)G16<G16_KS>::BUF;
   static bool attr = false;
   if (!attr) {
@@ -259,8 +240,7 @@ static hipError_t gemm16(const float* A, int lda, const float* W, int M, int N, 
     if (e) return e;
     attr = true;
   }
-  hipLaunchKernelGGL((k_gemm16<G16_KS, GELU, 2>), dim3(N / 16), dim3(G16_NTH), lds, s, A, lda, W, K, M, K, bias, C, ldc,
-                     kv);
+  hipLaunchKernelGGL((k_gemm16<G16_KS, GELU, 2>), dim3(N / 16), dim3(G16_NTH), lds, s, A, lda, W, K, M, K, bias, C, ldc);
   return hipGetLastError();
 }
 
@@ -321,34 +301,49 @@ struct PfAttnSmem {
   float part[PF_ROWS][PF_ROWS][DH];  // per-wave partial weighted sums [wave][row][d]
 };
 
-// Causal attention of head blockIdx.x for query rows t0..t0+7 (t0 = 8*blockIdx.y)
-// over the row-batch QKV buffer [n][3D].  The key/value rows 0..t0+7 and the eight
-// query rows are staged in LDS once; wave w then takes row t = t0 + w: lane j
+// Causal attention of head blockIdx.x for query rows t0..t0+7 (t0 = 8*blockIdx.y).
+// The QKV projection arrives as SP split-K partial sums part[z][t][3D] (z < SP); a
+// staged value is ((part[0] + part[1]) + ...) + bias.  The key/value rows 0..t0+7
+// and the eight query rows are staged in LDS once; kv (or null) also receives the
+// keys and values of rows t0..t0+7, at kv[t * 12 * 1536 + col - 768] for projection
+// column col >= 768, the cachedStep layout of position t for the layer kv points at
+// (the prefill's handoff to the cached step).  Wave w then takes row t = t0 + w: lane j
 // scores keys j and j+64 (four interleaved partial dot products), and the softmax
 // maximum and sum are wave reductions.  The weighted sums are split over the keys:
 // wave w sums keys 16w..16w+15 for all eight rows and 64 outputs (lane l: row l/8,
 // outputs 8(l%8)..+7), and the eight partial sums are added in wave order.
-__global__ __launch_bounds__(PF_ATT_THREADS) void k_pf_attn(const float* __restrict__ qkv, int n,
-                                                            float* __restrict__ att) {
+template <int SP>
+__global__ __launch_bounds__(PF_ATT_THREADS) void k_pf_attn(const float* __restrict__ part, const float* __restrict__ bias,
+                                                            int n, float* __restrict__ att, float* __restrict__ kv) {
   __shared__ __align__(16) PfAttnSmem sm;
   const int h = blockIdx.x, t0 = PF_ROWS * blockIdx.y;
   const int tend = min(t0 + PF_ROWS, n);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  // Stage rows 0..tend-1: 16 threads per row, each 16 keys and 16 values, and the
+  const size_t pstride = (size_t)n * D3;
+  auto sum_parts = [&](const float* p) {
+    f4 v = *(const f4*)p;
+#pragma unroll
+    for (int z = 1; z < SP; ++z) v = v + *(const f4*)(p + z * pstride);
+    return v;
+  };
+  // Stage rows 0..tend-1: 16 threads per row, each four keys and four values, and the
   // query rows (indexes past the last row re-read it; all loads before any store).
   {
     constexpr int U = PMAX * 16 / PF_ATT_THREADS;
     f4 kk[U], vv[U], qq;
+    const int qr = threadIdx.x >> 4, qc = (threadIdx.x & 15) * 4;  // 128 threads: 8 rows x 16 float4
+    const f4 bk = *(const f4*)(bias + D + h * DH + (threadIdx.x & 15) * 4);
+    const f4 bvv = *(const f4*)(bias + 2 * D + h * DH + (threadIdx.x & 15) * 4);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int idx = threadIdx.x + PF_ATT_THREADS * u;
       const int j = min(idx >> 4, tend - 1), c = (idx & 15) * 4;
-      const float* row = qkv + (size_t)j * D3 + h * DH;
-      kk[u] = *(const f4*)(row + D + c);
-      vv[u] = *(const f4*)(row + 2 * D + c);
+      const float* row = part + (size_t)j * D3 + h * DH + c;
+      kk[u] = sum_parts(row + D) + bk;
+      vv[u] = sum_parts(row + 2 * D) + bvv;
     }
-    const int qr = threadIdx.x >> 4, qc = (threadIdx.x & 15) * 4;  // 128 threads: 8 rows x 16 float4
-    if (threadIdx.x < PF_ROWS * 16) qq = *(const f4*)(qkv + (size_t)min(t0 + qr, tend - 1) * D3 + h * DH + qc);
+    if (threadIdx.x < PF_ROWS * 16)
+      qq = sum_parts(part + (size_t)min(t0 + qr, tend - 1) * D3 + h * DH + qc) + *(const f4*)(bias + h * DH + qc);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int idx = threadIdx.x + PF_ATT_THREADS * u;
@@ -356,6 +351,10 @@ __global__ __launch_bounds__(PF_ATT_THREADS) void k_pf_attn(const float* __restr
       if (j < tend) {
         *(f4*)&sm.k[j][c] = kk[u];
         *(f4*)&sm.v[j][c] = vv[u];
+        if (kv && j >= t0) {
+          *(f4*)(kv + (size_t)j * CACHE_POS + h * DH + c) = kk[u];
+          *(f4*)(kv + (size_t)j * CACHE_POS + D + h * DH + c) = vv[u];
+        }
       }
     }
     if (threadIdx.x < PF_ROWS * 16) *(f4*)&sm.q[qr][qc] = qq;
@@ -434,25 +433,34 @@ __global__ __launch_bounds__(PF_ATT_THREADS) void k_pf_attn(const float* __restr
 
 hipError_t launch_head_f32(const Weights& w, const float* x_row, float* logits, hipStream_t s);
 
-// Split-K factors: the K range of every projection is cut into S equal runs of
-// whole GK-element stages; N/NT column tiles x S workgroups per launch.
-constexpr int S_O = 8, S_PR = 8;
-static_assert((size_t)S_O * D * PMAX <= PF_PART_WORDS && (size_t)S_PR * D * PMAX <= PF_PART_WORDS,
+// Split-K factors: the K range of a projection is cut into S equal runs of whole
+// GK-element stages; N/32 column tiles x S workgroups per launch (QKV: 216, O and
+// MLP projection: 192).  The partial sums are added in split order by the kernel
+// that consumes them (attention for QKV, the residual-and-LayerNorm kernel for O
+// and the MLP projection).
+#ifndef PF_S_QKV
+#define PF_S_QKV 3
+#endif
+constexpr int S_QKV = PF_S_QKV, S_O = 8, S_PR = 8;
+static_assert((size_t)S_QKV * D3 * PMAX <= PF_PART_WORDS && (size_t)S_O * D * PMAX <= PF_PART_WORDS &&
+                  (size_t)S_PR * D * PMAX <= PF_PART_WORDS,
               "partial-sum buffer");
-static_assert(D % (GK * S_O) == 0 && F % (GK * S_PR) == 0, "split K ranges are whole stages");
-static_assert(D3 % 16 == 0 && F % 16 == 0 && D % G16_KS == 0, "k_gemm16 tiles");
+static_assert(D % (GK * S_QKV) == 0 && D % (GK * S_O) == 0 && F % (GK * S_PR) == 0, "split K ranges are whole stages");
+static_assert(D3 % 32 == 0 && D % 32 == 0, "k_gemm column tiles");
+static_assert(F % 16 == 0 && D % G16_KS == 0, "k_gemm16 tiles");
 
-// NT = 64 where N allows it, else 32 (N must be a multiple of 32, K of GK * split).
+// N must be a multiple of 32, K of GK * split, 1 <= M <= GM.
 template <int EPI>
-static void mm(const float* A, int lda, const float* W, int K, int M, int N, const float* bias, float* C, int ldc,
-               int split, bool wide, hipStream_t s) {
-  const int klen = K / split;
-  if (wide)
-    hipLaunchKernelGGL((k_gemm<64, EPI, 2>), dim3(N / 64, split), dim3(GemmCfg<64>::NTH), 0, s, A, lda, W, K, M,
-                       bias, C, ldc, klen);
-  else
-    hipLaunchKernelGGL((k_gemm<32, EPI, 2>), dim3(N / 32, split), dim3(GemmCfg<32>::NTH), 0, s, A, lda, W, K, M,
-                       bias, C, ldc, klen);
+static hipError_t mm(const float* A, int lda, const float* W, int K, int M, int N, const float* bias, float* C, int ldc,
+                     int split, hipStream_t s) {
+  static bool attr = false;
+  if (!attr) {
+    const hipError_t e = hipFuncSetAttribute((const void*)k_gemm<EPI>, hipFuncAttributeMaxDynamicSharedMemorySize, MM_LDS);
+    if (e) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL((k_gemm<EPI>), dim3(N / 32, split), dim3(256), MM_LDS, s, A, lda, W, K, M, bias, C, ldc, K / split);
+  return hipGetLastError();
 }
 
 hipError_t launch_infer(const Weights& w, const Work& k, const uint32_t* toks, int n, float* logits,
@@ -463,15 +471,14 @@ hipError_t launch_infer(const Weights& w, const Work& k, const uint32_t* toks, i
   hipLaunchKernelGGL(k_pf_embed_ln, dim3(n), dim3(64), 0, s, w, tk, k.pf_x, small_p(w, 0, sp::LN1_G),
                      small_p(w, 0, sp::LN1_B), k.pf_h);
   for (int l = 0; l < L; ++l) {
-    if ((e = gemm16<false>(k.pf_h, D, f32_mat(w, l, M_QKV), n, D3, D, small_p(w, l, sp::B_QKV), k.pf_qkv, D3, s,
-                           cache ? cache + (size_t)l * KV_ROW : nullptr)))
-      return e;
-    hipLaunchKernelGGL(k_pf_attn, dim3(H, (n + PF_ROWS - 1) / PF_ROWS), dim3(PF_ATT_THREADS), 0, s, k.pf_qkv, n, k.pf_att);
-    mm<EPI_PART>(k.pf_att, D, f32_mat(w, l, M_O), D, n, D, nullptr, k.pf_part, D, S_O, false, s);
+    if ((e = mm<EPI_PART>(k.pf_h, D, f32_mat(w, l, M_QKV), D, n, D3, nullptr, k.pf_part, D3, S_QKV, s))) return e;
+    hipLaunchKernelGGL(k_pf_attn<S_QKV>, dim3(H, (n + PF_ROWS - 1) / PF_ROWS), dim3(PF_ATT_THREADS), 0, s, k.pf_part,
+                       small_p(w, l, sp::B_QKV), n, k.pf_att, cache ? cache + (size_t)l * KV_ROW : nullptr);
+    if ((e = mm<EPI_PART>(k.pf_att, D, f32_mat(w, l, M_O), D, n, D, nullptr, k.pf_part, D, S_O, s))) return e;
     hipLaunchKernelGGL(k_pf_resid_ln<S_O>, dim3(n), dim3(64), 0, s, k.pf_part, n, small_p(w, l, sp::B_O), k.pf_x,
                        small_p(w, l, sp::LN2_G), small_p(w, l, sp::LN2_B), k.pf_h);
     if ((e = gemm16<true>(k.pf_h, D, f32_mat(w, l, M_FC), n, F, D, small_p(w, l, sp::B_FC), k.pf_u, F, s))) return e;
-    mm<EPI_PART>(k.pf_u, F, f32_mat(w, l, M_PR), F, n, D, nullptr, k.pf_part, D, S_PR, false, s);
+    if ((e = mm<EPI_PART>(k.pf_u, F, f32_mat(w, l, M_PR), F, n, D, nullptr, k.pf_part, D, S_PR, s))) return e;
     const bool last = l + 1 == L;
     hipLaunchKernelGGL(k_pf_resid_ln<S_PR>, dim3(n), dim3(64), 0, s, k.pf_part, n, small_p(w, l, sp::B_PR), k.pf_x,
                        last ? nullptr : small_p(w, l + 1, sp::LN1_G), last ? nullptr : small_p(w, l + 1, sp::LN1_B),
@@ -487,8 +494,7 @@ hipError_t launch_gemm16_test(const float* A, const float* W, const float* bias,
 }
 
 hipError_t launch_gemm_test(const float* A, const float* W, float* C, int M, int N, int K, hipStream_t s) {
-  mm<EPI_STORE>(A, K, W, K, M, N, nullptr, C, N, 1, N % 64 == 0, s);
-  return hipGetLastError();
+  return mm<EPI_STORE>(A, K, W, K, M, N, nullptr, C, N, 1, s);
 }
 
 }  // namespace g2
