@@ -276,12 +276,12 @@ int gpt2_test_layernorm_seq(const float* x_dev, int rows, const float* gamma_dev
  * x >= 88.72283935546875 gives +inf.  tanh(z) = 1 - 2/(exp(2|z|) + 1) with the sign of z. */
 int gpt2_test_special(int kind, uint32_t first_bits, size_t n, float* y, void* stream);
 
-/* C[M][N] = A[M][K] * W[N][K]^T with the prefill matrix-core kernel
- * (M 1..128, N a multiple of 32, K a multiple of 32). */
+/* C[M][N] = A[M][K] * W[N][K]^T with the prefill's split-K matrix-core kernel run
+ * over all of K in one split (M 1..128, N a multiple of 32, K a multiple of 32). */
 int gpt2_test_gemm(const float* A_dev, const float* W_dev, float* C_dev, int M, int N, int K, void* stream);
 
 /* C[M][N] = A[M][K] * W[N][K]^T + bias[N], then tanh-GELU when gelu is 1, with the
- * prefill's full-K kernel for the wide projections (M 1..128, N a multiple of 16,
+ * prefill's full-K kernel of the MLP's first projection (M 1..128, N a multiple of 16,
  * K a multiple of 32; gelu 0 or 1). */
 int gpt2_test_gemm_bias(const float* A_dev, const float* W_dev, const float* bias_dev, float* C_dev, int M, int N,
                         int K, int gelu, void* stream);

@@ -123,7 +123,7 @@ def test_prefill_gemm_matches_float64(M, N, K):
 @pytest.mark.parametrize("M,N,K,gelu", [(128, 2304, 768, 0), (128, 3072, 768, 1), (77, 2304, 768, 0), (1, 16, 64, 1),
                                         (33, 48, 128, 0)])
 def test_prefill_full_k_gemm_bias_gelu(M, N, K, gelu):
-    """The wide projections' kernel (all of K in 16-column tiles, bias and GELU in
+    """The FC projection's kernel (all of K in 16-column tiles, bias and GELU in
     the epilogue) against float64 products; with GELU, against the oracle's GELU of
     the float64 result, within the GELU's slope times the product bound plus a few
     ulps of its own rounding."""
