@@ -199,10 +199,11 @@ __global__ __launch_bounds__(128) void k_attn(const ProjArgs a) {
 }
 
 // ---- int8 group-64 projections (batch 1) -------------------------------------
-// LayerNorm inputs use the sequential-order LayerNorm (layernorm_seq), and the
-// attention the sequential-order attn_compute_seq, as the fused int8 step does.
-// The block quantizes its fp32 input in LDS (every block does the same work and
-// gets the same codes), then each wave streams its rows' int8 codes: lane l takes
+// LayerNorm inputs use the sequential-order LayerNorm, taken by the whole
+// workgroup (layernorm_seq_wg, so those projections run eight waves a workgroup),
+// and the attention the sequential-order attn_compute_seq, as the fused int8 step
+// does.  The block quantizes its fp32 input in LDS (every block does the same work
+// and gets the same codes), then each wave streams its rows' int8 codes: lane l takes
 // 16 codes at byte 1024*i + 16*l, so group 16*i + l/4; v_dot4 gives a lane partial
 // and two exact integer butterfly steps give the group accumulator.  The rescale
 // runs in one fixed order: y = 0; y = y + ((float)acc_g * sw_g) * sx_g for
@@ -236,15 +237,26 @@ __device__ __forceinline__ float q8_dot_groups(const i4 (&wc)[(K + 1023) / 1024]
   return y;
 }
 
+// Waves of a k_q8proj workgroup: eight where the input is a LayerNorm output, so
+// that the whole workgroup takes the sequential sums (layernorm_seq_wg), else four.
+__host__ __device__ constexpr int q8_waves(int mode) {
+  return mode == MODE_QKV || mode == MODE_FC || mode == MODE_HEAD ? 8 : 4;
+}
+
 template <int MODE, int RPW>
-__global__ __launch_bounds__(256) void k_q8proj(const ProjArgs a) {
+__global__ __launch_bounds__(64 * q8_waves(MODE)) void k_q8proj(const ProjArgs a) {
   constexpr int K = MODE == MODE_PR ? F : D;
   constexpr int NI = K / 256;
   constexpr int G = K / 64;
   constexpr int NCH = (K + 1023) / 1024;
   constexpr int NROWS = mode_rows<MODE>();
+  constexpr int NW = q8_waves(MODE), NT = 64 * NW;
+  constexpr bool LN = mode_ln<MODE>();
+  static_assert(!LN || NW == 8, "layernorm_seq_wg takes 512 threads");
   __shared__ __align__(16) float xf[K];
-  __shared__ __align__(16) float lntmp[mode_ln<MODE>() ? D : 1];
+  __shared__ __align__(16) float xn[LN ? D : 1];       // LayerNorm output
+  __shared__ __align__(16) float lntmp[LN ? D : 1];
+  __shared__ __align__(16) float tab[LN ? SEQ_TAB_FLOATS : 1];
   __shared__ __align__(16) int8_t xc[K];
   __shared__ float xsc[G];
   __shared__ float xm[G];
@@ -259,36 +271,37 @@ __global__ __launch_bounds__(256) void k_q8proj(const ProjArgs a) {
     store_frag<NI>(xf, x);
   }
   __syncthreads();
-  if constexpr (mode_ln<MODE>()) {
-    if (wave == 0) layernorm_seq(xf, ln_gamma<MODE>(a), ln_beta<MODE>(a), xf, lntmp);
+  if constexpr (LN) {
+    layernorm_seq_wg<2>(xf, ln_gamma<MODE>(a), ln_beta<MODE>(a), xn, lntmp, tab);
     __syncthreads();
   }
+  const float* xq = LN ? xn : xf;  // the projection's input
   if (qx == 1) {
-    for (int g = wave; g < G; g += 4) {
+    for (int g = wave; g < G; g += NW) {
       float s;
-      const int c = quant_lane(xf[g * 64 + lane], s);
+      const int c = quant_lane(xq[g * 64 + lane], s);
       xc[g * 64 + lane] = (int8_t)c;
       if (lane == 0) xsc[g] = s;
     }
   } else {
-    for (int g = wave; g < G; g += 4) {
-      const float m = wave_max(fabsf(xf[g * 64 + lane]));
+    for (int g = wave; g < G; g += NW) {
+      const float m = wave_max(fabsf(xq[g * 64 + lane]));
       if (lane == 0) xm[g] = m;
     }
     __syncthreads();
-    for (int g = wave; g < G; g += 4) {
+    for (int g = wave; g < G; g += NW) {
       const int g0 = g - g % qx;
       float m = 0.0f;
       for (int t = 0; t < qx; ++t) m = fmaxf(m, xm[g0 + t]);
       const float sc = m == 0.0f ? 0.0f : m / 127.0f;
-      xc[g * 64 + lane] = m == 0.0f ? 0 : (int8_t)quant_code(xf[g * 64 + lane], sc);
+      xc[g * 64 + lane] = m == 0.0f ? 0 : (int8_t)quant_code(xq[g * 64 + lane], sc);
       if (lane == 0) xsc[g] = sc;
     }
   }
   __syncthreads();
   if (cap && blockIdx.x == 0) {
-    for (int i = threadIdx.x; i < K; i += 256) {
-      ((float*)(cap + cl.in))[i] = xf[i];
+    for (int i = threadIdx.x; i < K; i += NT) {
+      ((float*)(cap + cl.in))[i] = xq[i];
       ((int8_t*)(cap + cl.codes))[i] = xc[i];
     }
     if (threadIdx.x < G) ((float*)(cap + cl.xs))[threadIdx.x] = xsc[threadIdx.x];
@@ -296,7 +309,7 @@ __global__ __launch_bounds__(256) void k_q8proj(const ProjArgs a) {
 
   const int8_t* codes = q8_codes(a.w, a.layer, MODE);
   const float* scales = q8_scales(a.w, a.layer, MODE);
-  const int row0 = (blockIdx.x * 4 + wave) * RPW;
+  const int row0 = (blockIdx.x * NW + wave) * RPW;
 #pragma unroll
   for (int rr = 0; rr < RPW; ++rr) {
     const int r = row0 + rr;
@@ -503,8 +516,9 @@ hipError_t launch_step_f32(const Weights& w, const Work& k, const Sessions& ss, 
 template <int MODE, int RPW>
 static void launch_q8(const ProjArgs& a, hipStream_t s) {
   const int rows = MODE == MODE_QKV ? D3 : MODE == MODE_FC ? F : MODE == MODE_HEAD ? V : D;
-  const int nblk = (rows + 4 * RPW - 1) / (4 * RPW);
-  hipLaunchKernelGGL((k_q8proj<MODE, RPW>), dim3(nblk), dim3(256), 0, s, a);
+  constexpr int NW = q8_waves(MODE);
+  const int nblk = (rows + NW * RPW - 1) / (NW * RPW);
+  hipLaunchKernelGGL((k_q8proj<MODE, RPW>), dim3(nblk), dim3(64 * NW), 0, s, a);
 }
 
 hipError_t launch_step_q8(const Weights& w, const Work& k, const Sessions& ss, float* cache,

@@ -322,9 +322,8 @@ __device__ __forceinline__ float gelu_tanh(float u) {
 //   mean = (((0 + x_0) + x_1) + ... + x_767) / 768;  d_i = x_i - mean;
 //   var = (((0 + d_0*d_0) + d_1*d_1) + ...) / 768;  r = 1/sqrt(var + 1e-5);
 //   y_i = (d_i*r)*gamma_i + beta_i.
-// The chain of 768 dependent adds is the cost: the wave reads the next 32 values
-// from LDS (broadcast reads) while it adds the current 32, so the chain never
-// waits for LDS.
+// A chain of dependent adds is the cost: a wave reads the next 32 values from LDS
+// (broadcast reads) while it adds the current 32, so the chain never waits for LDS.
 __device__ __forceinline__ void lds_load32(f4 (&v)[8], const float* p) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = *(const f4*)(p + 4 * i);
@@ -338,52 +337,11 @@ __device__ __forceinline__ void seq_add32(float& s, const f4 (&v)[8]) {
     s = s + v[i].w;
   }
 }
-// s = 0 + t_0 + t_1 + ... + t_767 in order, t in LDS.
-__device__ __forceinline__ float seq_sum768(const float* t) {
-  f4 a[8], b[8];
-  lds_load32(a, t);
-  float s = 0.0f;
-#pragma unroll 1
-  for (int c = 0; c < 24; c += 2) {
-    lds_load32(b, t + 32 * (c + 1));
-    __builtin_amdgcn_sched_barrier(0);
-    seq_add32(s, a);
-    __builtin_amdgcn_sched_barrier(0);
-    lds_load32(a, t + 32 * min(c + 2, 23));
-    __builtin_amdgcn_sched_barrier(0);
-    seq_add32(s, b);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  return s;
-}
-// One wave: xs (LDS) -> ys (LDS, may be xs); tmp is 768 floats of LDS scratch.
-__device__ __forceinline__ void layernorm_seq(const float* xs, const float* __restrict__ gamma,
-                                              const float* __restrict__ beta, float* ys, float* tmp) {
-  const int lane = lane_id();
-  const float mean = seq_sum768(xs) / 768.0f;
-  f4 d[3];
-  load_frag<3>(d, xs);
-#pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    d[i] = d[i] - mean;
-    *(f4*)(tmp + 256 * i + 4 * lane) = d[i] * d[i];
-  }
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the squares are in LDS
-  __builtin_amdgcn_wave_barrier();
-  const float var = seq_sum768(tmp) / 768.0f;
-  const float r = 1.0f / sqrtf(var + 1e-5f);
-  f4 g[3], b[3];
-  load_frag<3>(g, gamma);
-  load_frag<3>(b, beta);
-#pragma unroll
-  for (int i = 0; i < 3; ++i) d[i] = (d[i] * r) * g[i] + b[i];
-  store_frag<3>(ys, d);
-}
-
 // ---- the same sequential sums, evaluated by a whole workgroup -----------------
 // seq_sum768_wg returns (((0 + t_0) + t_1) + ... + t_767), one binary32 rounding per
-// add, bit for bit the sequential loop's value for finite t, in about two thirds
-// of the loop's latency.  All 512 threads (8 waves) of the workgroup call it.
+// add, bit for bit the sequential loop's value for finite t, in about half the
+// latency of one wave running the loop.  All 512 threads (8 waves) of the
+// workgroup call it.
 //  1. Estimates: every wave forms the binary64 prefix sums of t (lane i sums
 //     t[12i..12i+11], then an inclusive scan over the lanes) and rounds the prefix
 //     at each segment start to binary32: E_k for segment k = t[96k..96k+95], k < 8.
@@ -522,8 +480,8 @@ __device__ __forceinline__ void quant_frag16(const f4 y, int8_t* xc, float* xsc,
   if ((T & 15) == 0) xsc[T >> 4] = s;
 }
 
-// The sequential LayerNorm of layernorm_seq by all 512 threads of a workgroup, with
-// both sums taken by seq_sum768_wg: the same output bits.  xs, ys (LDS, distinct),
+// The sequential-order LayerNorm defined above, by all 512 threads of a workgroup,
+// with both sums taken by seq_sum768_wg: the sequential loop's output bits.  xs, ys (LDS, distinct),
 // tmp (768 floats) and tab of LDS scratch.  ys is complete for the
 // workgroup after the caller's next barrier.  tab: SEQ_TAB_FLOATS floats.  WALK as
 // for seq_sum768_wg.  With xc given, the output is also quantized in groups of 64
