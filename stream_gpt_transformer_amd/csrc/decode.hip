@@ -265,15 +265,26 @@ __global__ __launch_bounds__(64 * q8_waves(MODE)) void k_q8proj(const ProjArgs a
   const CapLayout cl = cap_item(MODE);
   char* cap = a.capture ? a.capture + cap_offset(a.layer, MODE) : nullptr;
 
+  // The wave's weight rows are requested first, so their latency overlaps the input's
+  // load, LayerNorm and quantization; the workgroup barriers below order LDS only and
+  // leave these loads in flight.  Rows past the matrix re-read its last row.
+  const int8_t* codes = q8_codes(a.w, a.layer, MODE);
+  const float* scales = q8_scales(a.w, a.layer, MODE);
+  const int row0 = (blockIdx.x * NW + wave) * RPW;
+  i4 wc[RPW][NCH];
+  float swl[RPW];
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) q8_load_row<K>(wc[rr], swl[rr], codes, scales, min(row0 + rr, NROWS - 1));
+
   if (wave == 0) {
     f4 x[NI];
     load_frag<NI>(x, proj_src<MODE>(a, 0));
     store_frag<NI>(xf, x);
   }
-  __syncthreads();
+  lds_barrier();
   if constexpr (LN) {
     layernorm_seq_wg<2>(xf, ln_gamma<MODE>(a), ln_beta<MODE>(a), xn, lntmp, tab);
-    __syncthreads();
+    lds_barrier();
   }
   const float* xq = LN ? xn : xf;  // the projection's input
   if (qx == 1) {
@@ -288,7 +299,7 @@ __global__ __launch_bounds__(64 * q8_waves(MODE)) void k_q8proj(const ProjArgs a
       const float m = wave_max(fabsf(xq[g * 64 + lane]));
       if (lane == 0) xm[g] = m;
     }
-    __syncthreads();
+    lds_barrier();
     for (int g = wave; g < G; g += NW) {
       const int g0 = g - g % qx;
       float m = 0.0f;
@@ -298,7 +309,7 @@ __global__ __launch_bounds__(64 * q8_waves(MODE)) void k_q8proj(const ProjArgs a
       if (lane == 0) xsc[g] = sc;
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (cap && blockIdx.x == 0) {
     for (int i = threadIdx.x; i < K; i += NT) {
       ((float*)(cap + cl.in))[i] = xq[i];
@@ -307,18 +318,12 @@ __global__ __launch_bounds__(64 * q8_waves(MODE)) void k_q8proj(const ProjArgs a
     if (threadIdx.x < G) ((float*)(cap + cl.xs))[threadIdx.x] = xsc[threadIdx.x];
   }
 
-  const int8_t* codes = q8_codes(a.w, a.layer, MODE);
-  const float* scales = q8_scales(a.w, a.layer, MODE);
-  const int row0 = (blockIdx.x * NW + wave) * RPW;
 #pragma unroll
   for (int rr = 0; rr < RPW; ++rr) {
     const int r = row0 + rr;
     if (r >= NROWS) break;
-    i4 wc[NCH];
-    float swl;
-    q8_load_row<K>(wc, swl, codes, scales, r);
     int32_t* ca = cap ? (int32_t*)(cap + cl.acc) + (size_t)r * G : nullptr;
-    float y = qm == 1 ? q8_dot<K>(wc, swl, xc, xsc, ca) : q8_dot_groups<K>(wc, swl, xc, xsc, qm);
+    float y = qm == 1 ? q8_dot<K>(wc[rr], swl[rr], xc, xsc, ca) : q8_dot_groups<K>(wc[rr], swl[rr], xc, xsc, qm);
     y = y + proj_bias<MODE>(a, r);
     if (cap && lane == 0) ((float*)(cap + cl.y))[r] = y;
     if (lane == 0) proj_store<MODE>(a, 0, r, y);
