@@ -200,9 +200,8 @@ __global__ __launch_bounds__(128) void k_attn(const ProjArgs a) {
 
 // ---- int8 group-64 projections (batch 1) -------------------------------------
 // LayerNorm inputs use the sequential-order LayerNorm, taken by the whole
-// workgroup (layernorm_seq_wg, so those projections run eight waves a workgroup),
-// and the attention the sequential-order attn_compute_seq, as the fused int8 step
-// does.  The block quantizes its fp32 input in LDS (every block does the same work
+// eight-wave workgroup (layernorm_seq_wg), and the attention the sequential-order
+// attn_compute_seq, as the fused int8 step does.  The block quantizes its fp32 input in LDS (every block does the same work
 // and gets the same codes), then each wave streams its rows' int8 codes: lane l takes
 // 16 codes at byte 1024*i + 16*l, so group 16*i + l/4; v_dot4 gives a lane partial
 // and two exact integer butterfly steps give the group accumulator.  The rescale
@@ -237,11 +236,9 @@ __device__ __forceinline__ float q8_dot_groups(const i4 (&wc)[(K + 1023) / 1024]
   return y;
 }
 
-// Waves of a k_q8proj workgroup: eight where the input is a LayerNorm output, so
-// that the whole workgroup takes the sequential sums (layernorm_seq_wg), else four.
-__host__ __device__ constexpr int q8_waves(int mode) {
-  return mode == MODE_QKV || mode == MODE_FC || mode == MODE_HEAD ? 8 : 4;
-}
+// Waves of a k_q8proj workgroup: eight (where the input is a LayerNorm output, the
+// whole workgroup takes the sequential sums, layernorm_seq_wg).
+__host__ __device__ constexpr int q8_waves(int) { return 8; }
 
 template <int MODE, int RPW>
 __global__ __launch_bounds__(64 * q8_waves(MODE)) void k_q8proj(const ProjArgs a) {
@@ -544,9 +541,9 @@ hipError_t launch_step_q8(const Weights& w, const Work& k, const Sessions& ss, f
     a.layer = l;
     launch_q8<MODE_QKV, 2>(a, s);
     hipLaunchKernelGGL(k_attn<true>, dim3(H, 1), dim3(128), 0, s, a);
-    launch_q8<MODE_O, 2>(a, s);
+    launch_q8<MODE_O, 1>(a, s);
     launch_q8<MODE_FC, 2>(a, s);
-    launch_q8<MODE_PR, 2>(a, s);
+    launch_q8<MODE_PR, 1>(a, s);
   }
   launch_q8<MODE_HEAD, 4>(a, s);
   return hipGetLastError();
