@@ -546,22 +546,48 @@ struct AttnSmem {
 
 // Stage key/value rows j0..j1-1 of one head into LDS with threads tid0..tid0+nthr-1
 // of the block.  Row j of the keys is at kv(j) (64 keys), its values at kv(j) + D.
-template <class RowPtr>
+// UB > 1: a thread's loads of UB chunks are all in flight before their stores (a
+// pass past the last chunk re-reads it and does not store it), so a few threads
+// staging many rows pay one memory latency per UB chunks instead of one per chunk.
+template <int UB = 1, class RowPtr>
 __device__ __forceinline__ void attn_stage_rows(AttnSmem& sm, RowPtr kv, int j0, int j1, int tid0, int nthr) {
   const int t = (int)threadIdx.x - tid0;
   if (t < 0 || t >= nthr) return;
-  for (int idx = t; idx < (j1 - j0) * 16; idx += nthr) {
-    const int j = j0 + (idx >> 4), c = (idx & 15) * 4;
-    const float* row = kv(j);
-    *(f4*)&sm.k[j][c] = *(const f4*)(row + c);
-    *(f4*)&sm.v[j][c] = *(const f4*)(row + D + c);
+  const int n = (j1 - j0) * 16;
+  if constexpr (UB == 1) {
+    for (int idx = t; idx < n; idx += nthr) {
+      const int j = j0 + (idx >> 4), c = (idx & 15) * 4;
+      const float* row = kv(j);
+      *(f4*)&sm.k[j][c] = *(const f4*)(row + c);
+      *(f4*)&sm.v[j][c] = *(const f4*)(row + D + c);
+    }
+  } else {
+    for (int base = t; base < n; base += UB * nthr) {
+      f4 kk[UB], vv[UB];
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int idx = min(base + u * nthr, n - 1);
+        const float* row = kv(j0 + (idx >> 4)) + (idx & 15) * 4;
+        kk[u] = *(const f4*)row;
+        vv[u] = *(const f4*)(row + D);
+      }
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int idx = base + u * nthr;
+        if (idx < n) {
+          const int j = j0 + (idx >> 4), c = (idx & 15) * 4;
+          *(f4*)&sm.k[j][c] = kk[u];
+          *(f4*)&sm.v[j][c] = vv[u];
+        }
+      }
+    }
   }
 }
 
-// Stage all npos rows and the query with the first 128 threads.
+// Stage all npos rows and the query with the first 128 threads, four chunks a pass.
 template <class RowPtr>
 __device__ __forceinline__ void attn_stage(AttnSmem& sm, RowPtr kv, int npos, const float* q) {
-  attn_stage_rows(sm, kv, 0, npos, 0, 128);
+  attn_stage_rows<4>(sm, kv, 0, npos, 0, 128);
   if (threadIdx.x < DH) sm.q[threadIdx.x] = q[threadIdx.x];
 }
 
