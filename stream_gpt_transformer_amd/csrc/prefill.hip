@@ -438,6 +438,8 @@ hipError_t launch_head_f32(const Weights& w, const float* x_row, float* logits, 
 // MLP projection: 192).  The partial sums are added in split order by the kernel
 // that consumes them (attention for QKV, the residual-and-LayerNorm kernel for O
 // and the MLP projection).
+// QKV's split can be set at build time (-DPF_S_QKV=2 or 4 fit the partial-sum
+// buffer and divide K = 768 into whole stages); 3 measured fastest.
 #ifndef PF_S_QKV
 #define PF_S_QKV 3
 #endif
