@@ -183,18 +183,23 @@ __global__ __launch_bounds__(64) void k_bln(const ProjArgs a) {
 
 // Attention of head blockIdx.x for session blockIdx.y over its positions 0..pos,
 // reading every key/value row (the current one included) from the session's cache
-// at (source*12 + layer)*1536 + offset.
+// at (source*12 + layer)*1536 + offset.  attn_threads<SEQ>() threads: the fp32 form
+// gives the same value for any multiple of 128 (the single-launch kernel runs it
+// with 512); the sequential-order form takes 128.
 template <bool SEQ>
-__global__ __launch_bounds__(128) void k_attn(const ProjArgs a) {
+constexpr int attn_threads() { return SEQ ? 128 : 512; }
+template <bool SEQ>
+__global__ __launch_bounds__(attn_threads<SEQ>()) void k_attn(const ProjArgs a) {
+  constexpr int NT = attn_threads<SEQ>();
   __shared__ __align__(16) AttnSmem sm;
   const int h = blockIdx.x, b = blockIdx.y;
   const int npos = a.ss.pos[b] + 1;
   const float* cache = a.caches + (size_t)b * a.cache_stride;
   const int l = a.layer;
   auto kv = [&](int j) { return cache + ((size_t)j * L + l) * KV_ROW + h * DH; };
-  attn_stage(sm, kv, npos, a.k.qkv + (size_t)b * D3 + h * DH);
+  attn_stage(sm, kv, npos, a.k.qkv + (size_t)b * D3 + h * DH, NT);
   __syncthreads();
-  const float o = SEQ ? attn_compute_seq(sm, npos) : attn_compute(sm, npos, 128);
+  const float o = SEQ ? attn_compute_seq(sm, npos) : attn_compute(sm, npos, NT);
   if (threadIdx.x < DH) a.k.att[(size_t)b * D + h * DH + threadIdx.x] = o;
 }
 
@@ -477,7 +482,7 @@ static void launch_layers(ProjArgs& a, hipStream_t s) {
   for (int l = 0; l < L; ++l) {
     a.layer = l;
     launch_proj_ln<MODE_QKV, RPW, BT768, H16>(a, s);
-    hipLaunchKernelGGL(k_attn<false>, dim3(H, B), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(k_attn<false>, dim3(H, B), dim3(attn_threads<false>()), 0, s, a);
     launch_proj<MODE_O, RPW, BT768, H16>(a, s);
     launch_proj_ln<MODE_FC, RPW, BT768, H16>(a, s);
     launch_proj<MODE_PR, RPW, BT3072, H16>(a, s);
@@ -540,7 +545,7 @@ hipError_t launch_step_q8(const Weights& w, const Work& k, const Sessions& ss, f
   for (int l = 0; l < L; ++l) {
     a.layer = l;
     launch_q8<MODE_QKV, 2>(a, s);
-    hipLaunchKernelGGL(k_attn<true>, dim3(H, 1), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(k_attn<true>, dim3(H, 1), dim3(attn_threads<true>()), 0, s, a);
     launch_q8<MODE_O, 1>(a, s);
     launch_q8<MODE_FC, 2>(a, s);
     launch_q8<MODE_PR, 1>(a, s);

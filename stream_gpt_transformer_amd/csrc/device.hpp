@@ -584,10 +584,10 @@ __device__ __forceinline__ void attn_stage_rows(AttnSmem& sm, RowPtr kv, int j0,
   }
 }
 
-// Stage all npos rows and the query with the first 128 threads, four chunks a pass.
+// Stage all npos rows and the query with the first nthr threads, four chunks a pass.
 template <class RowPtr>
-__device__ __forceinline__ void attn_stage(AttnSmem& sm, RowPtr kv, int npos, const float* q) {
-  attn_stage_rows<4>(sm, kv, 0, npos, 0, 128);
+__device__ __forceinline__ void attn_stage(AttnSmem& sm, RowPtr kv, int npos, const float* q, int nthr = 128) {
+  attn_stage_rows<4>(sm, kv, 0, npos, 0, nthr);
   if (threadIdx.x < DH) sm.q[threadIdx.x] = q[threadIdx.x];
 }
 
