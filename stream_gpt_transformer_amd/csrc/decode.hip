@@ -457,8 +457,8 @@ __global__ __launch_bounds__(256) void k_special_bits(int kind, uint32_t first, 
 #ifndef BATCH_HEAD_SB
 #define BATCH_HEAD_SB 32
 #endif
-#ifndef BATCH_HEAD_BT
-#define BATCH_HEAD_BT 16
+#ifndef BATCH_HEAD_BT  // sessions staged per pass: 24 KB of LDS, so more workgroups fit a CU
+#define BATCH_HEAD_BT 8
 #endif
 
 template <int MODE, int RPW, int BT, bool H16>
