@@ -5,9 +5,19 @@ roofline, with the CPU oracle timed on the host beside it.
 
 A step is one cachedStep call: one token through the 12 blocks and the tied head.
 The workload is the 128-position session (uniform-random token ids, seed 101) of
-the seed-0 N(0, 0.02) checkpoint: the timed steps walk positions 0..127 and start
-over from an empty cache.  Inputs are resident in HBM before timing starts.
+the seed-0 N(0, 0.02) checkpoint.  Each weight form first runs the whole session in
+order, which fills a 128-position cache; the timed steps then take positions
+p = 37*i mod 128 (i = 0, 1, ...), so any number of steps samples the whole range
+0..127 (128 steps visit every position once), each step reading the session's
+rows 0..p-1 and rewriting row p with the same values.  Inputs are resident in HBM
+before timing starts.  After every timed leg the workspace error word is read: a
+nonzero word (a bounded wait inside the step gave up, so that step's outputs are
+invalid) is printed in the line and the bench exits with status 1.
 Prints one JSON line.
+
+--timeline: per-block phase times of the single-launch step from its timestamp
+hook (fp32 and int8 at chosen positions) and per-position step times over the
+session, as a markdown summary (no JSON line).
 """
 from __future__ import annotations
 
@@ -40,21 +50,32 @@ KV_PER_POS = 73_728
 LOGITS = 201_028
 PREFILL_FLOP = 21_743_271_936 + 304_349_184  # block GEMMs + causal attention at T = 128
 # Batched step, 64 sessions: 2 FLOP per weight and session over the 48 block matrices and
-# the head (123,532,032 weights), i.e. 15,812,100,096 FLOP per step; fp32 vector FMA peak.
+# the head (123,532,032 weights), i.e. 15,812,100,096 FLOP per step, against the fp32
+# vector FMA rate: 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP x 2.4 GHz = 78.6 TFLOP/s with
+# the unpacked instructions this library is built for (packed fp32 is turned off); the
+# packed-instruction figure, 157.3 TFLOP/s, is reported beside it.
 BATCH = 64
 BATCH_FLOP = 2 * BATCH * 123_532_032
-FP32_VECTOR_PEAK_TF = 157.3
+FP32_VECTOR_PEAK_TF = 78.6
+FP32_VECTOR_PACKED_PEAK_TF = 157.3
+
+STRIDE = 37  # odd, so p = 37 i mod 128 visits all 128 positions in any 128 consecutive steps
+NPOS = 128
 
 
 def step_bytes(fixed: int, p: int) -> int:
     return fixed + KV_PER_POS * (p + 1) + LOGITS
 
 
-# Measured memory traffic of the fp32 step kernel: a text summary under profiles/
-# (two rocprofv3 --pmc runs of `bench.py --pmc-probe`, FETCH_SIZE then WRITE_SIZE,
-# scaled by a plain copy of known size).  Its figures hold for the kernel sources
-# they name by SHA-256; after any change to those sources the traffic is unknown
-# (null) until the counters are taken again.
+def spread_positions(n: int, start: int = 0):
+    return [(STRIDE * i) % NPOS for i in range(start, start + n)]
+
+
+# Measured memory traffic of the step kernels: a text summary under profiles/ (two
+# rocprofv3 --pmc runs of `bench.py --pmc-probe`, FETCH_SIZE then WRITE_SIZE, scaled by
+# a plain copy of known size).  Its figures hold for the kernel sources they name by
+# SHA-256; after any change to those sources the traffic is unknown (null) until the
+# counters are taken again.
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_fused_f32_b1_traffic.md")
 KERNEL_SOURCES = ["fused.hip", "device.hpp", "internal.hpp", "layout.hpp"]
 PMC_COPY_BYTES = 256 << 20
@@ -70,7 +91,7 @@ def kernel_sources_sha256() -> str:
 
 
 def measured_traffic(key: str = "traffic_bytes_per_launch"):
-    """Bytes per step launch (fp32 kernel; key ..._f16 for the binary16-weight kernel)
+    """Bytes per step launch (fp32 kernel; key ..._f16 / ..._q8 for the other forms)
     from the committed counter summary, or None."""
     try:
         with open(TRAFFIC_SUMMARY) as f:
@@ -90,16 +111,210 @@ def measured_traffic(key: str = "traffic_bytes_per_launch"):
         return None
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, toks, cycle_seconds: float) -> dict:
+    """The oracle as it stands, on the host: single-thread medians of the fp32 and
+    int8 steps at positions 0..7 and one infer(128); then all threads (OpenMP over
+    independent outputs, bit-identical to one thread) cycling the fp32 and int8 steps
+    over the session for a time budget, and one infer(128)."""
+    import numpy as np
+
+    import oracle
+    import synth
+    if not os.path.exists(oracle.LIB):
+        oracle.build()
+    d = synth.GPT2
+    per = oracle.cache_words_per_pos(d)
+    q8 = oracle.q8_quantize_weights(d, w)  # the packing, not timed
+
+    def step(kind, cache, p):
+        if kind == "int8":
+            rc, _ = oracle.q8_cached_step(d, w, q8[0], q8[1], cache, p * per, int(toks[p]), p)
+        else:
+            rc, _ = oracle.cached_step(d, w, cache, p * per, int(toks[p]), p)
+        assert rc == 0, rc
+
+    def first8(kind):
+        cache = np.zeros(8 * per, np.float32)
+        ts = []
+        for p in range(8):
+            t0 = time.perf_counter()
+            step(kind, cache, p)
+            ts.append(time.perf_counter() - t0)
+        return statistics.median(ts)
+
+    def cycle(kind, seconds):
+        cache = np.zeros(NPOS * per, np.float32)
+        n, t0 = 0, time.perf_counter()
+        while n == 0 or time.perf_counter() - t0 < seconds:
+            step(kind, cache, n % NPOS)
+            n += 1
+        el = time.perf_counter() - t0
+        return n, el
+
+    def infer128():
+        t0 = time.perf_counter()
+        rc, _ = oracle.infer(d, w, toks[:NPOS])
+        assert rc == 0, rc
+        return time.perf_counter() - t0
+
+    oracle.set_threads(1)
+    st = {"fp32_step_ms_median_pos0_7": round(first8("fp32") * 1e3, 2),
+          "int8_step_ms_median_pos0_7": round(first8("int8") * 1e3, 2),
+          "infer128_s": round(infer128(), 2)}
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    nthreads = max(1, min(avail, 16))
+    oracle.set_threads(nthreads)
+    used = oracle.max_threads()
+    n32, el32 = cycle("fp32", cycle_seconds)
+    n8, el8 = cycle("int8", cycle_seconds / 2)
+    inf_all = infer128()
+    return {"value": round(n32 / el32, 3), "unit": "tok/s", "cores": used, "kind": "oracle",
+            "sample": f"fp32 cachedStep on {used} threads: {n32} calls cycling positions 0..127 of the 128-token "
+                      f"session ({el32:.1f} s); int8 {n8} calls ({el8:.1f} s); infer(128) once; single-thread: "
+                      f"steps at positions 0..7 and one infer(128)",
+            "host_cpus": os.cpu_count(), "affinity_cpus": avail, "cpu_model": cpu_model(),
+            "single_thread": st,
+            "all_threads": {"threads": used, "fp32_tok_s": round(n32 / el32, 3), "int8_tok_s": round(n8 / el8, 3),
+                            "infer128_s": round(inf_all, 2)}}
+
+
+# ---- --timeline ---------------------------------------------------------------
+# The single-launch step's timestamp hook (gpt2_test_fused_trace) writes a 100 MHz
+# wall-clock stamp per workgroup: slot 0 at its start; for block l, computed by the
+# set l % 2, slot 1+4l when the block input x is in LDS (head units: after their
+# share of the reduce-scatter), 2+4l when a regular unit's QKV rows are published
+# (head units: attention output ready), 3+4l when x1 is in LDS, 4+4l when the
+# XCD's GELU slice is in LDS; 49 head input, 50 head rows done, 51 end.  Workgroup
+# b runs on XCD b % 8 with rank b // 8 (the kernel checks this placement): set =
+# rank % 2, q = rank // 2, and it is a head unit when q < (2 if XCD < 4 else 1).
+TICK_US = 0.01
+NGRID = 256
+
+
+def _roles():
+    reg = {0: [], 1: []}
+    head = {0: [], 1: []}
+    for b in range(NGRID):
+        X, rank = b % 8, b // 8
+        st, q = rank % 2, rank // 2
+        (head if q < (2 if X < 4 else 1) else reg)[st].append(b)
+    return reg, head
+
+
+def _block_phases(tr):
+    """tr: [256][64] int ticks of one launch -> per-block phase times (us)."""
+    import numpy as np
+    reg, head = _roles()
+    t0 = tr[:, 0].min()
+    t = (tr.astype(np.int64) - t0) * TICK_US
+
+    def med(slot, units):
+        return float(np.median(t[units, slot]))
+
+    rows = []
+    for l in range(12):
+        st = l % 2
+        rows.append({"in": med(1 + 4 * l, reg[st]), "qkv": med(2 + 4 * l, reg[st]), "att": med(2 + 4 * l, head[st]),
+                     "x1": med(3 + 4 * l, reg[st]), "g": med(4 + 4 * l, reg[st])})
+    allu = list(range(NGRID))
+    head_in, head_done, end = med(49, allu), float(t[:, 50].max()), float(t[:, 51].max())
+    for l in range(12):
+        rows[l]["next"] = rows[l + 1]["in"] if l < 11 else head_in
+    return rows, head_in, head_done, end
+
+
+def timeline_report(g, m, call, filled_cache, stream, positions, reps) -> int:
+    import numpy as np
+    import torch
+    dev = m.packed.device
+    trace = torch.zeros(NGRID * 64, dtype=torch.int64, device=dev)
+    forms = (("fp32", g.gpt2_cached_step), ("int8-g64", g.gpt2_q8_cached_step))
+    print("# Timeline of the single-launch step (medians over workgroups of a role, then over "
+          f"{reps} launches; us from the first workgroup's start)\n")
+    for name, fn in forms:
+        cache = filled_cache(fn)
+        for pos in positions:
+            runs = []
+            for _ in range(reps):
+                trace.zero_()
+                torch.cuda.synchronize()
+                g.gpt2_test_fused_trace(trace.data_ptr())
+                call(fn, cache, pos)
+                torch.cuda.synchronize()
+                g.gpt2_test_fused_trace(None)
+                runs.append(_block_phases(trace.view(NGRID, 64).cpu().numpy()))
+            keys = ("in", "qkv", "att", "x1", "g", "next")
+            rows = [{k: float(np.median([r[0][l][k] for r in runs])) for k in keys} for l in range(12)]
+            head_in = float(np.median([r[1] for r in runs]))
+            head_done = float(np.median([r[2] for r in runs]))
+            end = float(np.median([r[3] for r in runs]))
+            print(f"## {name}, position {pos}\n")
+            print("| block | x in | x -> QKV published | QKV -> attention out | attention -> x1 | "
+                  "x1 -> GELU slice | GELU -> next x | block |")
+            print("|---|---|---|---|---|---|---|---|")
+            for l, r in enumerate(rows):
+                print(f"| {l} | {r['in']:.2f} | {r['qkv'] - r['in']:.2f} | {r['att'] - r['qkv']:.2f} | "
+                      f"{r['x1'] - r['att']:.2f} | {r['g'] - r['x1']:.2f} | {r['next'] - r['g']:.2f} | "
+                      f"{r['next'] - r['in']:.2f} |")
+            blk = [r["next"] - r["in"] for r in rows]
+            seg = {k: float(np.mean([r[b] - r[a] for r in rows]))
+                   for a, b, k in (("in", "qkv", "qkv"), ("qkv", "att", "att"), ("att", "x1", "x1"),
+                                   ("x1", "g", "g"), ("g", "next", "next"))}
+            print(f"| mean | | {seg['qkv']:.2f} | {seg['att']:.2f} | {seg['x1']:.2f} | {seg['g']:.2f} | "
+                  f"{seg['next']:.2f} | {float(np.mean(blk)):.2f} |\n")
+            print(f"- start -> block 0 input: {rows[0]['in']:.2f} us; head input at {head_in:.2f} us; "
+                  f"head rows done {head_done:.2f} us (head {head_done - head_in:.2f} us); last workgroup ends "
+                  f"{end:.2f} us\n")
+        # per-position step time over the session (events around each launch), median of 3 passes
+        per = np.zeros((3, NPOS))
+        for rep in range(3):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(NPOS + 1)]
+            ev[0].record(stream)
+            for p in range(NPOS):
+                call(fn, cache, p)
+                ev[p + 1].record(stream)
+            torch.cuda.synchronize()
+            per[rep] = [ev[p].elapsed_time(ev[p + 1]) * 1e3 for p in range(NPOS)]
+        med = np.median(per, axis=0)
+        print(f"## {name}: step time by position (us, median of 3 passes over the session)\n")
+        print("| positions | " + " | ".join(f"{a}..{a + 15}" for a in range(0, NPOS, 16)) + " |")
+        print("|---|" + "---|" * (NPOS // 16))
+        print("| mean | " + " | ".join(f"{med[a:a + 16].mean():.1f}" for a in range(0, NPOS, 16)) + " |\n")
+        print(f"- session mean {med.mean():.2f} us, min {med.min():.2f}, max {med.max():.2f}\n")
+    st = m.status()
+    print(f"- workspace error word after the runs: {st}")
+    return 1 if st else 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1280)
     ap.add_argument("--warmup", type=int, default=128)
     ap.add_argument("--skip-cpu", action="store_true", help="omit the CPU-oracle baseline leg")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=6.0,
+                    help="time budget of the all-thread fp32 cycling leg (int8 takes half)")
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for counter runs: 128 fp32, 128 int8, then 128 binary16 steps (positions 0..127) and one "
                          "device copy of 256 MiB, nothing timed or printed")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-block phase times and per-position step times (markdown), no JSON line")
+    ap.add_argument("--timeline-positions", default="1,64,127")
+    ap.add_argument("--timeline-reps", type=int, default=7)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the decode step is a single-GPU path); got --gpus {args.gpus}",
@@ -115,52 +330,65 @@ def main() -> int:
     dev = torch.device("cuda", int(os.environ.get("LOCAL_RANK", 0)))
     torch.cuda.set_device(dev)
     w = synth.make_checkpoint(0, synth.GPT2)
-    toks = synth.make_tokens(synth.SEED_SESSION, 128)
+    toks = synth.make_tokens(synth.SEED_SESSION, NPOS)
     ck = torch.from_numpy(w).to(dev)
     m = g.Model(ck, g.GPT2_PACK_F32 | g.GPT2_PACK_Q8 | g.GPT2_PACK_F16)
     torch.cuda.synchronize()
     del ck
     stream = torch.cuda.current_stream()
-    cache = m.new_cache(128)
     logits = torch.empty(g.GPT2_VOCAB, dtype=torch.float32, device=dev)
-    h, ws, c, lp, s = m.handle, m.ws.data_ptr(), cache.data_ptr(), logits.data_ptr(), stream.cuda_stream
+    h, ws, lp, s = m.handle, m.ws.data_ptr(), logits.data_ptr(), stream.cuda_stream
     PER = g.GPT2_CACHE_WORDS_PER_POS
+    FIXED = {g.gpt2_cached_step: F32_FIXED, g.gpt2_q8_cached_step: Q8_FIXED, g.gpt2_f16_cached_step: F16_FIXED}
 
-    def run(fn, n, start=0):
-        for i in range(start, start + n):
-            p = i % 128
-            rc = fn(h, c, p * PER, int(toks[p]), p, ws, lp, s)
-            if rc:
-                raise g.Gpt2Error(rc, fn.__name__)
+    def call(fn, cache, p):
+        rc = fn(h, cache.data_ptr(), p * PER, int(toks[p]), p, ws, lp, s)
+        if rc:
+            raise g.Gpt2Error(rc, fn.__name__)
+
+    def filled_cache(fn):
+        """A 128-position cache holding the session's rows (the session run in order)."""
+        cache = m.new_cache(NPOS)
+        for p in range(NPOS):
+            call(fn, cache, p)
+        return cache
 
     def timed(fn, steps, warmup):
-        run(fn, warmup)
+        cache = filled_cache(fn)
+        for p in spread_positions(warmup):
+            call(fn, cache, p)
+        pos = spread_positions(steps, warmup)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        run(fn, steps)
+        for p in pos:
+            call(fn, cache, p)
         e1.record(stream)
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
-        fixed = {g.gpt2_cached_step: F32_FIXED, g.gpt2_q8_cached_step: Q8_FIXED, g.gpt2_f16_cached_step: F16_FIXED}[fn]
-        nbytes = sum(step_bytes(fixed, i % 128) for i in range(steps))
-        return ms, nbytes
+        return e0.elapsed_time(e1), sum(step_bytes(FIXED[fn], p) for p in pos), m.status()
 
     if args.pmc_probe:
-        run(g.gpt2_cached_step, 128)
-        run(g.gpt2_q8_cached_step, 128)
-        run(g.gpt2_f16_cached_step, 128)
+        for fn in (g.gpt2_cached_step, g.gpt2_q8_cached_step, g.gpt2_f16_cached_step):
+            filled_cache(fn)
         src = torch.ones(PMC_COPY_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
+        st = m.status()
         m.close()
-        return 0
+        return 1 if st else 0
 
-    ms32, b32 = timed(g.gpt2_cached_step, args.steps, args.warmup)
-    ms8, b8 = timed(g.gpt2_q8_cached_step, args.steps, args.warmup)
-    ms16, b16 = timed(g.gpt2_f16_cached_step, args.steps, args.warmup)
+    if args.timeline:
+        rc = timeline_report(g, m, call, filled_cache, stream,
+                             [int(x) for x in args.timeline_positions.split(",") if x != ""], args.timeline_reps)
+        m.close()
+        return rc
+
+    status = {}
+    ms32, b32, status["fp32"] = timed(g.gpt2_cached_step, args.steps, args.warmup)
+    ms8, b8, status["int8"] = timed(g.gpt2_q8_cached_step, args.steps, args.warmup)
+    ms16, b16, status["binary16"] = timed(g.gpt2_f16_cached_step, args.steps, args.warmup)
     tok32 = args.steps / (ms32 * 1e-3)
     tok8 = args.steps / (ms8 * 1e-3)
     tok16 = args.steps / (ms16 * 1e-3)
@@ -172,9 +400,9 @@ def main() -> int:
     # the whole row): ms/step over the 128-position session and the logits' deviation
     # from the fp32 step's on the same tokens (synthetic weights: a size of the
     # quantization error, not an accuracy claim)
-    ref = torch.empty((128, g.GPT2_VOCAB), dtype=torch.float32, device=dev)
-    vcache = m.new_cache(128)
-    for p in range(128):
+    ref = torch.empty((NPOS, g.GPT2_VOCAB), dtype=torch.float32, device=dev)
+    vcache = m.new_cache(NPOS)
+    for p in range(NPOS):
         g.gpt2_cached_step(h, vcache.data_ptr(), p * PER, int(toks[p]), p, ws, ref[p].data_ptr(), s)
     vout = torch.empty_like(ref)
     variants = []
@@ -191,14 +419,15 @@ def main() -> int:
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            for p in range(128):
+            for p in range(NPOS):
                 rc = g.gpt2_q8_cached_step_grouped(mv.handle, gx, vcache.data_ptr(), p * PER, int(toks[p]), p,
                                                    mv.ws.data_ptr(), vout[p].data_ptr(), s)
                 if rc:
                     raise g.Gpt2Error(rc, "gpt2_q8_cached_step_grouped")
             e1.record(stream)
             torch.cuda.synchronize()
-            vts.append(e0.elapsed_time(e1) / 128)
+            vts.append(e0.elapsed_time(e1) / NPOS)
+        status[f"q8_variant_{gw or 'row'}_{gx or 'row'}"] = mv.status()
         dl = (vout - ref).abs()
         variants.append({"weight_group": gw or "row", "input_group": gx or "row",
                          "ms_per_step": round(min(vts), 4),
@@ -212,7 +441,7 @@ def main() -> int:
     # greedy generation on the device: an 8-token prompt and 120 chosen tokens
     # (127 steps and 120 on-device choices per call), median of 5 calls
     gprompt = toks[:8].tolist()
-    gcache = torch.zeros(128 * PER, dtype=torch.float32, device=dev)
+    gcache = torch.zeros(NPOS * PER, dtype=torch.float32, device=dev)
     gout = torch.empty(120, dtype=torch.int32, device=dev)
     gst = torch.empty(1, dtype=torch.int32, device=dev)
     gts = []
@@ -224,19 +453,20 @@ def main() -> int:
         torch.cuda.synchronize()
         if i:
             gts.append(e0.elapsed_time(e1))
-    assert int(gst.item()) == 0
+    status["generate"] = m.status()
+    status["generate_logits"] = int(gst.item())
     gms = statistics.median(gts)
 
     # batched step: 64 sessions (seeded token streams 1000..1063) advanced together over
     # positions 0..127, after a warm-up pass over positions 0..15; per batched step, the
     # median of three passes over the 128 positions (each pass rewrites the cache rows
     # it reads, so every pass does the same work)
-    btoks = np.stack([synth.make_tokens(synth.SEED_BATCH_BASE + b, 128) for b in range(BATCH)])
-    bcaches = torch.zeros((BATCH, 128 * PER), dtype=torch.float32, device=dev)
+    btoks = np.stack([synth.make_tokens(synth.SEED_BATCH_BASE + b, NPOS) for b in range(BATCH)])
+    bcaches = torch.zeros((BATCH, NPOS * PER), dtype=torch.float32, device=dev)
     blog = torch.empty((BATCH, g.GPT2_VOCAB), dtype=torch.float32, device=dev)
 
     def bstep(p):
-        rc = g.gpt2_batched_cached_step(h, bcaches.data_ptr(), 128 * PER, [p * PER] * BATCH,
+        rc = g.gpt2_batched_cached_step(h, bcaches.data_ptr(), NPOS * PER, [p * PER] * BATCH,
                                         btoks[:, p].tolist(), [p] * BATCH, ws, blog.data_ptr(), s)
         if rc:
             raise g.Gpt2Error(rc, "gpt2_batched_cached_step")
@@ -248,16 +478,17 @@ def main() -> int:
     for _ in range(3):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for p in range(128):
+        for p in range(NPOS):
             bstep(p)
         e1.record(stream)
         torch.cuda.synchronize()
-        bts.append(e0.elapsed_time(e1) / 128)
+        bts.append(e0.elapsed_time(e1) / NPOS)
     bms = statistics.median(bts)
+    status["batched"] = m.status()
     del bcaches, blog
 
     # prefill: median of 20 infer(128) calls after warm-up
-    ptoks = synth.make_tokens(synth.SEED_PREFILL, 128).tolist()
+    ptoks = synth.make_tokens(synth.SEED_PREFILL, NPOS).tolist()
     for _ in range(3):
         g.gpt2_infer(h, ptoks, ws, lp, s)
     pts = []
@@ -269,28 +500,14 @@ def main() -> int:
         torch.cuda.synchronize()
         pts.append(e0.elapsed_time(e1))
     pms = statistics.median(pts)
+    status["prefill"] = m.status()
 
-    cpu = None
-    if not args.skip_cpu:
-        import oracle
-        oracle.build() if not os.path.exists(oracle.LIB) else None
-        nthreads = min(os.cpu_count() or 1, 16)
-        oracle.set_threads(nthreads)
-        ocache = np.zeros(128 * PER, np.float32)
-        t0 = time.perf_counter()
-        n = 0
-        # the session's positions in order, starting over from an empty cache after 127,
-        # until the time budget is spent (at least one step)
-        while n == 0 or time.perf_counter() - t0 < args.cpu_seconds:
-            p = n % 128
-            rc, _ = oracle.cached_step(synth.GPT2, w, ocache, p * PER, int(toks[p]), p)
-            assert rc == 0
-            n += 1
-        el = time.perf_counter() - t0
-        cpu = {"value": round(n / el, 3), "unit": "tok/s", "cores": oracle.max_threads(), "kind": "oracle",
-               "sample": f"{n} fp32 cachedStep calls cycling positions 0..127 of the same 128-token session "
-                         f"({el:.1f} s, OpenMP over independent outputs)"}
+    cpu = None if args.skip_cpu else cpu_baseline(w, toks, args.cpu_seconds)
 
+    bflops = BATCH_FLOP / (bms * 1e-3) / 1e12
+    pos_note = (f"positions 37*i mod 128 over a filled 128-position cache "
+                f"({'all 128' if args.steps >= NPOS else str(len(set(spread_positions(args.steps, args.warmup))))} "
+                f"distinct positions timed)")
     out = {
         "metric": "batch-1 cachedStep tok/s (fp32 & int8-g64) + % of HBM roofline",
         "value": round(tok32, 1),
@@ -305,12 +522,14 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic (seed-0 N(0,0.02) weights, seeded uniform token ids)",
         "config": {"workload": "GPT-2 124M batch-1 cachedStep, 128-position session, fp32",
-                   "positions": "0..127 cycled", "batch": 1},
+                   "positions": pos_note, "batch": 1},
         "roofline": {"bound": "hbm", "achieved": round(gbs32, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs32 / HBM_PEAK_GBS, 4), "traffic": measured_traffic()},
+        "status": status,
         "int8_g64": {"value": round(tok8, 1), "unit": "tok/s", "ms_per_step": round(ms8 / args.steps, 5),
                      "roofline": {"bound": "hbm", "achieved": round(gbs8, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                  "frac": round(gbs8 / HBM_PEAK_GBS, 4)}},
+                                  "frac": round(gbs8 / HBM_PEAK_GBS, 4),
+                                  "traffic": measured_traffic("traffic_bytes_per_launch_q8")}},
         "f16_weights": {"value": round(tok16, 1), "unit": "tok/s", "ms_per_step": round(ms16 / args.steps, 5),
                         "roofline": {"bound": "hbm", "achieved": round(gbs16, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                      "frac": round(gbs16 / HBM_PEAK_GBS, 4),
@@ -318,12 +537,13 @@ def main() -> int:
         "q8_variants": {"session": "128 positions, seed-101 tokens, seed-0 checkpoint", "rows": variants},
         "batched": {"value": round(BATCH / (bms * 1e-3), 1), "unit": "tok/s", "ms_per_step": round(bms, 4),
                     "sample": "64 sessions advanced together, positions 0..127 (fp32), median of 3 passes",
-                    "roofline": {"bound": "alu", "achieved": round(BATCH_FLOP / (bms * 1e-3) / 1e12, 2),
-                                 "peak": FP32_VECTOR_PEAK_TF, "unit": "TFLOP/s",
-                                 "frac": round(BATCH_FLOP / (bms * 1e-3) / 1e12 / FP32_VECTOR_PEAK_TF, 4)}},
+                    "roofline": {"bound": "alu", "achieved": round(bflops, 2), "peak": FP32_VECTOR_PEAK_TF,
+                                 "unit": "TFLOP/s", "frac": round(bflops / FP32_VECTOR_PEAK_TF, 4),
+                                 "peak_packed_fp32": FP32_VECTOR_PACKED_PEAK_TF,
+                                 "frac_of_packed_peak": round(bflops / FP32_VECTOR_PACKED_PEAK_TF, 4)}},
         "generate": {"value": round(120 / (gms * 1e-3), 1), "unit": "tok/s", "ms_per_call": round(gms, 3),
                      "sample": "fp32 greedy, 8-token prompt + 120 tokens chosen on the GPU (127 steps)"},
-        "prefill": {"value": round(128 / (pms * 1e-3), 1), "unit": "tok/s", "ms_median": round(pms, 4),
+        "prefill": {"value": round(NPOS / (pms * 1e-3), 1), "unit": "tok/s", "ms_median": round(pms, 4),
                     "roofline": {"bound": "mfma", "achieved": round(PREFILL_FLOP / (pms * 1e-3) / 1e12, 2),
                                  "peak": FP32_MFMA_PEAK_TF, "unit": "TFLOP/s",
                                  "frac": round(PREFILL_FLOP / (pms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TF, 4)}},
@@ -331,6 +551,10 @@ def main() -> int:
     }
     print(json.dumps(out), flush=True)
     m.close()
+    bad = {k: v for k, v in status.items() if v}
+    if bad:
+        print(f"workspace error words set: {bad}; the timed outputs are invalid", file=sys.stderr)
+        return 1
     return 0
 
 

@@ -126,7 +126,10 @@ int gpt2_pack_weights_grouped(const void* ckpt_dev, size_t ckpt_nbytes, void* pa
 /* The int8 weight-scale group a model was packed with (0 = per row), -1 for null. */
 int gpt2_q8_weight_group(const gpt2_model* model);
 
-/* Free the host handle (device memory is the caller's). */
+/* Free the host handle made by gpt2_pack_weights (the marXiv 2609.00018 abstract
+ * lists buffer release among the obligations of a session).  The device memory
+ * (packed weights, workspaces, caches) is the caller's and is not touched.  A null
+ * handle is ignored; a handle must not be used after it is released. */
 void gpt2_release(gpt2_model* model);
 
 /* cachedStep (LeanExe GPT-2 README, cachedStep paragraph): one token at `position`.
@@ -179,12 +182,18 @@ int gpt2_f16_cached_step(const gpt2_model* model, float* cache_dev, size_t cache
 int gpt2_q8_cached_step_grouped(const gpt2_model* model, int input_group, float* cache_dev, size_t cache_nwords,
                                 uint32_t token, int32_t position, void* ws_dev, float* logits_dev, void* stream);
 
-/* B independent sessions (1..64) advanced by one token each.
+/* B independent sessions (1..64) advanced by one token each: the cachedStep of the
+ * LeanExe GPT-2 README applied to every session, with the batch invariance of the
+ * muInference README's batch-invariance paragraph (a request's output does not
+ * depend on what else is in the batch).
  *  caches_dev         : session b's cache starts at caches_dev + b*cache_stride_words;
  *                       same layout and in-place append as gpt2_cached_step.
- *  cache_stride_words : >= (max_b position[b] + 1) * 18,432 and a multiple of 4.
+ *  cache_stride_words : >= (max_b position[b] + 1) * 18,432 and a multiple of 4
+ *                       (GPT2_ECACHE otherwise).  One allocation holds all B caches.
  *  cache_nwords_host, tokens_host, positions_host : host arrays of B entries, each
  *                       validated like gpt2_cached_step's scalars.
+ *  B                  : 1..64 (GPT2_EARG otherwise).
+ *  ws_dev             : gpt2_workspace_nbytes() bytes; it has room for 64 sessions.
  *  logits_dev         : [B][50,257].
  * Session b's logits and cache are bit-identical to gpt2_cached_step run on that
  * session alone.  Needs GPT2_PACK_F32. */
@@ -200,9 +209,15 @@ int gpt2_infer(const gpt2_model* model, const uint32_t* tokens_host, int n, void
                void* stream);
 
 /* Error word of a workspace, given a host copy of at least its first 16 bytes:
- * 0 = fine; nonzero = a wait inside the single-launch decode step gave up (after
- * about 2^21 polls); that step's outputs are invalid and the word stays set until
- * the caller zero-fills the workspace again. */
+ * 0 = fine; 1 = a wait inside the single-launch decode step gave up (after about
+ * 2^21 polls); 2 = its workgroups were not dealt round-robin over the eight XCDs.
+ * Either way that step's outputs, and those of every later step on the workspace,
+ * are invalid (the waits of later steps return at once), and the word stays set
+ * until the caller zero-fills the workspace again.  The single-launch step is one
+ * ordinary launch of 256 workgroups, one per compute unit, whose waits need all of
+ * them resident together: on a GPU that other work shares, a step can end this way
+ * although the call returned GPT2_OK, so a caller that shares the GPU reads this
+ * word after its steps. */
 int gpt2_workspace_status(const void* ws_host_copy);
 
 /* ---- test hooks (not needed by applications) -------------------------------- */
@@ -217,10 +232,6 @@ void gpt2_test_force_phase_kernels(int on);
  * phases of block l received; 49 head input received; 50 head rows done; 51 end).
  * NULL turns it off. */
 void gpt2_test_fused_trace(void* trace_dev);
-
-/* on != 0: launch the single-launch step with an ordinary launch instead of a
- * cooperative one (its waits are bounded either way). */
-void gpt2_test_fused_plain_launch(int on);
 
 /* Prefill that hands the session over to the cached step.  This is an extension:
  * the LeanExe README's infer returns logits only; the `lean` page's engine reuses

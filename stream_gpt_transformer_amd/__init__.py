@@ -60,7 +60,6 @@ SIGNATURES = {
     "gpt2_q8_capture_nbytes": (_sz, []),
     "gpt2_test_force_phase_kernels": (None, [_i]),
     "gpt2_test_fused_trace": (None, [_vp]),
-    "gpt2_test_fused_plain_launch": (None, [_i]),
     "gpt2_workspace_status": (_i, [_vp]),
     "gpt2_q8_capture_offsets": (_i, [_i, _i] + [ctypes.POINTER(_sz)] * 6),
     "gpt2_q8_cached_step_capture": (_i, [_vp, _vp, _sz, _u32, ctypes.c_int32, _vp, _vp, _vp, _vp]),
@@ -214,10 +213,6 @@ def gpt2_test_force_phase_kernels(on: bool) -> None:
 
 def gpt2_test_fused_trace(trace_dev) -> None:
     lib().gpt2_test_fused_trace(trace_dev)
-
-
-def gpt2_test_fused_plain_launch(on: bool) -> None:
-    lib().gpt2_test_fused_plain_launch(1 if on else 0)
 
 
 def gpt2_workspace_status(ws_host_copy: bytes) -> int:

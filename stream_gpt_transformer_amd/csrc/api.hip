@@ -278,7 +278,6 @@ int gpt2_test_gemm_bias(const float* A, const float* W, const float* bias, float
 void gpt2_test_force_phase_kernels(int on) { g_force_phase_kernels = on != 0; }
 
 void gpt2_test_fused_trace(void* trace_dev) { g_fused_trace = (uint64_t*)trace_dev; }
-void gpt2_test_fused_plain_launch(int on) { g_fused_plain_launch = on != 0; }
 
 int gpt2_workspace_status(const void* ws_host_copy) {
   return ws_host_copy ? (int)((const uint32_t*)ws_host_copy)[2] : 0;

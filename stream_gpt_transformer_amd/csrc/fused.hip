@@ -1138,7 +1138,6 @@ struct FusedConfig {
 };
 static FusedConfig g_cfg[7][64];
 uint64_t* g_fused_trace = nullptr;  // timeline test hook
-int g_fused_plain_launch = 1;       // 1: ordinary launch (default), 0: cooperative launch
 
 template <bool Q8, bool CAP, bool TOKP, bool H16>
 static hipError_t fused_config(FusedConfig& c) {
@@ -1179,12 +1178,16 @@ static hipError_t launch_fused_t(const Weights& w, const Work& k, uint32_t token
   a.trace = g_fused_trace;
   a.token = token;
   a.pos = pos;
+  // An ordinary launch of one workgroup per compute unit.  The waits between
+  // workgroups need all 256 resident at once: fused_config admits the kernel only on
+  // a device of exactly 256 compute units that fits one workgroup per unit (the LDS
+  // size allows at most one), so on an otherwise idle GPU the dispatcher places all of
+  // them at once.  If another kernel holds compute units (a GPU shared with other
+  // work), a workgroup can wait for a unit that never frees: the waits then give up
+  // after their bound, the error word is set and the step's outputs are invalid,
+  // while the call itself has returned GPT2_OK.
   void* args[] = {&a};
-  if (g_fused_plain_launch)
-    e = hipLaunchKernel((const void*)k_fused<Q8, CAP, TOKP, H16>, dim3(GRID), dim3(FT), args, sizeof(FusedSmem), s);
-  else
-    e = hipLaunchCooperativeKernel((const void*)k_fused<Q8, CAP, TOKP, H16>, dim3(GRID), dim3(FT), args,
-                                   sizeof(FusedSmem), s);
+  e = hipLaunchKernel((const void*)k_fused<Q8, CAP, TOKP, H16>, dim3(GRID), dim3(FT), args, sizeof(FusedSmem), s);
   if (e == hipSuccess) *used = true;
   return e;
 }

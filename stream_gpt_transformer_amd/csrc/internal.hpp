@@ -85,7 +85,6 @@ hipError_t launch_fused(WFmt f, const Weights& w, const Work& k, uint32_t token,
                         float* logits, char* capture, hipStream_t s, bool* used, bool device_token = false);
 extern bool g_force_phase_kernels;
 extern uint64_t* g_fused_trace;
-extern int g_fused_plain_launch;
 hipError_t launch_special_bits(int kind, uint32_t first, long long n, float* y, hipStream_t s);
 hipError_t launch_layernorm_seq(const float* x, int rows, const float* gamma, const float* beta, float* y,
                                 hipStream_t s);
