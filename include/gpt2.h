@@ -202,6 +202,27 @@ int gpt2_batched_cached_step(const gpt2_model* model, float* caches_dev, size_t 
                              const int32_t* positions_host, int B, void* ws_dev, float* logits_dev,
                              void* stream);
 
+/* gpt2_cached_step for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): no
+ * workspace argument and no allocation of any kind.  The step's scratch (its header
+ * and exchange area, GPT2_NOALLOC_SCRATCH_BYTES) is a static device array of the
+ * library, one copy per GPU, held until the process ends; the first call on a GPU
+ * looks up that GPU's copy.  Every call on one GPU shares it, so calls that overlap
+ * on one GPU (several streams, several threads) race and give invalid results:
+ * order them on one stream.  A batch-1 step needs a fixed amount of scratch, so no
+ * input can exceed it; position is limited to 0..127 as for gpt2_cached_step.
+ *  status_dev : device int32, or NULL.  Receives the step's error word (0 = fine,
+ *               1 = a wait inside the step gave up, 2 = the workgroups were not
+ *               dealt round-robin over the XCDs; then the logits are invalid).  The
+ *               word is cleared after every call, so one failed call does not spoil
+ *               the next.
+ * The other arguments, the errors and the results are those of gpt2_cached_step
+ * (same logits and cache, bit for bit).  The step must run as the single-launch
+ * kernel (an MI355X with all 256 compute units free): GPT2_EHIP where it cannot. */
+#define GPT2_NOALLOC_SCRATCH_BYTES 6555904u
+int gpt2_cached_step_noalloc(const gpt2_model* model, float* cache_dev, size_t cache_nwords, uint32_t token,
+                             int32_t position, float* logits_dev, int32_t* status_dev, void* stream);
+
 /* infer (LeanExe GPT-2 README, infer paragraph): recompute a prefix of n = 1..128
  * tokens (host array; GPT2_ETOKEN for n outside 1..128 or any id >= 50,257) and
  * write the final row's 50,257 logits.  Needs GPT2_PACK_F32. */

@@ -26,6 +26,7 @@ GPT2_CKPT_WORDS = 124_439_808
 GPT2_CKPT_BYTES = 497_759_232
 GPT2_CACHE_WORDS_PER_POS = 18_432
 GPT2_MAX_BATCH = 64
+GPT2_NOALLOC_SCRATCH_BYTES = 6_555_904
 GPT2_PACK_F32 = 1
 GPT2_PACK_Q8 = 2
 GPT2_PACK_F16 = 4
@@ -49,6 +50,7 @@ SIGNATURES = {
     "gpt2_pack_weights_grouped": (_i, [_vp, _sz, _vp, _sz, _i, _i, _vp, ctypes.POINTER(_vp)]),
     "gpt2_q8_weight_group": (_i, [_vp]),
     "gpt2_batched_cached_step": (_i, [_vp, _vp, _sz, _vp, _vp, _vp, _i, _vp, _vp, _vp]),
+    "gpt2_cached_step_noalloc": (_i, [_vp, _vp, _sz, _u32, ctypes.c_int32, _vp, _vp, _vp]),
     "gpt2_infer": (_i, [_vp, _vp, _i, _vp, _vp, _vp]),
     "gpt2_generate": (_i, [_vp, _vp, _sz, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "gpt2_prefill": (_i, [_vp, _vp, _i, _vp, _sz, _vp, _vp, _vp]),
@@ -143,6 +145,12 @@ def gpt2_cached_step(model, cache_dev, cache_nwords, token, position, ws_dev, lo
 def gpt2_q8_cached_step(model, cache_dev, cache_nwords, token, position, ws_dev, logits_dev, stream=0) -> int:
     return lib().gpt2_q8_cached_step(model, cache_dev, cache_nwords, token & 0xFFFFFFFF, position, ws_dev,
                                      logits_dev, stream)
+
+
+def gpt2_cached_step_noalloc(model, cache_dev, cache_nwords, token, position, logits_dev, status_dev=None,
+                             stream=0) -> int:
+    return lib().gpt2_cached_step_noalloc(model, cache_dev, cache_nwords, token & 0xFFFFFFFF, position,
+                                          logits_dev, status_dev, stream)
 
 
 def gpt2_f16_cached_step(model, cache_dev, cache_nwords, token, position, ws_dev, logits_dev, stream=0) -> int:

@@ -1,6 +1,7 @@
 // C-ABI of the library: host-side validation, the model handle and dispatch to the
 // kernel launchers.  Entry points and their input rules follow the LeanExe GPT-2
 // README (infer and cachedStep paragraphs) and the marXiv 2609.00018 abstract.
+#include <mutex>
 #include <new>
 
 #include "../../include/gpt2.h"
@@ -193,6 +194,67 @@ int gpt2_q8_cached_step_grouped(const gpt2_model* m, int input_group, float* cac
 }
 
 int gpt2_q8_weight_group(const gpt2_model* m) { return m ? m->q8_group : -1; }
+
+// ---- gpt2_cached_step_noalloc: the batch-1 fp32 step without a caller workspace ----
+// Its scratch is the single-launch step's header and exchange area, in a file-scope
+// device array: each GPU the library runs on holds its own copy until the process
+// ends.  In host code `scratch` names a host-side stand-in, not device memory, so the
+// kernels get the address hipGetSymbolAddress returns for the current device.  The
+// code-object loader zero-fills the array (an uninitialised ELF section), which is
+// the state a fresh workspace must start in: epoch 0 in the header and in every
+// exchange word.  After that each launch keeps it consistent by itself (the last
+// workgroup resets the finished counter, advances the epoch and, here, reports and
+// clears the error word), so no call clears anything.
+}  // extern "C"
+constexpr size_t NOALLOC_SCRATCH_BYTES = 256 + FX_WORDS * 8;  // header + exchange area, 6,555,904 B
+static_assert(NOALLOC_SCRATCH_BYTES == GPT2_NOALLOC_SCRATCH_BYTES, "declared size");
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+namespace {
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_noalloc_mu;
+void* g_noalloc_ptr[NOALLOC_MAX_DEVICES];
+
+// The current device's copy of the scratch: looked up once per device, with that
+// device current (the first call on it), then kept.
+hipError_t noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_noalloc_ptr[dev] = p;
+  }
+  *out = g_noalloc_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+extern "C" {
+
+int gpt2_cached_step_noalloc(const gpt2_model* m, float* cache, size_t cache_nwords, uint32_t token, int32_t pos,
+                             float* logits, int32_t* status, void* stream) {
+  if (!m) return GPT2_EARG;
+  if (!(m->flags & GPT2_PACK_F32)) return GPT2_ENOTPACKED;
+  if (token >= (uint32_t)V) return GPT2_ETOKEN;
+  if (pos < 0 || pos >= PMAX) return GPT2_EPOSITION;
+  if (!cache || !aligned16(cache) || cache_nwords != (size_t)pos * CACHE_POS) return GPT2_ECACHE;
+  if (!logits || !aligned4(logits) || (status && !aligned4(status))) return GPT2_EARG;
+  void* p = nullptr;
+  if (noalloc_scratch(&p) != hipSuccess) return GPT2_EHIP;
+  Work k{};
+  k.header = (uint32_t*)p;
+  k.ll = (unsigned long long*)((char*)p + 256);
+  k.self_clearing = true;
+  k.step_status = status;
+  bool used = false;
+  if (launch_fused(WF_F32, m->w, k, token, pos, cache, logits, nullptr, (hipStream_t)stream, &used) != hipSuccess)
+    return GPT2_EHIP;
+  return used ? GPT2_OK : GPT2_EHIP;
+}
 
 int gpt2_q8_cached_step_capture(const gpt2_model* m, float* cache, size_t cache_nwords, uint32_t token,
                                 int32_t pos, void* ws, float* logits, void* capture, void* stream) {

@@ -120,8 +120,10 @@ struct FusedArgs {
   uint32_t* header;
   char* capture;     // int8 test capture or null
   uint64_t* trace;   // timeline test hook or null: [grid][64] timestamps
+  int32_t* status_out;  // with clear_error: receives the launch's error word (may be null)
   uint32_t token;
   int32_t pos;
+  uint32_t clear_error;  // 1: the last workgroup reports the error word and clears it
 };
 
 // Timeline test hook (100 MHz wall clock), per workgroup: 0 start; for block l
@@ -1125,6 +1127,13 @@ __global__ __launch_bounds__(FT, 1) void k_fused(const FusedArgs a) {
     bad = __syncthreads_or(bad);
     if (threadIdx.x == 0) {
       if (bad) set_error(hdr, ERR_XCC);
+      // Every other workgroup has finished (and with it every wait that could set the
+      // word), so a scratch shared by all calls can start the next launch clean.
+      if (a.clear_error) {
+        const uint32_t err = ld32(&hdr[HDR_ERROR]);
+        if (a.status_out) *a.status_out = (int32_t)err;
+        __hip_atomic_store(&hdr[HDR_ERROR], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       hdr[HDR_DONE] = 0;
       __hip_atomic_store(&hdr[HDR_EPOCH], c.E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -1176,6 +1185,8 @@ static hipError_t launch_fused_t(const Weights& w, const Work& k, uint32_t token
   a.header = k.header;
   a.capture = capture;
   a.trace = g_fused_trace;
+  a.status_out = k.step_status;
+  a.clear_error = k.self_clearing ? 1u : 0u;
   a.token = token;
   a.pos = pos;
   // An ordinary launch of one workgroup per compute unit.  The waits between

@@ -51,6 +51,10 @@ struct Work {
   float* g;    // [B][F]
   unsigned long long* ll;
   float *pf_x, *pf_h, *pf_qkv, *pf_att, *pf_u, *pf_part;
+  // A workspace that every call shares (the library's own scratch): the single-launch
+  // step reports its error word into step_status (device, may be null) and clears it.
+  bool self_clearing;
+  int32_t* step_status;
 };
 
 Work work_ptrs(void* ws, int max_batch);

@@ -90,6 +90,7 @@ def test_step_validation_without_model():
     for grp in (32, 96, 1536, 3072, -64):
         rc, h = g.gpt2_pack_weights_grouped(FAKE, g.GPT2_CKPT_BYTES, FAKE, 1 << 40, g.GPT2_PACK_Q8, grp)
         assert rc == g.GPT2_EARG and h is None
+    assert g.gpt2_cached_step_noalloc(None, FAKE, 0, 0, 0, FAKE) == g.GPT2_EARG
     assert g.gpt2_infer(None, [1, 2], FAKE, FAKE) == g.GPT2_EARG
     assert g.gpt2_batched_cached_step(None, FAKE, 18432, [0], [0], [0], FAKE, FAKE) == g.GPT2_EARG
 
