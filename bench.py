@@ -234,6 +234,14 @@ def _block_phases(tr):
     head_in, head_done, end = med(49, allu), float(t[:, 50].max()), float(t[:, 51].max())
     for l in range(12):
         rows[l]["next"] = rows[l + 1]["in"] if l < 11 else head_in
+    # inside block 6 (set 0): regular units' wave 0 (52 own reduce-scatter share polled, 53
+    # all terms in LDS, 54 x published, 56 x1 published) and wave 1 (59 after the QKV
+    # barrier, 60 LayerNorm output loaded, 62 MLP phase start, 63 MLP partials
+    # published); head units' wave 0 (52 terms in LDS, 53 x published, 54 q/k/v
+    # received, 56 output-projection terms published)
+    det = {f"r{k}": med(k, reg[0]) for k in (52, 53, 54, 56, 59, 60, 62, 63)}
+    det.update({f"h{k}": med(k, head[0]) for k in (52, 53, 54, 56)})
+    rows.append(det)
     return rows, head_in, head_done, end
 
 
@@ -259,6 +267,7 @@ def timeline_report(g, m, call, filled_cache, stream, positions, reps) -> int:
                 runs.append(_block_phases(trace.view(NGRID, 64).cpu().numpy()))
             keys = ("in", "qkv", "att", "x1", "g", "next")
             rows = [{k: float(np.median([r[0][l][k] for r in runs])) for k in keys} for l in range(12)]
+            det = {k: float(np.median([r[0][12][k] for r in runs])) for k in runs[0][0][12]}
             head_in = float(np.median([r[1] for r in runs]))
             head_done = float(np.median([r[2] for r in runs]))
             end = float(np.median([r[3] for r in runs]))
@@ -278,7 +287,16 @@ def timeline_report(g, m, call, filled_cache, stream, positions, reps) -> int:
                   f"{seg['next']:.2f} | {float(np.mean(blk)):.2f} |\n")
             print(f"- start -> block 0 input: {rows[0]['in']:.2f} us; head input at {head_in:.2f} us; "
                   f"head rows done {head_done:.2f} us (head {head_done - head_in:.2f} us); last workgroup ends "
-                  f"{end:.2f} us\n")
+                  f"{end:.2f} us")
+            b6 = rows[6]["in"]
+            print("- inside block 6, us after its x is in LDS (previous block's MLP terms polled -> next input): "
+                  f"regular wave 0: own reduce-scatter share polled {det['r52'] - b6:.2f}, all terms in LDS "
+                  f"{det['r53'] - b6:.2f}, x published {det['r54'] - b6:.2f}, x1 published {det['r56'] - b6:.2f}; "
+                  f"regular wave 1: after QKV barrier {det['r59'] - b6:.2f}, LayerNorm output loaded "
+                  f"{det['r60'] - b6:.2f}, MLP phase start {det['r62'] - b6:.2f}, MLP partials published "
+                  f"{det['r63'] - b6:.2f}; head wave 0: terms in LDS {det['h52'] - b6:.2f}, x published "
+                  f"{det['h53'] - b6:.2f}, q/k/v received {det['h54'] - b6:.2f}, output-projection terms published "
+                  f"{det['h56'] - b6:.2f}\n")
         # per-position step time over the session (events around each launch), median of 3 passes
         per = np.zeros((3, NPOS))
         for rep in range(3):

@@ -521,6 +521,8 @@ __device__ __forceinline__ void layernorm_lds(const float* xs, const float* __re
 // for its outstanding global loads and stores (a __syncthreads would also wait for
 // every store of the wave to be acknowledged).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// This wave's LDS writes are complete before its later LDS reads (of other lanes' words).
+__device__ __forceinline__ void wave_lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // ---- attention (one session, one head) --------------------------------------
 // fp32 path, npos keys (1..128):
@@ -653,49 +655,163 @@ __device__ __forceinline__ float attn_compute(AttnSmem& sm, int npos, int nthr) 
   return acc;
 }
 
-// The int8 path's attention, in the oracle's order (its output is quantized, so
-// it must not depend on a reduction tree): s_t as above; m = max_t s_t;
-// e_t = exp_spec(s_t - m); Z = ((0 + e_0) + e_1) + ... ; w_t = e_t / Z;
-// a_d = ((0 + w_0*V_0,d) + w_1*V_1,d) + ... .  Wave 0 runs the two ordered sums.
-// Same calling rules as attn_compute.
+// ---- the int8 path's attention, in the oracle's order -------------------------
+// Its output is quantized, so it must not depend on a reduction tree:
+//   s_t = (((0 + q_0*K_t,0) + q_1*K_t,1) + ... + q_63*K_t,63) * 0.125;  m = max_t s_t;
+//   e_t = exp_spec(s_t - m);  Z = ((0 + e_0) + e_1) + ... ;  w_t = e_t / Z;
+//   a_d = ((0 + w_0*V_0,d) + w_1*V_1,d) + ... .
+// s + t[0] + ... + t[31] in order (t in LDS, 32 values in flight).
+__device__ __forceinline__ float seq_chain32(float s, const float* t) {
+  f4 a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = *(const f4*)(t + 4 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = *(const f4*)(t + 16 + 4 * i);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { s = s + a[i].x; s = s + a[i].y; s = s + a[i].z; s = s + a[i].w; }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { s = s + b[i].x; s = s + b[i].y; s = s + b[i].z; s = s + b[i].w; }
+  return s;
+}
+// binary64 inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ double wave_scan_d(double p) {
+  p = p + dpp_d0<0x111, 0xf>(p);  // row_shr:1
+  p = p + dpp_d0<0x112, 0xf>(p);  // row_shr:2
+  p = p + dpp_d0<0x114, 0xf>(p);  // row_shr:4
+  p = p + dpp_d0<0x118, 0xf>(p);  // row_shr:8
+  p = p + dpp_d0<DPP_ROW_BCAST15, 0xa>(p);
+  p = p + dpp_d0<DPP_ROW_BCAST31, 0xc>(p);
+  return p;
+}
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)b, l), hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+  return __longlong_as_double(((long long)hi << 32) | (uint32_t)lo);
+}
+// Z = ((0 + w[0]) + w[1]) + ... + w[127] for nonnegative w (LDS; w[64j + lane] = e_j in
+// the calling wave), by one wave, bit for bit the loop: lane 16k + c runs segment k
+// (w[32k..32k+31]) from the binary32 value c - 8 steps away from the binary64 prefix
+// estimate E_k of its start (nonnegative values order as their bit patterns), then a
+// walk over the four segments takes the chain that started at the true running sum.
+// The walk has no branches; if a true start lies outside its segment's candidates the
+// walk runs again, taking such a segment's chain from the running sum itself.
+__device__ __forceinline__ float seq_sum128_pos(const float* w, float e0, float e1) {
+  const int lane = (int)(threadIdx.x & 63);
+  const double p0 = wave_scan_d((double)e0), p1 = wave_scan_d((double)e1);
+  const double h0 = readlane_d(p0, 31), t0 = readlane_d(p0, 63), h1 = readlane_d(p1, 31);
+  const int eb1 = __float_as_int((float)h0), eb2 = __float_as_int((float)t0), eb3 = __float_as_int((float)(t0 + h1));
+  const int k = lane >> 4, c = lane & 15;
+  const int ek = k == 0 ? 0 : k == 1 ? eb1 : k == 2 ? eb2 : eb3;
+  const float res = seq_chain32(__int_as_float(ek + c - 8), w + 32 * k);
+  const uint32_t eb[4] = {0u, (uint32_t)eb1, (uint32_t)eb2, (uint32_t)eb3};
+  uint32_t sb = 0, miss = 0;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const uint32_t dd = sb - eb[s] + 8u;
+    miss |= (uint32_t)(dd >= 16u);
+    sb = (uint32_t)__builtin_amdgcn_readlane(__float_as_int(res), 16 * s + (int)(dd & 15u));
+  }
+  if (__builtin_expect(miss != 0, 0)) {
+    sb = 0;
+#pragma unroll 1
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t dd = sb - eb[s] + 8u;
+      if (dd < 16u)
+        sb = (uint32_t)__builtin_amdgcn_readlane(__float_as_int(res), 16 * s + (int)dd);
+      else
+        sb = (uint32_t)__builtin_amdgcn_readfirstlane(__float_as_int(seq_chain32(__uint_as_float(sb), w + 32 * s)));
+    }
+  }
+  return __uint_as_float(sb);
+}
+// Threads t < npos score key t (threads 0..127: at least two waves); after one LDS
+// barrier wave 0 alone takes the softmax, Z, the weights and the ordered weighted
+// sums.  Returns a_d in the threads of wave 0 (d = lane), 0 elsewhere.  Every thread
+// of the block (128 or more) must call it.  sm.w is overwritten; the caller
+// synchronises before sm is written again.
 __device__ __forceinline__ float attn_compute_seq(AttnSmem& sm, int npos) {
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
-  const bool act = t < 128;
-  float s = -INFINITY;
-  if (act && t < npos) {
-    float acc = 0.0f;
-#pragma unroll 4
-    for (int i = 0; i < DH / 4; ++i) {
-      const f4 kr = *(const f4*)&sm.k[t][4 * i];
-      const f4 qq = *(const f4*)&sm.q[4 * i];
-      acc = acc + qq.x * kr.x;
-      acc = acc + qq.y * kr.y;
-      acc = acc + qq.z * kr.z;
-      acc = acc + qq.w * kr.w;
+  if (t < PMAX) {
+    float s = -INFINITY;
+    if (t < npos) {
+      // 16 key and query values in flight while the previous 16 are added
+      float acc = 0.0f;
+      f4 ka[4], qa[4], kb[4], qb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ka[i] = *(const f4*)&sm.k[t][4 * i];
+        qa[i] = *(const f4*)&sm.q[4 * i];
+      }
+#pragma unroll
+      for (int bb = 0; bb < 4; bb += 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          kb[i] = *(const f4*)&sm.k[t][16 * (bb + 1) + 4 * i];
+          qb[i] = *(const f4*)&sm.q[16 * (bb + 1) + 4 * i];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc = acc + qa[i].x * ka[i].x;
+          acc = acc + qa[i].y * ka[i].y;
+          acc = acc + qa[i].z * ka[i].z;
+          acc = acc + qa[i].w * ka[i].w;
+        }
+        if (bb + 2 < 4) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            ka[i] = *(const f4*)&sm.k[t][16 * (bb + 2) + 4 * i];
+            qa[i] = *(const f4*)&sm.q[16 * (bb + 2) + 4 * i];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc = acc + qb[i].x * kb[i].x;
+          acc = acc + qb[i].y * kb[i].y;
+          acc = acc + qb[i].z * kb[i].z;
+          acc = acc + qb[i].w * kb[i].w;
+        }
+      }
+      s = acc * 0.125f;
     }
-    s = acc * 0.125f;
-  }
-  const float mw = wave_max(s);
-  if (act && lane == 0) sm.red[wv] = mw;
-  lds_barrier();
-  const float m = fmaxf(sm.red[0], sm.red[1]);
-  const float e = (act && t < npos) ? exp_spec(s - m) : 0.0f;
-  if (act) sm.w[t] = e;
-  lds_barrier();
-  if (wv == 0) {
-    float Z = 0.0f;
-#pragma unroll 16
-    for (int j = 0; j < npos; ++j) Z = Z + sm.w[j];
-    if (lane == 0) sm.red[2] = Z;
+    sm.w[t] = s;
   }
   lds_barrier();
-  if (act && t < npos) sm.w[t] = e / sm.red[2];
-  lds_barrier();
+  if (wv != 0) return 0.0f;
+  const float s0 = sm.w[lane], s1 = sm.w[64 + lane];
+  const float m = fmaxf(wave_max(s0), wave_max(s1));
+  const float e0 = lane < npos ? exp_spec(s0 - m) : 0.0f;
+  const float e1 = 64 + lane < npos ? exp_spec(s1 - m) : 0.0f;
+  sm.w[lane] = e0;
+  sm.w[64 + lane] = e1;
+  wave_lds_wait();
+  float Z;
+  if (npos <= 48) {
+    // the slots past npos hold +0, which leaves a nonnegative running sum unchanged
+    Z = 0.0f;
+    for (int j = 0; j < npos; j += 8) {
+      const f4 a = *(const f4*)&sm.w[j], b = *(const f4*)&sm.w[j + 4];
+      Z = Z + a.x; Z = Z + a.y; Z = Z + a.z; Z = Z + a.w;
+      Z = Z + b.x; Z = Z + b.y; Z = Z + b.z; Z = Z + b.w;
+    }
+  } else {
+    Z = seq_sum128_pos(sm.w, e0, e1);
+  }
+  sm.w[lane] = e0 / Z;
+  sm.w[64 + lane] = e1 / Z;
+  wave_lds_wait();
   float acc = 0.0f;
-  if (wv == 0) {
-#pragma unroll 16
-    for (int j = 0; j < npos; ++j) acc = acc + sm.w[j] * sm.v[j][lane];
+  int j = 0;
+  for (; j + 8 <= npos; j += 8) {
+    const f4 wa = *(const f4*)&sm.w[j], wb = *(const f4*)&sm.w[j + 4];
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = sm.v[j + u][lane];
+    acc = acc + wa.x * v[0]; acc = acc + wa.y * v[1]; acc = acc + wa.z * v[2]; acc = acc + wa.w * v[3];
+    acc = acc + wb.x * v[4]; acc = acc + wb.y * v[5]; acc = acc + wb.z * v[6]; acc = acc + wb.w * v[7];
   }
+  for (; j < npos; ++j) acc = acc + sm.w[j] * sm.v[j][lane];
   return acc;
 }
 

@@ -590,18 +590,24 @@ template <bool Q8>
 __device__ __forceinline__ void rs_pr_poll(const FusedArgs& a, FusedSmem& S, const Ctx& c, int l, int wave) {
   rs_poll_part<Q8 ? NG_PR : NX>(glb_of(c, l) + GL_P, c.q, c.E, S.rs, a.header, wave);
 }
-template <bool Q8, bool CAP>
-__device__ __forceinline__ float rs_pr(const FusedArgs& a, FusedSmem& S, const Ctx& c, int l, float bpr) {
-  const int lane = lane_id();
-  float y = rs_sum<Q8 ? NG_PR : NX>(S.rs);
+// The unit's share of x1 of block l (lanes < RSN), published inside the XCD in the
+// middle of block l: the wave that takes the reduce-scatter reads it before it polls
+// the MLP terms, so this read is off the path that waits for them.
+__device__ __forceinline__ float x1_share(const FusedArgs& a, const Ctx& c, int l) {
   float x1[1];
   poll<1, true>(loc_of(c, l) + LO_X1 + RSN * c.q, RSN, [](int k) { return k; }, c.E, x1, a.header);
+  return x1[0];
+}
+template <bool Q8, bool CAP>
+__device__ __forceinline__ float rs_pr(const FusedArgs& a, FusedSmem& S, const Ctx& c, int l, float bpr, float x1) {
+  const int lane = lane_id();
+  float y = rs_sum<Q8 ? NG_PR : NX>(S.rs);
   float xr = 0.0f;
   if (lane < RSN) {
     const int o = RSN * c.q + lane;
     y = y + bpr;
     if (CAP && c.X == 0) ((float*)(a.capture + cap_offset(l, M_PR) + cap_item(M_PR).y))[o] = y;
-    xr = x1[0] + y;
+    xr = x1 + y;
     st_loc(loc_of(c, l) + LO_X2 + o, pack(xr, c.E));
   }
   return xr;
@@ -704,14 +710,18 @@ __device__ __forceinline__ void regular_io(const FusedArgs& a, FusedSmem& S, con
   wg_barrier();  // B0
   for (int l = l0; l < L; l += 2) {
     u64* loc = loc_of(c, l);
-    if (l > 0) rs_pr_poll<Q8>(a, S, c, l - 1, 0);
+    float x1p = 0.0f;
+    if (l > 0) {
+      x1p = x1_share(a, c, l - 1);
+      rs_pr_poll<Q8>(a, S, c, l - 1, 0);
+    }
     dstamp(a.trace, l, 52);
     wg_barrier();  // BA: the reduce-scatter terms are in LDS
     dstamp(a.trace, l, 53);
     if (l == 0) {
       xr = embed<TOKP>(a, S.xs, c.q);
     } else {
-      xr = rs_pr<Q8, CAP>(a, S, c, l - 1, bpr);
+      xr = rs_pr<Q8, CAP>(a, S, c, l - 1, bpr, x1p);
       dstamp(a.trace, l, 54);
       gather<12>(loc_of(c, l - 1) + LO_X2, E, S.xs, hdr);
     }
@@ -761,9 +771,13 @@ __device__ __forceinline__ void regular_io(const FusedArgs& a, FusedSmem& S, con
     if (ln - 1 < L) bpr = small_p(a.w, ln - 1, sp::B_PR)[o];
   }
   // the tied head: set 0 reduces block 11's MLP projection, both gather x12
-  if (c.set == 0) rs_pr_poll<Q8>(a, S, c, L - 1, 0);
+  float x1p = 0.0f;
+  if (c.set == 0) {
+    x1p = x1_share(a, c, L - 1);
+    rs_pr_poll<Q8>(a, S, c, L - 1, 0);
+  }
   wg_barrier();  // BT
-  if (c.set == 0) rs_pr<Q8, CAP>(a, S, c, L - 1, bpr);
+  if (c.set == 0) rs_pr<Q8, CAP>(a, S, c, L - 1, bpr, x1p);
   gather<12>(loc_of(c, L - 1) + LO_X2, E, S.xs, hdr);
   if (lane == 0) stamp(a.trace, 49);
 }
@@ -943,13 +957,15 @@ __device__ __forceinline__ void head_unit(const FusedArgs& a, FusedSmem& S, cons
   wg_barrier();
   for (int l = l0; l < L; l += 2) {
     u64* glb = glb_of(c, l) + GL_O + (size_t)h * D;
+    float x1p = 0.0f;
     if (l > 0) {
+      if (wave == 0) x1p = x1_share(a, c, l - 1);
       rs_pr_poll<Q8>(a, S, c, l - 1, wave);
       wg_barrier();
     }
     if (wave == 0) {
       dstamp(a.trace, l, 52);
-      xr = l == 0 ? embed<TOKP>(a, nullptr, c.q) : rs_pr<Q8, CAP>(a, S, c, l - 1, bpr);
+      xr = l == 0 ? embed<TOKP>(a, nullptr, c.q) : rs_pr<Q8, CAP>(a, S, c, l - 1, bpr, x1p);
       if (lane == 0) stamp(a.trace, 1 + 4 * l);
       float v[3];
       poll<3, true>(loc_of(c, l) + LO_QKV + 192 * c.q, 192, [](int k) { return k; }, E, v, hdr);
@@ -1048,10 +1064,14 @@ __device__ __forceinline__ void head_unit(const FusedArgs& a, FusedSmem& S, cons
     }
     wg_barrier();
   }
-  if (c.set == 0) rs_pr_poll<Q8>(a, S, c, L - 1, wave);
+  float x1p = 0.0f;
+  if (c.set == 0) {
+    if (wave == 0) x1p = x1_share(a, c, L - 1);
+    rs_pr_poll<Q8>(a, S, c, L - 1, wave);
+  }
   wg_barrier();
   if (wave == 0) {
-    if (c.set == 0) rs_pr<Q8, CAP>(a, S, c, L - 1, bpr);
+    if (c.set == 0) rs_pr<Q8, CAP>(a, S, c, L - 1, bpr, x1p);
     gather<12>(loc_of(c, L - 1) + LO_X2, E, S.xs, hdr);
     if (lane == 0) stamp(a.trace, 49);
   }
