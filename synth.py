@@ -19,6 +19,13 @@ order): N(0, 0.02) for wte, wpe and the four block matrices; LayerNorm gamma = 1
 beta = 0 and every bias 0 in the plain recipe.  The "robust" recipe also draws
 biases ~ N(0, 0.02), gamma ~ 1 + N(0, 0.1) and beta ~ N(0, 0.02) so that offset
 mistakes hidden by zeros and ones surface.
+
+The "peaked" recipe takes the plain draw and multiplies the query and key columns
+of every block's attn_w by PEAK_QK_SCALE (10), so attention scores spread over
+tens of units instead of N(0, 0.3^2): softmax weights are close to one-hot and the
+exponential's argument falls below -87 (where it underflows to 0) for most keys.
+It also copies position row 5 into rows 9 and 17, so a token repeated at
+positions 5, 9 and 17 gives identical layer-0 keys there (tied scores).
 """
 from __future__ import annotations
 
@@ -90,8 +97,25 @@ def offsets(d: Dims = GPT2) -> Dict[str, Tuple[int, int]]:
     return {name: (off, n) for name, off, n, _ in layout(d)}
 
 
-def make_checkpoint(seed: int = 0, d: Dims = GPT2, robust: bool = False) -> np.ndarray:
+PEAK_QK_SCALE = 10.0
+PEAK_TIED_POSITIONS = (5, 9, 17)
+
+
+def make_checkpoint(seed: int = 0, d: Dims = GPT2, robust: bool = False, peaked: bool = False) -> np.ndarray:
     """Packed little-endian float32 checkpoint (numpy float32 is little-endian here)."""
+    if peaked:
+        w = make_checkpoint(seed, d, robust)
+        offs = offsets(d)
+        D = d.d_model
+        for l in range(d.n_layer):
+            off, n = offs[f"h{l}.attn_w"]
+            m = w[off:off + n].reshape(D, 3 * D)  # [input][q | k | v]
+            m[:, :2 * D] *= np.float32(PEAK_QK_SCALE)
+        wpe_off, _ = offs["wpe"]
+        p0 = PEAK_TIED_POSITIONS[0]
+        for p in PEAK_TIED_POSITIONS[1:]:
+            w[wpe_off + p * D:wpe_off + (p + 1) * D] = w[wpe_off + p0 * D:wpe_off + (p0 + 1) * D]
+        return w
     rng = np.random.default_rng(seed)
     w = np.empty(ckpt_words(d), dtype="<f4")
     for name, off, n, kind in layout(d):
@@ -112,9 +136,20 @@ def make_tokens(seed: int, count: int, d: Dims = GPT2) -> np.ndarray:
     return np.random.default_rng(seed).integers(0, d.vocab, size=count, dtype=np.uint32)
 
 
+def make_tied_tokens(seed: int, count: int, d: Dims = GPT2) -> np.ndarray:
+    """make_tokens with the token at the first tied position repeated at the others
+    (with the peaked recipe's equal position rows, their layer-0 keys are equal)."""
+    t = make_tokens(seed, count, d)
+    for p in PEAK_TIED_POSITIONS[1:]:
+        if p < count:
+            t[p] = t[PEAK_TIED_POSITIONS[0]]
+    return t
+
+
 # Token seeds of the workloads: the 8-step session, the 128-step sessions (fp32 and
 # int8 use the same tokens), the 128-token prefill and the 64 batched sessions.
 SEED_SHORT = 100
 SEED_SESSION = 101
 SEED_PREFILL = 102
 SEED_BATCH_BASE = 1000
+SEED_PEAKED = 103

@@ -29,13 +29,13 @@ def need_gpu():
 
 
 @functools.lru_cache(maxsize=None)
-def checkpoint(seed: int = 0, robust: bool = False) -> np.ndarray:
-    return synth.make_checkpoint(seed, D, robust=robust)
+def checkpoint(seed: int = 0, robust: bool = False, peaked: bool = False) -> np.ndarray:
+    return synth.make_checkpoint(seed, D, robust=robust, peaked=peaked)
 
 
 @functools.lru_cache(maxsize=None)
-def model(seed: int = 0, robust: bool = False, flags: int = 3) -> g.Model:
-    ck = torch.from_numpy(checkpoint(seed, robust)).cuda()
+def model(seed: int = 0, robust: bool = False, flags: int = 3, peaked: bool = False) -> g.Model:
+    ck = torch.from_numpy(checkpoint(seed, robust, peaked)).cuda()
     m = g.Model(ck, flags)
     torch.cuda.synchronize()
     del ck

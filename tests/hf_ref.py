@@ -75,3 +75,19 @@ def build(w: np.ndarray, d: synth.Dims, f16: bool = False):
 def logits_all_positions(model, toks: np.ndarray) -> np.ndarray:
     ids = torch.from_numpy(np.asarray(toks, dtype=np.int64))[None, :]
     return model(input_ids=ids).logits[0].numpy()
+
+
+@torch.no_grad()
+def cache_all_positions(model, toks: np.ndarray, d: synth.Dims) -> np.ndarray:
+    """The float64 keys and values of every position and layer, in the cachedStep
+    layout: word (position*n_layer + layer)*2D + offset, keys then values."""
+    ids = torch.from_numpy(np.asarray(toks, dtype=np.int64))[None, :]
+    pkv = model(input_ids=ids, use_cache=True).past_key_values
+    T, D = len(toks), d.d_model
+    out = np.zeros((T, d.n_layer, 2 * D))
+    for l in range(d.n_layer):
+        lay = pkv.layers[l] if hasattr(pkv, "layers") else None
+        k, v = (lay.keys, lay.values) if lay is not None else pkv[l]
+        out[:, l, :D] = k[0].permute(1, 0, 2).reshape(T, D).numpy()   # [heads][T][dh] -> [T][heads*dh]
+        out[:, l, D:] = v[0].permute(1, 0, 2).reshape(T, D).numpy()
+    return out.reshape(-1)

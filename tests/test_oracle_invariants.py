@@ -70,6 +70,42 @@ def test_single_key_attention_returns_value_exactly():
         assert np.array_equal(a, V[0])
 
 
+def test_dominant_key_with_underflowing_rest_returns_its_value_exactly():
+    """Peaked scores: when every other score lies more than 87 below the largest, the
+    specified exponential returns exactly 0 for them, so Z = 1, the weights are one-hot
+    and the output is the dominant key's value row, bit for bit, wherever it sits."""
+    rng = np.random.default_rng(3)
+    for npos, top in ((2, 0), (17, 9), (128, 127), (100, 37)):
+        q = np.zeros(64, np.float32)
+        q[0] = 8.0
+        K = rng.standard_normal((npos, 64)).astype(np.float32)
+        K[:, 0] = -100.0 + rng.random(npos).astype(np.float32)  # scores (q.k)*0.125 near -100
+        K[top, 0] = 20.0                                        # score 20
+        V = rng.standard_normal((npos, 64)).astype(np.float32)
+        a, wts = oracle.attention_head(q, K, V)
+        expect = np.zeros(npos, np.float32)
+        expect[top] = 1.0
+        assert np.array_equal(wts, expect), (npos, top)
+        assert np.array_equal(a, V[top]), (npos, top)
+
+
+def test_tied_top_keys_share_the_weight():
+    """Two equal keys with the largest score: equal weights, each within rounding of 1/2
+    when the rest underflow."""
+    rng = np.random.default_rng(4)
+    q = np.zeros(64, np.float32)
+    q[0] = 8.0
+    K = rng.standard_normal((40, 64)).astype(np.float32)
+    K[:, 0] = -100.0
+    K[5, 0] = K[17, 0] = 20.0
+    K[17] = K[5]
+    V = rng.standard_normal((40, 64)).astype(np.float32)
+    a, wts = oracle.attention_head(q, K, V)
+    assert wts[5] == wts[17] == np.float32(0.5)
+    assert np.count_nonzero(wts) == 2
+    assert np.array_equal(a, (np.float32(0.5) * V[5]) + np.float32(0.5) * V[17])
+
+
 def test_softmax_mass_and_order():
     rng = np.random.default_rng(2)
     for npos in (2, 17, 128):

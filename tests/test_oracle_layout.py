@@ -58,3 +58,28 @@ def test_generator_recipe():
     toks = synth.make_tokens(100, 1000, d)
     assert toks.dtype == np.uint32 and toks.min() >= 0 and toks.max() < d.vocab
     assert np.array_equal(toks, synth.make_tokens(100, 1000, d))
+
+
+def test_peaked_recipe():
+    """The peaked variant is the plain draw with query/key columns times 10 and
+    position rows 5 = 9 = 17; the tied token stream repeats a token there."""
+    d = synth.TINY
+    base = synth.make_checkpoint(0, d)
+    pk = synth.make_checkpoint(0, d, peaked=True)
+    off = synth.offsets(d)
+    D = d.d_model
+    for name, (o, n) in off.items():
+        if name.endswith(".attn_w"):
+            m0, m1 = base[o:o + n].reshape(D, 3 * D), pk[o:o + n].reshape(D, 3 * D)
+            assert np.array_equal(m1[:, :2 * D], m0[:, :2 * D] * np.float32(synth.PEAK_QK_SCALE)), name
+            assert np.array_equal(m1[:, 2 * D:], m0[:, 2 * D:]), name
+        elif name == "wpe":
+            r0, r1 = base[o:o + n].reshape(-1, D), pk[o:o + n].reshape(-1, D)
+            p0 = synth.PEAK_TIED_POSITIONS[0]
+            for p in range(r0.shape[0]):
+                want = r0[p0] if p in synth.PEAK_TIED_POSITIONS else r0[p]
+                assert np.array_equal(r1[p], want), p
+        else:
+            assert np.array_equal(pk[o:o + n], base[o:o + n]), name
+    t = synth.make_tied_tokens(5, 20, d)
+    assert t[5] == t[9] == t[17]

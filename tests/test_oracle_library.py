@@ -25,6 +25,16 @@ def test_tiny_robust_session_matches_transformers(ckpt_tiny_robust):
 
 
 @pytest.mark.slow
+def test_tiny_robust_cache_matches_transformers_keys_values(ckpt_tiny_robust):
+    """The cache rows (position*layers + layer)*2D + offset hold the float64 library's
+    keys and values of that position and layer, within float32 rounding."""
+    d = synth.TINY
+    toks = synth.make_tokens(7, d.max_pos, d)
+    _, cache = oracle.session(d, ckpt_tiny_robust, toks)
+    ref = hf_ref.cache_all_positions(hf_ref.build(ckpt_tiny_robust, d), toks, d)
+    assert np.abs(cache.astype(np.float64) - ref).max() <= 1e-5
+
+
 def test_gpt2_seed0_eight_steps_match_transformers(ckpt_gpt2):
     d = synth.GPT2
     toks = synth.make_tokens(synth.SEED_SHORT, 8, d)
