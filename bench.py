@@ -232,6 +232,7 @@ def _block_phases(tr):
                      "x1": med(3 + 4 * l, reg[st]), "g": med(4 + 4 * l, reg[st])})
     allu = list(range(NGRID))
     head_in, head_done, end = med(49, allu), float(t[:, 50].max()), float(t[:, 51].max())
+    head_rows_start, head_preloaded = med(55, allu), med(57, allu)
     for l in range(12):
         rows[l]["next"] = rows[l + 1]["in"] if l < 11 else head_in
     # inside block 6 (set 0): regular units' wave 0 (52 own reduce-scatter share polled, 53
@@ -241,6 +242,7 @@ def _block_phases(tr):
     # received, 56 output-projection terms published)
     det = {f"r{k}": med(k, reg[0]) for k in (52, 53, 54, 56, 59, 60, 62, 63)}
     det.update({f"h{k}": med(k, head[0]) for k in (52, 53, 54, 56)})
+    det.update({"head_rows_start": head_rows_start, "head_preloaded": head_preloaded})
     rows.append(det)
     return rows, head_in, head_done, end
 
@@ -287,7 +289,8 @@ def timeline_report(g, m, call, filled_cache, stream, positions, reps) -> int:
                   f"{seg['next']:.2f} | {float(np.mean(blk)):.2f} |\n")
             print(f"- start -> block 0 input: {rows[0]['in']:.2f} us; head input at {head_in:.2f} us; "
                   f"head rows done {head_done:.2f} us (head {head_done - head_in:.2f} us); last workgroup ends "
-                  f"{end:.2f} us")
+                  f"{end:.2f} us; head rows start {det['head_rows_start']:.2f} us (after the final LayerNorm), "
+                  f"preloaded rows used by {det['head_preloaded']:.2f} us")
             b6 = rows[6]["in"]
             print("- inside block 6, us after its x is in LDS (previous block's MLP terms polled -> next input): "
                   f"regular wave 0: own reduce-scatter share polled {det['r52'] - b6:.2f}, all terms in LDS "

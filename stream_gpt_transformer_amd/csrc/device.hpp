@@ -871,6 +871,39 @@ __device__ __forceinline__ float q8_dot(const i4 (&wc)[(K + 1023) / 1024], float
   return y;
 }
 
+// The 768-input form of q8_dot with the weight scales in quad layout: lane l < 48
+// holds the row's codes at bytes 16l..16l+15 (group g = l/4) and swq, the row's
+// scale of group l/4 (0 in lanes 48..63, whose codes are 0).  acc[g] is the exact
+// quad sum in lanes 4g..4g+3, so t[g] is formed there and the fixed-order rescale
+// reads lane 4g: the same values and operations as q8_dot<768>, without moving the
+// group sums across lanes first.  cap_acc as for q8_dot.
+__device__ __forceinline__ float q8_dot768q(const i4 wc, float swq, const int8_t* xc, const float* xsc,
+                                            int32_t* cap_acc) {
+  const int lane = lane_id();
+  const i4 xv = *(const i4*)(xc + 16 * min(lane, 47));
+  int p = 0;
+  p = __builtin_amdgcn_sdot4(wc.x, xv.x, p, false);
+  p = __builtin_amdgcn_sdot4(wc.y, xv.y, p, false);
+  p = __builtin_amdgcn_sdot4(wc.z, xv.z, p, false);
+  p = __builtin_amdgcn_sdot4(wc.w, xv.w, p, false);
+  p = quad_sum(p);
+  if (cap_acc && lane < 48 && (lane & 3) == 0) cap_acc[lane >> 2] = p;
+  const float t = lane < 48 ? ((float)p * swq) * xsc[min(lane >> 2, 11)] : 0.0f;
+  float y = 0.0f;
+#pragma unroll
+  for (int g = 0; g < 12; ++g) y = y + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 4 * g));
+  return y;
+}
+// Codes of int8 row r of a [rows][768] matrix (lanes 48..63 zero) and its group
+// scales in quad layout, for q8_dot768q (nontemporal loads).
+__device__ __forceinline__ void q8_load_row768q(i4& wc, float& swq, const int8_t* codes, const float* scales, int r) {
+  const int lane = lane_id_fresh();
+  const i4 v = __builtin_nontemporal_load((const i4*)(codes + (size_t)r * 768 + 16 * min(lane, 47)));
+  wc = lane < 48 ? v : i4{0, 0, 0, 0};
+  const float sv = scales[(size_t)r * 12 + min(lane >> 2, 11)];
+  swq = lane < 48 ? sv : 0.0f;
+}
+
 // Load the codes and lane-g scale of int8 row r of a [rows][K] matrix (nontemporal).
 template <int K>
 __device__ __forceinline__ void q8_load_row(i4 (&wc)[(K + 1023) / 1024], float& swl, const int8_t* codes,

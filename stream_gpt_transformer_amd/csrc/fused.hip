@@ -135,6 +135,7 @@ struct FusedArgs {
 __device__ __forceinline__ void stamp(const uint64_t* trace, int slot) {
   if (trace) ((uint64_t*)trace)[blockIdx.x * 64 + slot] = __builtin_amdgcn_s_memrealtime();
 }
+// Head phase (wave 1): 55 head LayerNorm done (rows start), 57 the preloaded rows used.
 // Detail stamps 52..63 inside block 6 (set 0): regular wave 0: 52 own share of the
 // reduce-scatter polled, 53 terms of all waves in LDS, 54 x published, 56 x1
 // published; regular wave 1: 59 after the QKV barrier, 60 LayerNorm done, 62 MLP
@@ -257,8 +258,12 @@ __device__ __forceinline__ float rs_sum(const float* scratch) {
   const int lane = lane_id();
   float y = 0.0f;
   if (lane < RSN) {
-#pragma unroll 8
-    for (int t = 0; t < NT; ++t) y = y + scratch[t * RSN + lane];
+    // every term is read before the ordered adds, so the chain pays one LDS latency
+    float v[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) v[t] = scratch[t * RSN + lane];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) y = y + v[t];
   }
   return y;
 }
@@ -345,9 +350,7 @@ __device__ __forceinline__ void load_row768(WRegs<Q8, H16>& R, int slot, const W
   } else if constexpr (!Q8) {
     ld_row3(&R.r[3 * slot], f32_mat(w, l, m) + (size_t)r * D);
   } else {
-    i4 t[1];
-    q8_load_row<D>(t, R.sc[slot], q8_codes(w, l, m), q8_scales(w, l, m), r);
-    R.c[slot] = t[0];
+    q8_load_row768q(R.c[slot], R.sc[slot], q8_codes(w, l, m), q8_scales(w, l, m), r);
   }
 }
 
@@ -481,9 +484,7 @@ __device__ __forceinline__ void load_head(WRegs<Q8, H16>& R, const Weights& w, i
   } else if constexpr (!Q8) {
     ld_row3(&R.r[3 * s], w.wte + (size_t)r * D);
   } else {
-    i4 t[1];
-    q8_load_row<D>(t, R.sc[s], q8_codes(w, 0, M_HEAD), q8_scales(w, 0, M_HEAD), r);
-    R.c[s] = t[0];
+    q8_load_row768q(R.c[s], R.sc[s], q8_codes(w, 0, M_HEAD), q8_scales(w, 0, M_HEAD), r);
   }
 }
 template <bool Q8, bool H16>
@@ -666,23 +667,47 @@ __device__ __forceinline__ void head_rows(const FusedArgs a, FusedSmem& S, WRegs
     load_frag<3>(x, S.xs);
     layernorm_frag(x, S.lnf[0], S.lnf[1]);
   }
+  if constexpr (!Q8) {
 #pragma unroll
-  for (int k = 0; k < HEAD_MAX_ROWS; ++k) {
-    // keep the loads in slot order: at most NHS rows in flight per wave
-    __builtin_amdgcn_sched_barrier(0);
-    const int r = hw + k * HEAD_STRIDE;
-    const int s = k % NS;
-    float y;
-    if constexpr (!Q8) {
-      y = dot_slots(R, 3 * s, x);
-    } else {
-      int32_t* ca = CAP && r < V ? (int32_t*)(a.capture + cap_offset(0, M_HEAD) + cap_item(M_HEAD).acc) + (size_t)r * 12
-                                 : nullptr;
-      y = q8_dot<D>(*reinterpret_cast<i4(*)[1]>(&R.c[s]), R.sc[s], S.xc, S.xsc, ca);
-      if (CAP && r < V && lane == 0) ((float*)(a.capture + cap_offset(0, M_HEAD) + cap_item(M_HEAD).y))[r] = y;
+    for (int k = 0; k < HEAD_MAX_ROWS; ++k) {
+      // keep the loads in slot order: at most NHS rows in flight per wave
+      __builtin_amdgcn_sched_barrier(0);
+      const int r = hw + k * HEAD_STRIDE;
+      const int s = k % NS;
+      const float y = dot_slots(R, 3 * s, x);
+      *(r < V ? a.logits + r : sinkf) = y;
+      if (k + NS < HEAD_MAX_ROWS) load_head<Q8, H16>(R, a.w, s, r + NS * HEAD_STRIDE);
+      if (k == NS - 1 && lane == 0 && (threadIdx.x >> 6) == 1) stamp(a.trace, 57);
     }
-    *(r < V ? a.logits + r : sinkf) = y;
-    if (k + NS < HEAD_MAX_ROWS) load_head<Q8, H16>(R, a.w, s, r + NS * HEAD_STRIDE);
+  } else {
+    // int8: an int8 row is a long dependent chain for few bytes, so HG rows are
+    // evaluated together (their chains overlap), then stored and their slots refilled
+    constexpr int HG = 4;
+    static_assert(NS % HG == 0, "head groups");
+#pragma unroll
+    for (int k0 = 0; k0 < HEAD_MAX_ROWS; k0 += HG) {
+      __builtin_amdgcn_sched_barrier(0);
+      float y[HG];
+#pragma unroll
+      for (int u = 0; u < HG; ++u) {
+        const int k = k0 + u, r = hw + k * HEAD_STRIDE, s = k % NS;
+        if (k < HEAD_MAX_ROWS) {
+          int32_t* ca = CAP && r < V ? (int32_t*)(a.capture + cap_offset(0, M_HEAD) + cap_item(M_HEAD).acc) + (size_t)r * 12
+                                     : nullptr;
+          y[u] = q8_dot768q(R.c[s], R.sc[s], S.xc, S.xsc, ca);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < HG; ++u) {
+        const int k = k0 + u, r = hw + k * HEAD_STRIDE, s = k % NS;
+        if (k < HEAD_MAX_ROWS) {
+          if (CAP && r < V && lane == 0) ((float*)(a.capture + cap_offset(0, M_HEAD) + cap_item(M_HEAD).y))[r] = y[u];
+          *(r < V ? a.logits + r : sinkf) = y[u];
+          if (k + NS < HEAD_MAX_ROWS) load_head<Q8, H16>(R, a.w, s, r + NS * HEAD_STRIDE);
+        }
+      }
+      if (k0 + HG == NS && lane == 0 && (threadIdx.x >> 6) == 1) stamp(a.trace, 57);
+    }
   }
 }
 
@@ -824,7 +849,7 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
         } else {
           int32_t* ca = CAP && own ? (int32_t*)(a.capture + cap_offset(l, M_QKV) + cap_item(M_QKV).acc) + (size_t)r * 12
                                    : nullptr;
-          y = q8_dot<D>(*reinterpret_cast<i4(*)[1]>(&R.c[k]), R.sc[k], S.xc, S.xsc, ca);
+          y = q8_dot768q(R.c[k], R.sc[k], S.xc, S.xsc, ca);
         }
         y = y + R.b[k];
         if (store_lane(64)) {
@@ -854,7 +879,7 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
         } else {
           int32_t* ca = CAP && own ? (int32_t*)(a.capture + cap_offset(l, M_FC) + cap_item(M_FC).acc) + (size_t)r * 12
                                    : nullptr;
-          y = q8_dot<D>(*reinterpret_cast<i4(*)[1]>(&R.c[UPW + k]), R.sc[UPW + k], S.xc, S.xsc, ca);
+          y = q8_dot768q(R.c[UPW + k], R.sc[UPW + k], S.xc, S.xsc, ca);
         }
         y = y + R.b[UPW + k];
         const float gy = gelu_tanh(y);
@@ -1115,6 +1140,7 @@ __global__ __launch_bounds__(FT, 1) void k_fused(const FusedArgs a) {
     wg_barrier();
     if (CAP && blockIdx.x == 0 && wave == 0) capture_input(a, S, 0, M_HEAD, S.xn, 0, D, lane, 64);
   }
+  if (lane == 0 && wave == 1) stamp(a.trace, 55);
   head_rows<Q8, CAP, H16>(a, S, R, hw, sinkf);
   if (lane == 0 && wave == 1) stamp(a.trace, 50);
 
