@@ -873,7 +873,7 @@ __device__ __forceinline__ float q8_dot(const i4 (&wc)[(K + 1023) / 1024], float
 
 // The 768-input form of q8_dot with the weight scales in quad layout: lane l < 48
 // holds the row's codes at bytes 16l..16l+15 (group g = l/4) and swq, the row's
-// scale of group l/4 (0 in lanes 48..63, whose codes are 0).  acc[g] is the exact
+// scale of group l/4 (lanes 48..63: any values, they contribute no term).  acc[g] is the exact
 // quad sum in lanes 4g..4g+3, so t[g] is formed there and the fixed-order rescale
 // reads lane 4g: the same values and operations as q8_dot<768>, without moving the
 // group sums across lanes first.  cap_acc as for q8_dot.
@@ -894,14 +894,14 @@ __device__ __forceinline__ float q8_dot768q(const i4 wc, float swq, const int8_t
   for (int g = 0; g < 12; ++g) y = y + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 4 * g));
   return y;
 }
-// Codes of int8 row r of a [rows][768] matrix (lanes 48..63 zero) and its group
-// scales in quad layout, for q8_dot768q (nontemporal loads).
+// Codes of int8 row r of a [rows][768] matrix and its group scales in quad layout,
+// for q8_dot768q (nontemporal loads).  Lanes 48..63 hold copies of lane 47's codes
+// and scale: q8_dot768q takes no term from those lanes, so nothing here uses the
+// loaded values and the loads stay in flight until the dot reads them.
 __device__ __forceinline__ void q8_load_row768q(i4& wc, float& swq, const int8_t* codes, const float* scales, int r) {
   const int lane = lane_id_fresh();
-  const i4 v = __builtin_nontemporal_load((const i4*)(codes + (size_t)r * 768 + 16 * min(lane, 47)));
-  wc = lane < 48 ? v : i4{0, 0, 0, 0};
-  const float sv = scales[(size_t)r * 12 + min(lane >> 2, 11)];
-  swq = lane < 48 ? sv : 0.0f;
+  wc = __builtin_nontemporal_load((const i4*)(codes + (size_t)r * 768 + 16 * min(lane, 47)));
+  swq = scales[(size_t)r * 12 + min(lane >> 2, 11)];
 }
 
 // Load the codes and lane-g scale of int8 row r of a [rows][K] matrix (nontemporal).

@@ -345,6 +345,7 @@ __device__ __forceinline__ void ld_row3_h(h4* dst, const uint16_t* row) {
 
 template <bool Q8, bool H16>
 __device__ __forceinline__ void load_row768(WRegs<Q8, H16>& R, int slot, const Weights& w, int l, int m, int r) {
+  r = __builtin_amdgcn_readfirstlane(r);  // one row per wave: its offset in scalar registers
   if constexpr (H16) {
     ld_row3_h(&R.r[3 * slot], f16_mat(w, l, m) + (size_t)r * D);
   } else if constexpr (!Q8) {
@@ -478,7 +479,7 @@ __device__ __forceinline__ void load_o_head(WRegs<Q8, H16>& R, char* stage, cons
 // Head row r (clamped to the last row) into head slot s.
 template <bool Q8, bool H16>
 __device__ __forceinline__ void load_head(WRegs<Q8, H16>& R, const Weights& w, int s, int r) {
-  r = min(r, V - 1);
+  r = __builtin_amdgcn_readfirstlane(min(r, V - 1));
   if constexpr (H16) {
     ld_row3_h(&R.r[3 * s], f16_mat(w, 0, M_HEAD) + (size_t)r * D);
   } else if constexpr (!Q8) {
@@ -827,6 +828,9 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
     u64* loc = loc_of(c, l);
     u64* glb = glb_of(c, l);
     if (l > 0) rs_pr_poll<Q8>(a, S, c, l - 1, wave);
+    // The block's weights (registers and direct-to-LDS copies) landed during the
+    // wait: retire them here, so later reads of them wait on no store of this block.
+    wave_vmem_sync();
     wg_barrier();  // BA
     if constexpr (Q8) {
       wg_barrier();
