@@ -143,9 +143,12 @@ __global__ __launch_bounds__(256) void k_proj(const ProjArgs a) {
       else w[rr][i] = nt_load((const f4*)(W + e));
     }
   }
-  float bias[RPW];
-#pragma unroll
-  for (int rr = 0; rr < RPW; ++rr) bias[rr] = row0 + rr < NROWS ? proj_bias<MODE>(a, row0 + rr) : 0.0f;
+  // Outputs of a pass of BT sessions are gathered one per lane (lane s*RPW + rr:
+  // session s, row rr), so the bias, the epilogue (GELU, residual add, cache copy)
+  // and the stores run once per lane instead of once per output on the whole wave.
+  static_assert(BT * RPW <= 64, "one lane per output of a pass");
+  const int orr = lane % RPW, os = lane / RPW, orow = row0 + orr;
+  const float bias = orow < NROWS ? proj_bias<MODE>(a, orow) : 0.0f;
   const int sb1 = min(a.ss.B, (int)(blockIdx.y + 1) * a.sb);
   for (int b0 = blockIdx.y * a.sb; b0 < sb1; b0 += BT) {
     const int nb = min(BT, sb1 - b0);
@@ -157,17 +160,20 @@ __global__ __launch_bounds__(256) void k_proj(const ProjArgs a) {
       store_frag<NI>(&xs[s][0], x);
     }
     __syncthreads();
-    for (int s = 0; s < nb; ++s) {
+    float yl = 0.0f;
+#pragma unroll
+    for (int s = 0; s < BT; ++s) {
+      if (s >= nb) break;
       f4 x[NI];
       load_frag<NI>(x, &xs[s][0]);
 #pragma unroll
       for (int rr = 0; rr < RPW; ++rr) {
-        const int r = row0 + rr;
-        if (r >= NROWS) break;
-        const float y = proj_dot<MODE, NI>(w[rr], x) + bias[rr];
-        if (lane == 0) proj_store<MODE>(a, b0 + s, r, y);
+        if (row0 + rr >= NROWS) break;
+        const float y = proj_dot<MODE, NI>(w[rr], x);
+        yl = lane == s * RPW + rr ? y : yl;
       }
     }
+    if (os < nb && orow < NROWS) proj_store<MODE>(a, b0 + os, orow, yl + bias);
   }
 }
 

@@ -40,14 +40,19 @@ enum : int {
   DPP_ROW_BCAST15 = 0x142,
   DPP_ROW_BCAST31 = 0x143,
 };
+// With every row enabled (the quad permutes and mirrors, whose source lanes all
+// exist) the move has no old value, so the compiler folds it into the VALU op that
+// consumes it (one v_add_f32_dpp instead of a move and an add).  With a partial row
+// mask the rows left out keep their own value.
 template <int CTRL, int ROWS = 0xf>
 __device__ __forceinline__ float dpp_f(float v) {
   const int i = __float_as_int(v);
-  return __int_as_float(__builtin_amdgcn_update_dpp(i, i, CTRL, ROWS, 0xf, false));
+  if constexpr (ROWS == 0xf) return __int_as_float(__builtin_amdgcn_mov_dpp(i, CTRL, 0xf, 0xf, true));
+  else return __int_as_float(__builtin_amdgcn_update_dpp(i, i, CTRL, ROWS, 0xf, false));
 }
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int v) {
-  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xf, 0xf, false);
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, true);
 }
 __device__ __forceinline__ float bcast_lane(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
