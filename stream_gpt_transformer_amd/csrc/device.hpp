@@ -31,7 +31,8 @@ __device__ __forceinline__ f4 widen(const h4 h) { return __builtin_convertvector
 // distance 1 and 2; row_half_mirror and row_mirror reverse 8- and 16-lane groups,
 // which acts as a swap at distance 4 and 8 once the quads (then the 8-lane halves)
 // hold equal values; row_bcast:15 adds row r-1's last lane into row r (rows 1, 3),
-// row_bcast:31 adds lane 31 into rows 2 and 3.
+// row_bcast:31 adds lane 31 into rows 2 and 3 (the prefix scans use these two).
+// Across rows the reductions use gfx950's row and half-wave swaps instead.
 enum : int {
   DPP_QUAD_1032 = 0xB1,
   DPP_QUAD_2301 = 0x4E,
@@ -68,22 +69,36 @@ __device__ __forceinline__ float row16_sum(float v) {
   v = v + dpp_f<DPP_ROW_MIRROR>(v);
   return v;
 }
-// Sum of the 64 lanes: row sums r0..r3 as above, then (r3 + r2) + (r1 + r0) in
-// lane 63, read back as a wave-uniform value.
+// Rows 0 and 1 (and 2 and 3) exchanged, then the two 32-lane halves (gfx950
+// v_permlane16_swap / v_permlane32_swap on two copies of v): a + b holds, in every
+// lane, the combination of the lane's row (half) with its partner row (half).
+__device__ __forceinline__ float swap_rows_add(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap_halves_add(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap_rows_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap_halves_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Sum of the 64 lanes: row sums r0..r3 as above, then (r0 + r1) + (r2 + r3) (each
+// add's operands in either order: the same value), in every lane.
 __device__ __forceinline__ float wave_sum(float v) {
-  v = row16_sum(v);
-  v = v + dpp_f<DPP_ROW_BCAST15, 0xa>(v);
-  v = v + dpp_f<DPP_ROW_BCAST31, 0xc>(v);
-  return bcast_lane(v, 63);
+  return swap_halves_add(swap_rows_add(row16_sum(v)));
 }
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp_f<DPP_QUAD_1032>(v));
   v = fmaxf(v, dpp_f<DPP_QUAD_2301>(v));
   v = fmaxf(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
   v = fmaxf(v, dpp_f<DPP_ROW_MIRROR>(v));
-  v = fmaxf(v, dpp_f<DPP_ROW_BCAST15, 0xa>(v));
-  v = fmaxf(v, dpp_f<DPP_ROW_BCAST31, 0xc>(v));
-  return bcast_lane(v, 63);
+  return swap_halves_max(swap_rows_max(v));
 }
 // N independent wave sums in lock step (the same tree as wave_sum for each value,
 // interleaved so that the lane moves of one hide the latency of the others).
@@ -98,11 +113,9 @@ __device__ __forceinline__ void wave_sum_n(float (&v)[N]) {
 #pragma unroll
   for (int k = 0; k < N; ++k) v[k] = v[k] + dpp_f<DPP_ROW_MIRROR>(v[k]);
 #pragma unroll
-  for (int k = 0; k < N; ++k) v[k] = v[k] + dpp_f<DPP_ROW_BCAST15, 0xa>(v[k]);
+  for (int k = 0; k < N; ++k) v[k] = swap_rows_add(v[k]);
 #pragma unroll
-  for (int k = 0; k < N; ++k) v[k] = v[k] + dpp_f<DPP_ROW_BCAST31, 0xc>(v[k]);
-#pragma unroll
-  for (int k = 0; k < N; ++k) v[k] = bcast_lane(v[k], 63);
+  for (int k = 0; k < N; ++k) v[k] = swap_halves_add(v[k]);
 }
 // The 16-lane tree of row16_sum evaluated inside one lane on s[0..15] (s[j] being
 // what lane j of the row holds): the same value, by commutativity of each add.
