@@ -121,11 +121,23 @@ __device__ __forceinline__ float proj_dot(const f4 (&w)[NI], const f4 (&x)[NI]) 
 // proj_dot(W_r, x_b) + bias_r — the same value for any B, RPW, BT or session split
 // (blockIdx.y takes sessions a.sb*y .. a.sb*y + a.sb - 1).  H16: the weights are read
 // as binary16 and widened (exact) when loaded.
+// A pass computes the BT*RPW outputs o = s*RPW + rr (session s, row rr) of a tile
+// together: every lane forms its lane partials as proj_dot does, the cross-lane
+// trees run transposed over the outputs (wave_treduce, row_treduce: the same adds
+// as wave_sum and row16_sum), the output projection's head chain and the MLP
+// projection's slice chains run in the lanes of row 0, and each result lands in
+// one lane, where its bias, epilogue (GELU, residual add, cache copy) and store run.
 template <int MODE, int RPW, int BT, bool H16>
 __global__ __launch_bounds__(256) void k_proj(const ProjArgs a) {
   constexpr int NI = MODE == MODE_PR ? F / 256 : D / 256;
   constexpr int K = 256 * NI;
   constexpr int NROWS = mode_rows<MODE>();
+  constexpr bool FULL = MODE != MODE_O && MODE != MODE_PR;  // one 64-lane tree per output
+  constexpr int NO = BT * RPW;                               // outputs of a pass
+  constexpr int GN = NO < 16 ? NO : 16;                      // outputs per transposed reduction
+  constexpr int NG = NO / GN;                                // reductions per pass (lane row g holds group g)
+  constexpr int SG = GN / RPW;                               // sessions per group
+  static_assert(NO % GN == 0 && GN % RPW == 0 && NG <= 4 && (FULL || NG == 1), "pass shape");
   __shared__ __align__(16) float xs[BT][K];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row0 = (blockIdx.x * 4 + wave) * RPW;
@@ -143,12 +155,12 @@ __global__ __launch_bounds__(256) void k_proj(const ProjArgs a) {
       else w[rr][i] = nt_load((const f4*)(W + e));
     }
   }
-  // Outputs of a pass of BT sessions are gathered one per lane (lane s*RPW + rr:
-  // session s, row rr), so the bias, the epilogue (GELU, residual add, cache copy)
-  // and the stores run once per lane instead of once per output on the whole wave.
-  static_assert(BT * RPW <= 64, "one lane per output of a pass");
-  const int orr = lane % RPW, os = lane / RPW, orow = row0 + orr;
-  const float bias = orow < NROWS ? proj_bias<MODE>(a, orow) : 0.0f;
+  // the output this lane receives: group grp (lane row), output o of the pass
+  const int t = lane & 15, grp = lane >> 4;
+  const int o = GN * grp + treduce_out<GN>(t);
+  const bool olane = grp < NG && t < GN;
+  const int os = o / RPW, orow = row0 + o % RPW;
+  const float bias = olane && orow < NROWS ? proj_bias<MODE>(a, orow) : 0.0f;
   const int sb1 = min(a.ss.B, (int)(blockIdx.y + 1) * a.sb);
   for (int b0 = blockIdx.y * a.sb; b0 < sb1; b0 += BT) {
     const int nb = min(BT, sb1 - b0);
@@ -160,20 +172,57 @@ __global__ __launch_bounds__(256) void k_proj(const ProjArgs a) {
       store_frag<NI>(&xs[s][0], x);
     }
     __syncthreads();
-    float yl = 0.0f;
+    // staged rows past nb hold stale values; their outputs are never stored
+    float y = 0.0f;
+    if constexpr (FULL) {
 #pragma unroll
-    for (int s = 0; s < BT; ++s) {
-      if (s >= nb) break;
-      f4 x[NI];
-      load_frag<NI>(x, &xs[s][0]);
+      for (int g = 0; g < NG; ++g) {
+        float p[GN];
 #pragma unroll
-      for (int rr = 0; rr < RPW; ++rr) {
-        if (row0 + rr >= NROWS) break;
-        const float y = proj_dot<MODE, NI>(w[rr], x);
-        yl = lane == s * RPW + rr ? y : yl;
+        for (int sl = 0; sl < SG; ++sl) {
+          f4 x[NI];
+          load_frag<NI>(x, &xs[g * SG + sl][0]);
+#pragma unroll
+          for (int rr = 0; rr < RPW; ++rr) p[sl * RPW + rr] = dot_lane<NI>(w[rr], x);
+        }
+        const float r = wave_treduce<GN>(p);
+        y = grp == g ? r : y;
+      }
+    } else {
+      // group sums: fragment i, lane row q holds the 64-input group 4i + q
+      float gs[NI][4];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        float p[GN];
+#pragma unroll
+        for (int sl = 0; sl < SG; ++sl) {
+          const f4 xv = *(const f4*)&xs[sl][256 * i + 4 * lane];
+#pragma unroll
+          for (int rr = 0; rr < RPW; ++rr) p[sl * RPW + rr] = fma4(w[rr][i], xv);
+        }
+        const float tr = row_treduce<GN>(p);
+        gs[i][0] = tr;
+        gs[i][1] = row1_to_row0(tr);
+        gs[i][2] = row2_to_row0(tr);
+        gs[i][3] = row3_to_row0(tr);
+      }
+      if constexpr (MODE == MODE_O) {
+        // y = 0, y = y + p_h for heads h = 0..11 (o_row)
+#pragma unroll
+        for (int h = 0; h < H; ++h) y = y + gs[h / 4][h % 4];
+      } else {
+        // p_s = q_6s + ... + q_6s+5, y = 0, y = y + p_s for s = 0..7 (pr_row)
+#pragma unroll
+        for (int sl = 0; sl < PR_SLICES; ++sl) {
+          const int g0 = PR_SLICE_GROUPS * sl;
+          float ps = gs[g0 / 4][g0 % 4];
+#pragma unroll
+          for (int k = 1; k < PR_SLICE_GROUPS; ++k) ps = ps + gs[(g0 + k) / 4][(g0 + k) % 4];
+          y = y + ps;
+        }
       }
     }
-    if (os < nb && orow < NROWS) proj_store<MODE>(a, b0 + os, orow, yl + bias);
+    if (olane && os < nb && orow < NROWS) proj_store<MODE>(a, b0 + os, orow, y + bias);
   }
 }
 
@@ -456,6 +505,11 @@ __global__ __launch_bounds__(256) void k_special_bits(int kind, uint32_t first, 
 #ifndef BATCH_SB
 #define BATCH_SB 8
 #endif
+// 1: the LayerNorm inputs are normalised once per session (k_bln) before the
+// projection; 0: every workgroup normalises the sessions it stages
+#ifndef BATCH_PRELN
+#define BATCH_PRELN 1
+#endif
 // the head (50,257 rows): more rows and sessions per workgroup, fewer input re-reads
 #ifndef BATCH_HEAD_RPW
 #define BATCH_HEAD_RPW 4
@@ -493,9 +547,10 @@ static void launch_layers(ProjArgs& a, hipStream_t s) {
     launch_proj_ln<MODE_FC, RPW, BT768, H16>(a, s);
     launch_proj<MODE_PR, RPW, BT3072, H16>(a, s);
   }
-  if (a.preln) {
+  if (B > 1) {
     ProjArgs ah = a;
     ah.sb = BATCH_HEAD_SB;
+    ah.preln = 1;
     launch_proj_ln<MODE_HEAD, BATCH_HEAD_RPW, BATCH_HEAD_BT, H16>(ah, s);
   } else {
     launch_proj_ln<MODE_HEAD, RPW, BT768, H16>(a, s);
@@ -520,7 +575,7 @@ hipError_t launch_step_f32(const Weights& w, const Work& k, const Sessions& ss, 
   } else if (ss.B == 1) {
     launch_layers<2, 1, 1, false>(a, s);
   } else {
-    a.preln = 1;
+    a.preln = BATCH_PRELN;
     launch_layers<BATCH_RPW, BATCH_BT768, BATCH_BT3072, false>(a, s);
   }
   return hipGetLastError();

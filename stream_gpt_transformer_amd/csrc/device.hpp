@@ -36,6 +36,7 @@ __device__ __forceinline__ f4 widen(const h4 h) { return __builtin_convertvector
 enum : int {
   DPP_QUAD_1032 = 0xB1,
   DPP_QUAD_2301 = 0x4E,
+  DPP_QUAD_3210 = 0x1B,
   DPP_ROW_MIRROR = 0x140,
   DPP_ROW_HALF_MIRROR = 0x141,
   DPP_ROW_BCAST15 = 0x142,
@@ -149,6 +150,73 @@ __device__ __forceinline__ int lane_id_fresh() {
   asm volatile("" : "+v"(l));
   return l;
 }
+
+// ---- many outputs at once ----------------------------------------------------
+// row16_sum's tree for N outputs (a power of two, <= 16) together, transposed over
+// the 16 lanes of each row.  Level k pairs lane b with lane b ^ m_k (m = 1, 3, 7,
+// 15: quad_perm [1,0,3,2], quad_perm [3,2,1,0], row_half_mirror, row_mirror), which
+// lies in the other 2^k-lane block of the same 2^(k+1)-lane block, as row16_sum's
+// level k does.  While outputs remain to split, the two partners hold partial sums
+// of the same outputs (over their two blocks); each keeps the half of them whose
+// output-index bit k equals c_k(lane) and adds its partner's copy of that half, the
+// partner keeping the other half (c_0 = b0^b1, c_1 = b1^b2, c_2 = b2^b3, c_3 = b3 for
+// the row's lane bits b: partners differ in c_k and agree in the earlier ones).
+// After the split levels the partners hold the same output and add as row16_sum.
+// Every add joins the same two block sums as in row16_sum, so each result is bit
+// for bit row16_sum's value of that output; lane t of every row ends with output
+// treduce_out<N>(t), the sum over its own row.
+__device__ __forceinline__ int treduce_c(int t, int k) { return k < 3 ? ((t >> k) ^ (t >> (k + 1))) & 1 : (t >> 3) & 1; }
+template <int N>
+__device__ __forceinline__ int treduce_out(int t) {
+  int o = 0;
+#pragma unroll
+  for (int k = 0; (1 << k) < N; ++k) o |= treduce_c(t, k) << k;
+  return o;
+}
+template <int CTRL, int N>
+__device__ __forceinline__ void treduce_level(float (&a)[16], int& n, bool c) {
+  if (n >= 2) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      if (2 * i < n) {
+        const float x = c ? a[2 * i + 1] : a[2 * i];
+        const float y = c ? a[2 * i] : a[2 * i + 1];
+        a[i] = x + dpp_f<CTRL>(y);
+      }
+    }
+    n /= 2;
+  } else {
+    a[0] = a[0] + dpp_f<CTRL>(a[0]);
+  }
+}
+template <int N>
+__device__ __forceinline__ float row_treduce(const float (&v)[N]) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "outputs per row reduction");
+  const int t = lane_id() & 15;
+  float a[16];
+#pragma unroll
+  for (int j = 0; j < N; ++j) a[j] = v[j];
+  int n = N;
+  treduce_level<DPP_QUAD_1032, N>(a, n, treduce_c(t, 0));
+  treduce_level<DPP_QUAD_3210, N>(a, n, treduce_c(t, 1));
+  treduce_level<DPP_ROW_HALF_MIRROR, N>(a, n, treduce_c(t, 2));
+  treduce_level<DPP_ROW_MIRROR, N>(a, n, treduce_c(t, 3));
+  return a[0];
+}
+// wave_sum's tree for N outputs together: lane t of every row holds the 64-lane sum
+// of output treduce_out<N>(t).
+template <int N>
+__device__ __forceinline__ float wave_treduce(const float (&v)[N]) {
+  return swap_halves_add(swap_rows_add(row_treduce<N>(v)));
+}
+// Row r's value of v in the lanes of row 0 (r = 1, 2, 3; other rows: any value).
+__device__ __forceinline__ float row1_to_row0(float v) {
+  return __uint_as_float(__builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false)[1]);
+}
+__device__ __forceinline__ float row2_to_row0(float v) {
+  return __uint_as_float(__builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false)[1]);
+}
+__device__ __forceinline__ float row3_to_row0(float v) { return row2_to_row0(row1_to_row0(v)); }
 
 // ---- lane fragments ---------------------------------------------------------
 // A K-vector (K = 256*NI) is spread over one wavefront as NI float4 per lane:
