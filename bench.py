@@ -332,6 +332,9 @@ def main() -> int:
     ap.add_argument("--pmc-probe", action="store_true",
                     help="for counter runs: 128 fp32, 128 int8, then 128 binary16 steps (positions 0..127) and one "
                          "device copy of 256 MiB, nothing timed or printed")
+    ap.add_argument("--prefill-probe", action="store_true",
+                    help="for counter runs: 10 infer(128) calls and 10 batched steps (64 sessions, positions 0..9), "
+                         "nothing timed or printed")
     ap.add_argument("--timeline", action="store_true",
                     help="per-block phase times and per-position step times (markdown), no JSON line")
     ap.add_argument("--timeline-positions", default="1,64,127")
@@ -395,6 +398,23 @@ def main() -> int:
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
+        torch.cuda.synchronize()
+        st = m.status()
+        m.close()
+        return 1 if st else 0
+
+    if args.prefill_probe:
+        ptoks = synth.make_tokens(synth.SEED_PREFILL, NPOS).tolist()
+        for _ in range(10):
+            g.gpt2_infer(h, ptoks, ws, lp, s)
+        btoks = np.stack([synth.make_tokens(synth.SEED_BATCH_BASE + b, NPOS) for b in range(BATCH)])
+        bcaches = torch.zeros((BATCH, NPOS * PER), dtype=torch.float32, device=dev)
+        blog = torch.empty((BATCH, g.GPT2_VOCAB), dtype=torch.float32, device=dev)
+        for p in range(10):
+            rc = g.gpt2_batched_cached_step(h, bcaches.data_ptr(), NPOS * PER, [p * PER] * BATCH,
+                                            btoks[:, p].tolist(), [p] * BATCH, ws, blog.data_ptr(), s)
+            if rc:
+                raise g.Gpt2Error(rc, "gpt2_batched_cached_step")
         torch.cuda.synchronize()
         st = m.status()
         m.close()

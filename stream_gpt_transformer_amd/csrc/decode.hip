@@ -515,7 +515,7 @@ __global__ __launch_bounds__(256) void k_special_bits(int kind, uint32_t first, 
 #define BATCH_HEAD_RPW 4
 #endif
 #ifndef BATCH_HEAD_SB
-#define BATCH_HEAD_SB 32
+#define BATCH_HEAD_SB 64
 #endif
 #ifndef BATCH_HEAD_BT  // sessions staged per pass: 24 KB of LDS, so more workgroups fit a CU
 #define BATCH_HEAD_BT 8

@@ -30,8 +30,10 @@ enum Epi { EPI_STORE = 0, EPI_PART = 1 };
 // one of NBUF LDS buffers by 16-byte direct-to-LDS loads, NBUF-1 stages ahead of the
 // one being multiplied, so no registers and no LDS store instructions carry the
 // operands.  A 1 KB region of a buffer holds eight rows, chunk c of row r at slot
-// c ^ (r % 8), so that the eight lanes of an MFMA operand read, which take the same
-// chunk of eight consecutive rows, hit distinct banks.  Each wave copies five of the
+// c ^ ((r / 2) % 8): the LDS serves a 16-byte-per-lane read sixteen lanes at a time
+// over 64 four-byte banks, and the sixteen lanes of an MFMA operand read take the
+// same chunk of sixteen consecutive rows (128 bytes apart, so two rows share a
+// bank offset), which this puts on distinct banks.  Each wave copies five of the
 // 20 regions; it waits until its own copies of a stage have landed, and a workgroup
 // barrier then makes the whole stage visible (and frees the buffer of the stage
 // before, which the copies of stage t+NBUF-1 overwrite).
@@ -61,7 +63,7 @@ __global__ __launch_bounds__(256) void k_gemm(const float* __restrict__ A, int l
   const float* src[MM_PERW];
 #pragma unroll
   for (int i = 0; i < MM_PERW; ++i) {
-    const int row = 8 * (wave + 4 * i) + lane / 8, c = (lane % 8) ^ (lane / 8);
+    const int row = 8 * (wave + 4 * i) + lane / 8, c = (lane % 8) ^ ((row >> 1) & 7);
     src[i] = (row < GM ? A + (size_t)min(row, M - 1) * lda : W + (size_t)(n0 + row - GM) * ldw) + kbeg + 4 * c;
   }
   auto copy_stage = [&](int t) {
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(256) void k_gemm(const float* __restrict__ A, int l
       __builtin_amdgcn_global_load_lds((const void*)(src[i] + o),
                                        (__attribute__((address_space(3))) void*)(buf + 1024 * (wave + 4 * i)), 16, 0, 0);
   };
-  const int h = lane >> 5, sw = lane & 7;
+  const int h = lane >> 5, sw = ((lane & 31) >> 1) & 7;  // (row / 2) % 8 of the lane's A and B rows
   const int aoff = (32 * wave + (lane & 31)) * (GK * 4), boff = (GM + (lane & 31)) * (GK * 4);
   f32x16 acc[2];
 #pragma unroll
@@ -127,7 +129,7 @@ __global__ __launch_bounds__(256) void k_gemm(const float* __restrict__ A, int l
 // v_mfma_f32_16x16x4_f32: lane l supplies A[l%16][k] and B[k][l%16] with its
 // K-group kg = l/16, and result register r of lane l is C[4(l/16) + r][l%16].
 // K is staged KS elements at a time (CH = KS/4 chunks of 16 bytes per row, chunk c
-// of row r at slot c ^ (r % 8)); group kg reads chunks kg*CH/4 .. (kg+1)*CH/4 - 1 of
+// of row r at slot c ^ ((r / 2) % 8), as in k_gemm); group kg reads chunks kg*CH/4 .. (kg+1)*CH/4 - 1 of
 // its operand rows, and product s (< KS/4) of a stage feeds element kg*KS/4 + s,
 // so a stage's elements are consumed once each.  Loads are held in registers PF
 // stages ahead; a pass reads the next stage's fragments before multiplying the
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(G16_NTH) void k_gemm16(const float* __restrict__ A,
     const int idx = u < G::UA ? (int)threadIdx.x + G16_NTH * u : GM * G::CH + ((int)threadIdx.x % G::NB);
     const int rr = idx / G::CH, c = idx % G::CH;
     src[u] = (u < G::UA ? A + (size_t)min(rr, M - 1) * lda : W + (size_t)(n0 + rr - GM) * ldw) + 4 * c;
-    dst[u] = rr * G::RB + 16 * (c ^ (rr & 7));
+    dst[u] = rr * G::RB + 16 * (c ^ ((rr >> 1) & 7));
   }
   const bool bstore = (int)threadIdx.x < G::NB;
   f4 pre[PF][G::U];
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(G16_NTH) void k_gemm16(const float* __restrict__ A,
       if (u < G::UA || bstore) *(f4*)(lds + buf * G::BUF + dst[u]) = pre[slot][u];
   };
   constexpr int FR = G::CH / 4;  // chunks per K-group per stage
-  const int kg = lane >> 4, sw = lane & 7;
+  const int kg = lane >> 4, sw = ((lane & 15) >> 1) & 7;  // (row / 2) % 8 of the lane's A and B rows
   const int aoff = (16 * wave + (lane & 15)) * G::RB, boff = (GM + (lane & 15)) * G::RB;
   auto lread = [&](f4 (&fa)[FR], f4 (&fb)[FR], int buf) {
     const char* b = lds + buf * G::BUF;
