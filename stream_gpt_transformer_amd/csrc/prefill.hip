@@ -11,6 +11,8 @@
 // (attention for QKV, which also adds the bias; the residual-and-LayerNorm kernel
 // for the other two), so results do not depend on timing.  Causal attention stages
 // each head's key/value rows in LDS once per eight query rows.
+#include <mutex>
+
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -46,7 +48,10 @@ enum Epi { EPI_STORE = 0, EPI_PART = 1 };
 // EPI_STORE: C = acc + bias (bias may be null); EPI_PART: part[z][row][col] = acc.
 constexpr int GK = 32;
 constexpr int GM = 128;
-constexpr int MM_NBUF = 4;                              // stage buffers in LDS
+#ifndef PF_MM_NBUF
+#define PF_MM_NBUF 4
+#endif
+constexpr int MM_NBUF = PF_MM_NBUF;                     // stage buffers in LDS
 constexpr int MM_ROWS = GM + 32;                        // staged rows per stage
 constexpr int MM_BUF = MM_ROWS * GK * 4;                // bytes of one stage buffer
 constexpr int MM_PERW = MM_ROWS / 8 / 4;                // 1 KB regions copied per wave per stage
@@ -231,18 +236,15 @@ __global__ __launch_bounds__(G16_NTH) void k_gemm16(const float* __restrict__ A,
 
 // Stage depth of the full-K kernel (K elements per LDS stage) and its launch.
 constexpr int G16_KS = 32;
+#ifndef PF_G16_PF
+#define PF_G16_PF 2
+#endif
+constexpr int G16_PF = PF_G16_PF;  // stages held in registers ahead of the LDS pair
 template <bool GELU>
 static hipError_t gemm16(const float* A, int lda, const float* W, int M, int N, int K, const float* bias, float* C,
                          int ldc, hipStream_t s) {
   constexpr size_t lds = 2 * (size_t)G16<G16_KS>::BUF;
-  static bool attr = false;
-  if (!attr) {
-    const hipError_t e =
-        hipFuncSetAttribute((const void*)k_gemm16<G16_KS, GELU, 2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e) return e;
-    attr = true;
-  }
-  hipLaunchKernelGGL((k_gemm16<G16_KS, GELU, 2>), dim3(N / 16), dim3(G16_NTH), lds, s, A, lda, W, K, M, K, bias, C, ldc);
+  hipLaunchKernelGGL((k_gemm16<G16_KS, GELU, G16_PF>), dim3(N / 16), dim3(G16_NTH), lds, s, A, lda, W, K, M, K, bias, C, ldc);
   return hipGetLastError();
 }
 
@@ -445,7 +447,13 @@ hipError_t launch_head_f32(const Weights& w, const float* x_row, float* logits, 
 #ifndef PF_S_QKV
 #define PF_S_QKV 3
 #endif
-constexpr int S_QKV = PF_S_QKV, S_O = 8, S_PR = 8;
+#ifndef PF_S_O
+#define PF_S_O 8
+#endif
+#ifndef PF_S_PR
+#define PF_S_PR 8
+#endif
+constexpr int S_QKV = PF_S_QKV, S_O = PF_S_O, S_PR = PF_S_PR;
 static_assert((size_t)S_QKV * D3 * PMAX <= PF_PART_WORDS && (size_t)S_O * D * PMAX <= PF_PART_WORDS &&
                   (size_t)S_PR * D * PMAX <= PF_PART_WORDS,
               "partial-sum buffer");
@@ -457,20 +465,31 @@ static_assert(F % 16 == 0 && D % G16_KS == 0, "k_gemm16 tiles");
 template <int EPI>
 static hipError_t mm(const float* A, int lda, const float* W, int K, int M, int N, const float* bias, float* C, int ldc,
                      int split, hipStream_t s) {
-  static bool attr = false;
-  if (!attr) {
-    const hipError_t e = hipFuncSetAttribute((const void*)k_gemm<EPI>, hipFuncAttributeMaxDynamicSharedMemorySize, MM_LDS);
-    if (e) return e;
-    attr = true;
-  }
   hipLaunchKernelGGL((k_gemm<EPI>), dim3(N / 32, split), dim3(256), MM_LDS, s, A, lda, W, K, M, bias, C, ldc, K / split);
   return hipGetLastError();
+}
+
+// The GEMM kernels' LDS limits, set once per process (thread-safe) before their first launch.
+static hipError_t prefill_attrs() {
+  static std::once_flag once;
+  static hipError_t err = hipSuccess;
+  std::call_once(once, [] {
+    const void* fs[] = {(const void*)k_gemm<EPI_PART>, (const void*)k_gemm<EPI_STORE>};
+    for (const void* f : fs)
+      if (err == hipSuccess) err = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, MM_LDS);
+    const void* gs[] = {(const void*)k_gemm16<G16_KS, true, G16_PF>, (const void*)k_gemm16<G16_KS, false, G16_PF>};
+    for (const void* f : gs)
+      if (err == hipSuccess)
+        err = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 2 * (int)G16<G16_KS>::BUF);
+  });
+  return err;
 }
 
 hipError_t launch_infer(const Weights& w, const Work& k, const uint32_t* toks, int n, float* logits,
                         hipStream_t s, float* cache) {
   Toks tk{};
   hipError_t e;
+  if ((e = prefill_attrs())) return e;
   for (int t = 0; t < n; ++t) tk.t[t] = toks[t];
   hipLaunchKernelGGL(k_pf_embed_ln, dim3(n), dim3(64), 0, s, w, tk, k.pf_x, small_p(w, 0, sp::LN1_G),
                      small_p(w, 0, sp::LN1_B), k.pf_h);
@@ -494,10 +513,12 @@ hipError_t launch_infer(const Weights& w, const Work& k, const uint32_t* toks, i
 hipError_t launch_gemm16_test(const float* A, const float* W, const float* bias, float* C, int M, int N, int K,
                               bool gelu, hipStream_t s) {
   if (K % G16_KS) return hipErrorInvalidValue;
+  if (const hipError_t e = prefill_attrs()) return e;
   return gelu ? gemm16<true>(A, K, W, M, N, K, bias, C, N, s) : gemm16<false>(A, K, W, M, N, K, bias, C, N, s);
 }
 
 hipError_t launch_gemm_test(const float* A, const float* W, float* C, int M, int N, int K, hipStream_t s) {
+  if (const hipError_t e = prefill_attrs()) return e;
   return mm<EPI_STORE>(A, K, W, K, M, N, nullptr, C, N, 1, s);
 }
 
