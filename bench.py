@@ -335,6 +335,9 @@ def main() -> int:
     ap.add_argument("--prefill-probe", action="store_true",
                     help="for counter runs: 10 infer(128) calls and 10 batched steps (64 sessions, positions 0..9), "
                          "nothing timed or printed")
+    ap.add_argument("--cache-probe", action="store_true",
+                    help="fp32 and int8 step times with and without a 1 GiB device write between steps (which "
+                         "evicts the L2 and the 256 MB Infinity Cache), markdown, no JSON line")
     ap.add_argument("--timeline", action="store_true",
                     help="per-block phase times and per-position step times (markdown), no JSON line")
     ap.add_argument("--timeline-positions", default="1,64,127")
@@ -400,6 +403,35 @@ def main() -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
         st = m.status()
+        m.close()
+        return 1 if st else 0
+
+    if args.cache_probe:
+        # Each step timed alone (events on the step), positions spread over the filled
+        # session; "evicted": a 1 GiB fill runs between steps, so no weight byte a step
+        # reads can still be in the L2 or the Infinity Cache from the step before.
+        big = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        print("# Step time with the caches warm and with them evicted between steps\n")
+        print("| step | warm: median us | evicted: median us | evicted / warm |")
+        print("|---|---|---|---|")
+        for name, fn in (("fp32", g.gpt2_cached_step), ("int8-g64", g.gpt2_q8_cached_step)):
+            cache = filled_cache(fn)
+            res = {}
+            for mode in ("warm", "evicted"):
+                ts = []
+                for p in spread_positions(128):
+                    if mode == "evicted":
+                        big.fill_(1.0)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    call(fn, cache, p)
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    ts.append(e0.elapsed_time(e1) * 1000)
+                res[mode] = statistics.median(ts)
+            print(f"| {name} | {res['warm']:.1f} | {res['evicted']:.1f} | {res['evicted'] / res['warm']:.3f} |")
+        st = m.status()
+        print(f"\n- workspace error word after the runs: {st}")
         m.close()
         return 1 if st else 0
 
