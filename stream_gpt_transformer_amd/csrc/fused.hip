@@ -68,8 +68,12 @@ constexpr int GPS = GS / 64;             // groups per slice (6)
 constexpr int NG_PR = F / 64;            // int8 MLP-projection groups (48)
 constexpr int NCW = NWV - 1;             // compute waves of a regular unit (waves 1..7)
 constexpr int UPW = 4;                   // units per compute wave per phase
+#ifndef FUSED_NHS_F32
+#define FUSED_NHS_F32 8
+#endif
 template <bool Q8>
-constexpr int nhs() { return Q8 ? 12 : 8; }  // head-row slots per wave
+constexpr int nhs() { return Q8 ? 12 : FUSED_NHS_F32; }  // head-row slots per wave
+constexpr int F32_SLOTS = 3 * FUSED_NHS_F32 > 24 ? 3 * FUSED_NHS_F32 : 24;  // f4 slots of an fp32 wave
 constexpr int HEAD_STRIDE = NWV * GRID;  // head rows hw, hw + 2048, ...
 constexpr int HEAD_MAX_ROWS = (V + HEAD_STRIDE - 1) / HEAD_STRIDE;
 #ifndef FUSED_DELAY
@@ -288,12 +292,12 @@ template <bool Q8, bool H16 = false>
 struct WRegs;
 template <>
 struct WRegs<false, false> {
-  f4 r[24];
+  f4 r[F32_SLOTS];
   float b[8];  // bias of QKV rows 0..3, FC rows 0..3
 };
 template <>
 struct WRegs<false, true> {
-  h4 r[24];
+  h4 r[F32_SLOTS];
   float b[8];
 };
 template <>
@@ -815,6 +819,7 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
   const uint32_t E = c.E;
   u64* sinkw = a.sinkw + ((size_t)blockIdx.x * 8 + wave) * 16;
   float* sinkf = (float*)(sinkw + 8);
+  const int hw = wave * GRID + (int)blockIdx.x;  // first head row of this wave
   Units U;
   U.X = c.X;
   U.nh = c.nh;
@@ -944,8 +949,11 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
     // behind a wave's weight loads would hold up the other set's reduce-scatter.
     wave_vmem_sync();
     if (l + 2 < L) load_block<Q8, H16>(R, S.pr, a.w, l + 2, U, wave);
-    else load_head_slots<Q8, H16>(R, a.w, wave * GRID + (int)blockIdx.x);
   }
+  // The first head rows, outside the loop, so the slots past the block weights are not
+  // live across it.  (Filling the slots whose block rows are used up during set 1's last
+  // block, to start its head stream earlier, delays that block's MLP terms: slower.)
+  load_head_slots<Q8, H16>(R, a.w, hw);
   if (c.set == 0) rs_pr_poll<Q8>(a, S, c, L - 1, wave);
   wg_barrier();  // BT
 }
@@ -1084,8 +1092,6 @@ __device__ __forceinline__ void head_unit(const FusedArgs& a, FusedSmem& S, cons
     if (ln < L) {
       load_o_head<Q8, H16>(R, (char*)&S.pr, a.w, ln, h);
       stage_kv(a, S, ln, h);
-    } else {
-      load_head_slots<Q8, H16>(R, a.w, wave * GRID + (int)blockIdx.x);
     }
     if (wave == 0) {
       if (ln < L) bo = small_p(a.w, ln, sp::B_O)[o];
@@ -1093,6 +1099,7 @@ __device__ __forceinline__ void head_unit(const FusedArgs& a, FusedSmem& S, cons
     }
     wg_barrier();
   }
+  load_head_slots<Q8, H16>(R, a.w, wave * GRID + (int)blockIdx.x);
   float x1p = 0.0f;
   if (c.set == 0) {
     if (wave == 0) x1p = x1_share(a, c, L - 1);
