@@ -245,7 +245,10 @@ __device__ __forceinline__ void layernorm_frag(f4 (&x)[3], const float* __restri
 #pragma unroll
   for (int i = 0; i < 3; ++i) { s = s + x[i].x; s = s + x[i].y; s = s + x[i].z; s = s + x[i].w; }
   s = wave_sum(s);
-  const float mean = s / 768.0f;
+  // the binary32 path's statistics: products by 1/768 and the hardware reciprocal
+  // square root (within an ulp or two of s/768 and 1/sqrt; every fp32 path uses this
+  // same function, so they stay identical to each other)
+  const float mean = s * (1.0f / 768.0f);
   float v = 0.0f;
 #pragma unroll
   for (int i = 0; i < 3; ++i) {
@@ -253,8 +256,8 @@ __device__ __forceinline__ void layernorm_frag(f4 (&x)[3], const float* __restri
     v = v + x[i].x * x[i].x; v = v + x[i].y * x[i].y; v = v + x[i].z * x[i].z; v = v + x[i].w * x[i].w;
   }
   v = wave_sum(v);
-  const float var = v / 768.0f;
-  const float r = 1.0f / sqrtf(var + 1e-5f);
+  const float var = v * (1.0f / 768.0f);
+  const float r = __builtin_amdgcn_rsqf(var + 1e-5f);
   f4 g[3], b[3];
   load_frag<3>(g, gamma);
   load_frag<3>(b, beta);
@@ -617,7 +620,7 @@ __device__ __forceinline__ void wave_lds_wait() { asm volatile("s_waitcnt lgkmcn
 //   s_t = ((P_t,0 + P_t,1) + (P_t,2 + P_t,3)) * 0.125   (1/sqrt(64));
 //   m = max_t s_t;  e_t = exp_spec(s_t - m);
 //   Z = Z_0 + Z_1 with Z_w = wave_sum of e_t over t in [64w, 64w+64);
-//   w_t = e_t / Z;
+//   w_t = e_t * rcp(Z) (the hardware reciprocal);
 //   p_b = sum over t in [8b, 8b+8), t < npos, ascending, of w_t*V_t,d (b < 16);
 //   a_d = ((((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7))) + (((p8+p9)+(p10+p11))+((p12+p13)+(p14+p15)))).
 // Every value is the same for any block size of 128 or more threads (the work is
@@ -711,8 +714,9 @@ __device__ __forceinline__ float attn_compute(AttnSmem& sm, int npos, int nthr) 
     const float e0 = lane < npos ? exp_spec(s0 - m) : 0.0f;
     const float e1 = 64 + lane < npos ? exp_spec(s1 - m) : 0.0f;
     const float Z = wave_sum(e0) + wave_sum(e1);
-    sm.w[lane] = e0 / Z;
-    sm.w[64 + lane] = e1 / Z;
+    const float rz = __builtin_amdgcn_rcpf(Z);  // Z >= 1 (the maximum's term is 1)
+    sm.w[lane] = e0 * rz;
+    sm.w[64 + lane] = e1 * rz;
   }
   lds_barrier();
   for (int b = wv; b < ATT_VB; b += nthr / 64) {
