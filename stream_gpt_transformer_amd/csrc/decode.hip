@@ -77,8 +77,9 @@ __device__ __forceinline__ void proj_input(const ProjArgs& a, int b, f4 (&x)[NI]
   if constexpr (mode_ln<MODE>()) layernorm_frag(*reinterpret_cast<f4(*)[3]>(&x), ln_gamma<MODE>(a), ln_beta<MODE>(a));
 }
 
-// Epilogue of output r of session b; y is the projection value including bias.
-template <int MODE>
+// Epilogue of output r of session b; y is the projection value including bias.  Q8:
+// the int8 path's GELU (gelu_tanh) instead of the binary32 one (gelu_f32).
+template <int MODE, bool Q8 = false>
 __device__ __forceinline__ void proj_store(const ProjArgs& a, int b, int r, float y) {
   if constexpr (MODE == MODE_QKV) {
     a.k.qkv[(size_t)b * D3 + r] = y;
@@ -90,7 +91,7 @@ __device__ __forceinline__ void proj_store(const ProjArgs& a, int b, int r, floa
     float* x = a.k.x + (size_t)b * D + r;
     *x = *x + y;
   } else if constexpr (MODE == MODE_FC) {
-    a.k.g[(size_t)b * F + r] = gelu_tanh(y);
+    a.k.g[(size_t)b * F + r] = Q8 ? gelu_tanh(y) : gelu_f32(y);
   } else {
     a.logits[(size_t)b * V + r] = y;
   }
@@ -383,7 +384,7 @@ __global__ __launch_bounds__(64 * q8_waves(MODE)) void k_q8proj(const ProjArgs a
     float y = qm == 1 ? q8_dot<K>(wc[rr], swl[rr], xc, xsc, ca) : q8_dot_groups<K>(wc[rr], swl[rr], xc, xsc, qm);
     y = y + proj_bias<MODE>(a, r);
     if (cap && lane == 0) ((float*)(cap + cl.y))[r] = y;
-    if (lane == 0) proj_store<MODE>(a, 0, r, y);
+    if (lane == 0) proj_store<MODE, true>(a, 0, r, y);
   }
 }
 

@@ -404,6 +404,20 @@ __device__ __forceinline__ float gelu_tanh(float u) {
   return (0.5f * u) * (1.0f + t);
 }
 
+// The binary32 path's GELU: the same tanh form, with exp(2|z|) from the hardware
+// base-2 exponential and 2/(e + 1) from the hardware reciprocal (a few ulp from
+// gelu_tanh).  The int8 path keeps gelu_tanh, whose exponential is the specified one;
+// every binary32 path uses this one, so they stay identical to each other.
+__device__ __forceinline__ float gelu_f32(float u) {
+  const float c = 0.7978845608028654f;
+  const float inner = u + 0.044715f * (u * u * u);
+  const float z = c * inner;
+  const float e = __builtin_amdgcn_exp2f(2.8853900817779268f * fabsf(z));  // 2 log2(e) |z|
+  const float t0 = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+  const float t = z < 0.0f ? -t0 : t0;
+  return (0.5f * u) * (1.0f + t);
+}
+
 // ---- sequential-order LayerNorm (the int8 path) -----------------------------
 // The int8 path quantizes LayerNorm outputs, so a one-ulp difference in an output
 // can move a code across a rounding boundary; its LayerNorm therefore takes every

@@ -891,7 +891,7 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
           y = q8_dot768q(R.c[UPW + k], R.sc[UPW + k], S.xc, S.xsc, ca);
         }
         y = y + R.b[UPW + k];
-        const float gy = gelu_tanh(y);
+        const float gy = Q8 ? gelu_tanh(y) : gelu_f32(y);
         if (store_lane(64)) st_loc(own ? loc + LO_G + n : sinkw, pack(gy, E));
         if (CAP && own && lane == 0) ((float*)(a.capture + cap_offset(l, M_FC) + cap_item(M_FC).y))[r] = y;
       }

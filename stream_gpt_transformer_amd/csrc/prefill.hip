@@ -229,7 +229,7 @@ __global__ __launch_bounds__(G16_NTH) void k_gemm16(const float* __restrict__ A,
     const int row = 16 * wave + 4 * kg + r;
     if (row >= M) continue;
     float y = (acc[0][r] + acc[1][r]) + bv;
-    if (GELU) y = gelu_tanh(y);
+    if (GELU) y = gelu_f32(y);
     C[(size_t)row * ldc + col] = y;
   }
 }
