@@ -404,6 +404,10 @@ __device__ __forceinline__ float gelu_tanh(float u) {
   return (0.5f * u) * (1.0f + t);
 }
 
+// The binary32 path's exponential for arguments <= 0 (softmax): the hardware base-2
+// exponential of x*log2(e), within a few ulp of exp_spec.
+__device__ __forceinline__ float exp_f32(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
 // The binary32 path's GELU: the same tanh form, with exp(2|z|) from the hardware
 // base-2 exponential and 2/(e + 1) from the hardware reciprocal (a few ulp from
 // gelu_tanh).  The int8 path keeps gelu_tanh, whose exponential is the specified one;
@@ -632,7 +636,7 @@ __device__ __forceinline__ void wave_lds_wait() { asm volatile("s_waitcnt lgkmcn
 //   P_t,r = ((a.x + a.y) + (a.z + a.w)) with a = the float4 sum over i = 0..3
 //     ascending of q[16r+4i..] * K_t[16r+4i..] (quarter r of the 64 dims);
 //   s_t = ((P_t,0 + P_t,1) + (P_t,2 + P_t,3)) * 0.125   (1/sqrt(64));
-//   m = max_t s_t;  e_t = exp_spec(s_t - m);
+//   m = max_t s_t;  e_t = exp_f32(s_t - m);
 //   Z = Z_0 + Z_1 with Z_w = wave_sum of e_t over t in [64w, 64w+64);
 //   w_t = e_t * rcp(Z) (the hardware reciprocal);
 //   p_b = sum over t in [8b, 8b+8), t < npos, ascending, of w_t*V_t,d (b < 16);
@@ -725,8 +729,8 @@ __device__ __forceinline__ float attn_compute(AttnSmem& sm, int npos, int nthr) 
     const float s0 = lane < npos ? sm.w[lane] : -INFINITY;
     const float s1 = 64 + lane < npos ? sm.w[64 + lane] : -INFINITY;
     const float m = fmaxf(wave_max(s0), wave_max(s1));
-    const float e0 = lane < npos ? exp_spec(s0 - m) : 0.0f;
-    const float e1 = 64 + lane < npos ? exp_spec(s1 - m) : 0.0f;
+    const float e0 = lane < npos ? exp_f32(s0 - m) : 0.0f;
+    const float e1 = 64 + lane < npos ? exp_f32(s1 - m) : 0.0f;
     const float Z = wave_sum(e0) + wave_sum(e1);
     const float rz = __builtin_amdgcn_rcpf(Z);  // Z >= 1 (the maximum's term is 1)
     sm.w[lane] = e0 * rz;

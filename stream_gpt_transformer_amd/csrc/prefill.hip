@@ -388,10 +388,11 @@ __global__ __launch_bounds__(PF_ATT_THREADS) void k_pf_attn(const float* __restr
     const float m = wave_max(fmaxf(s[0], s[1]));
     float e[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) e[u] = lane + 64 * u <= t ? exp_spec(s[u] - m) : 0.0f;
+    for (int u = 0; u < 2; ++u) e[u] = lane + 64 * u <= t ? exp_f32(s[u] - m) : 0.0f;
     const float Z = wave_sum(e[0] + e[1]);
+    const float rz = __builtin_amdgcn_rcpf(Z);  // Z >= 1 (the maximum's term is 1)
 #pragma unroll
-    for (int u = 0; u < 2; ++u) sm.w[wave][lane + 64 * u] = e[u] / Z;
+    for (int u = 0; u < 2; ++u) sm.w[wave][lane + 64 * u] = e[u] * rz;
   } else {
 #pragma unroll
     for (int u = 0; u < 2; ++u) sm.w[wave][lane + 64 * u] = 0.0f;
