@@ -69,13 +69,28 @@ constexpr int NG_PR = F / 64;            // int8 MLP-projection groups (48)
 constexpr int NCW = NWV - 1;             // compute waves of a regular unit (waves 1..7)
 constexpr int UPW = 4;                   // units per compute wave per phase
 #ifndef FUSED_NHS_F32
-#define FUSED_NHS_F32 8
+#define FUSED_NHS_F32 16
 #endif
 template <bool Q8>
 constexpr int nhs() { return Q8 ? 12 : FUSED_NHS_F32; }  // head-row slots per wave
 constexpr int F32_SLOTS = 3 * FUSED_NHS_F32 > 24 ? 3 * FUSED_NHS_F32 : 24;  // f4 slots of an fp32 wave
-constexpr int HEAD_STRIDE = NWV * GRID;  // head rows hw, hw + 2048, ...
-constexpr int HEAD_MAX_ROWS = (V + HEAD_STRIDE - 1) / HEAD_STRIDE;
+// Head rows: the 1,024 waves of each set take rows first + 1024 k, k < n.  Set 0 is
+// idle during block 11, so its waves load their first slots while that block runs;
+// set 1's only after it.  Set 0 therefore takes more rows per wave (HEAD_N0) than
+// set 1 (HEAD_TOTAL - HEAD_N0), so both have about as many rows left to stream when
+// the head starts.
+constexpr int HEAD_SET_WAVES = NWV * GRID / 2;
+constexpr int HEAD_TOTAL = (V + HEAD_SET_WAVES - 1) / HEAD_SET_WAVES;  // rows per set-0 + set-1 wave pair (50)
+#ifndef FUSED_HEAD_N0_F32
+#define FUSED_HEAD_N0_F32 31
+#endif
+template <bool Q8>
+constexpr int head_n0() { return Q8 ? HEAD_TOTAL / 2 : FUSED_HEAD_N0_F32; }
+template <bool Q8>
+constexpr int head_nmax() { return head_n0<Q8>() > HEAD_TOTAL - head_n0<Q8>() ? head_n0<Q8>() : HEAD_TOTAL - head_n0<Q8>(); }
+struct HeadRows {
+  int first, n;  // rows first + HEAD_SET_WAVES * k, k < n
+};
 #ifndef FUSED_DELAY
 #define FUSED_DELAY 0
 #endif
@@ -98,7 +113,9 @@ static_assert(H > NX && H <= 2 * NX, "one or two heads per XCD");
 static_assert(UPW * NCW * (NQ - 2) >= 2 * 192 && UPW * NCW * (NQ - 2) >= GS && UPW * NCW * (NQ - 2) >= D / 2 &&
                   UPW * NCW * (NQ - 2) >= GPS * D / 16,
               "units per phase");
-static_assert(HEAD_MAX_ROWS > nhs<true>() && HEAD_MAX_ROWS > nhs<false>(), "head ring");
+static_assert(HEAD_TOTAL - head_n0<true>() >= nhs<true>() && head_n0<true>() >= nhs<true>() &&
+                  HEAD_TOTAL - head_n0<false>() >= nhs<false>() && head_n0<false>() >= nhs<false>(),
+              "head ring");
 
 __device__ __forceinline__ int heads_of(int X) { return X + NX < H ? 2 : 1; }
 
@@ -493,9 +510,9 @@ __device__ __forceinline__ void load_head(WRegs<Q8, H16>& R, const Weights& w, i
   }
 }
 template <bool Q8, bool H16>
-__device__ __forceinline__ void load_head_slots(WRegs<Q8, H16>& R, const Weights& w, int hw) {
+__device__ __forceinline__ void load_head_slots(WRegs<Q8, H16>& R, const Weights& w, HeadRows hr) {
 #pragma unroll
-  for (int s = 0; s < nhs<Q8>(); ++s) load_head<Q8, H16>(R, w, s, hw + s * HEAD_STRIDE);
+  for (int s = 0; s < nhs<Q8>(); ++s) load_head<Q8, H16>(R, w, s, hr.first + s * HEAD_SET_WAVES);
 }
 
 // int8 group accumulator of a quad: lanes 4k..4k+3 each hold 16 codes of one group.
@@ -542,6 +559,13 @@ struct Ctx {
   u64* loc;    // this XCD's local words, block 0
   u64* glb;    // global words, block 0
 };
+// The head rows of wave `wave` of this workgroup: index i < 1,024 within its set.
+template <bool Q8>
+__device__ __forceinline__ HeadRows head_rows_of(const Ctx& c, int wave) {
+  const int i = wave * (GRID / 2) + ((int)blockIdx.x % NX) + NX * c.q;
+  constexpr int n0 = head_n0<Q8>();
+  return c.set == 0 ? HeadRows{i, n0} : HeadRows{n0 * HEAD_SET_WAVES + i, HEAD_TOTAL - n0};
+}
 __device__ __forceinline__ u64* loc_of(const Ctx& c, int l) { return c.loc + (size_t)l * FX_LOC_PER_LAYER; }
 __device__ __forceinline__ u64* glb_of(const Ctx& c, int l) { return c.glb + (size_t)l * FX_GLB_PER_LAYER; }
 
@@ -660,11 +684,13 @@ __device__ __forceinline__ void capture_input(const FusedArgs& a, FusedSmem& S, 
 }
 
 // ---- the tied head -------------------------------------------------------------
-// Head rows of wave hw (rows hw + k*HEAD_STRIDE): the first NS slots were loaded
-// ahead; each slot is refilled with the row NS further on as soon as it has been
-// used.  Rows past the vocabulary compute on the last row and store to the sink.
+// Head rows of a wave (hr): the first NS slots were loaded ahead; each slot is
+// refilled with the row NS further on as soon as it has been used.  Rows past the
+// vocabulary compute on the last row and store to the sink.
 template <bool Q8, bool CAP, bool H16>
-__device__ __forceinline__ void head_rows(const FusedArgs a, FusedSmem& S, WRegs<Q8, H16>& R, int hw, float* sinkf) {
+__device__ __forceinline__ void head_rows(const FusedArgs a, FusedSmem& S, WRegs<Q8, H16>& R, HeadRows hr,
+                                          float* sinkf) {
+  constexpr int NMAX = head_nmax<Q8>();
   const int lane = lane_id();
   constexpr int NS = nhs<Q8>();
   f4 x[3];
@@ -674,15 +700,17 @@ __device__ __forceinline__ void head_rows(const FusedArgs a, FusedSmem& S, WRegs
   }
   if constexpr (!Q8) {
 #pragma unroll
-    for (int k = 0; k < HEAD_MAX_ROWS; ++k) {
+    for (int k = 0; k < NMAX; ++k) {
       // keep the loads in slot order: at most NHS rows in flight per wave
       __builtin_amdgcn_sched_barrier(0);
-      const int r = hw + k * HEAD_STRIDE;
-      const int s = k % NS;
-      const float y = dot_slots(R, 3 * s, x);
-      *(r < V ? a.logits + r : sinkf) = y;
-      if (k + NS < HEAD_MAX_ROWS) load_head<Q8, H16>(R, a.w, s, r + NS * HEAD_STRIDE);
-      if (k == NS - 1 && lane == 0 && (threadIdx.x >> 6) == 1) stamp(a.trace, 57);
+      if (k < hr.n) {  // a uniform guard, not a break: the loop stays fully unrolled
+        const int r = hr.first + k * HEAD_SET_WAVES;
+        const int s = k % NS;
+        const float y = dot_slots(R, 3 * s, x);
+        *(r < V ? a.logits + r : sinkf) = y;
+        if (k + NS < hr.n) load_head<Q8, H16>(R, a.w, s, r + NS * HEAD_SET_WAVES);
+        if (k == NS - 1 && lane == 0 && (threadIdx.x >> 6) == 1) stamp(a.trace, 57);
+      }
     }
   } else {
     // int8: an int8 row is a long dependent chain for few bytes, so HG rows are
@@ -690,13 +718,13 @@ __device__ __forceinline__ void head_rows(const FusedArgs a, FusedSmem& S, WRegs
     constexpr int HG = 4;
     static_assert(NS % HG == 0, "head groups");
 #pragma unroll
-    for (int k0 = 0; k0 < HEAD_MAX_ROWS; k0 += HG) {
+    for (int k0 = 0; k0 < NMAX; k0 += HG) {
       __builtin_amdgcn_sched_barrier(0);
       float y[HG];
 #pragma unroll
       for (int u = 0; u < HG; ++u) {
-        const int k = k0 + u, r = hw + k * HEAD_STRIDE, s = k % NS;
-        if (k < HEAD_MAX_ROWS) {
+        const int k = k0 + u, r = hr.first + k * HEAD_SET_WAVES, s = k % NS;
+        if (k < hr.n) {
           int32_t* ca = CAP && r < V ? (int32_t*)(a.capture + cap_offset(0, M_HEAD) + cap_item(M_HEAD).acc) + (size_t)r * 12
                                      : nullptr;
           y[u] = q8_dot768q(R.c[s], R.sc[s], S.xc, S.xsc, ca);
@@ -704,11 +732,11 @@ __device__ __forceinline__ void head_rows(const FusedArgs a, FusedSmem& S, WRegs
       }
 #pragma unroll
       for (int u = 0; u < HG; ++u) {
-        const int k = k0 + u, r = hw + k * HEAD_STRIDE, s = k % NS;
-        if (k < HEAD_MAX_ROWS) {
+        const int k = k0 + u, r = hr.first + k * HEAD_SET_WAVES, s = k % NS;
+        if (k < hr.n) {
           if (CAP && r < V && lane == 0) ((float*)(a.capture + cap_offset(0, M_HEAD) + cap_item(M_HEAD).y))[r] = y[u];
           *(r < V ? a.logits + r : sinkf) = y[u];
-          if (k + NS < HEAD_MAX_ROWS) load_head<Q8, H16>(R, a.w, s, r + NS * HEAD_STRIDE);
+          if (k + NS < hr.n) load_head<Q8, H16>(R, a.w, s, r + NS * HEAD_SET_WAVES);
         }
       }
       if (k0 + HG == NS && lane == 0 && (threadIdx.x >> 6) == 1) stamp(a.trace, 57);
@@ -819,7 +847,6 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
   const uint32_t E = c.E;
   u64* sinkw = a.sinkw + ((size_t)blockIdx.x * 8 + wave) * 16;
   float* sinkf = (float*)(sinkw + 8);
-  const int hw = wave * GRID + (int)blockIdx.x;  // first head row of this wave
   Units U;
   U.X = c.X;
   U.nh = c.nh;
@@ -953,7 +980,7 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
   // The first head rows, outside the loop, so the slots past the block weights are not
   // live across it.  (Filling the slots whose block rows are used up during set 1's last
   // block, to start its head stream earlier, delays that block's MLP terms: slower.)
-  load_head_slots<Q8, H16>(R, a.w, hw);
+  load_head_slots<Q8, H16>(R, a.w, head_rows_of<Q8>(c, wave));
   if (c.set == 0) rs_pr_poll<Q8>(a, S, c, L - 1, wave);
   wg_barrier();  // BT
 }
@@ -1099,7 +1126,7 @@ __device__ __forceinline__ void head_unit(const FusedArgs& a, FusedSmem& S, cons
     }
     wg_barrier();
   }
-  load_head_slots<Q8, H16>(R, a.w, wave * GRID + (int)blockIdx.x);
+  load_head_slots<Q8, H16>(R, a.w, head_rows_of<Q8>(c, wave));
   float x1p = 0.0f;
   if (c.set == 0) {
     if (wave == 0) x1p = x1_share(a, c, L - 1);
@@ -1135,7 +1162,7 @@ __global__ __launch_bounds__(FT, 1) void k_fused(const FusedArgs a) {
   c.loc = a.fx + (size_t)c.X * L * FX_LOC_PER_LAYER;
   c.glb = a.fx + LOC_WORDS;
   float* sinkf = (float*)(a.sinkw + ((size_t)blockIdx.x * 8 + wave) * 16 + 8);
-  const int hw = wave * GRID + (int)blockIdx.x;  // first head row of this wave
+  const HeadRows hr = head_rows_of<Q8>(c, wave);  // this wave's head rows
 
   WRegs<Q8, H16> R;
   if (c.head) head_unit<Q8, CAP, TOKP, H16>(a, S, c, R, wave);
@@ -1144,7 +1171,7 @@ __global__ __launch_bounds__(FT, 1) void k_fused(const FusedArgs a) {
 
   // ---- the tied head: every wave takes its head rows (the first ones are in its
   // registers already, except on wave 0 of a regular unit)
-  if (!c.head && wave == 0) load_head_slots<Q8, H16>(R, a.w, hw);
+  if (!c.head && wave == 0) load_head_slots<Q8, H16>(R, a.w, hr);
   wg_barrier();  // x12 is in LDS
   if constexpr (Q8) {
     layernorm_seq_wg<2>(S.xs, S.lnf[0], S.lnf[1], S.xn, S.lntmp, seq_tab(S), S.xc, S.xsc);
@@ -1152,7 +1179,7 @@ __global__ __launch_bounds__(FT, 1) void k_fused(const FusedArgs a) {
     if (CAP && blockIdx.x == 0 && wave == 0) capture_input(a, S, 0, M_HEAD, S.xn, 0, D, lane, 64);
   }
   if (lane == 0 && wave == 1) stamp(a.trace, 55);
-  head_rows<Q8, CAP, H16>(a, S, R, hw, sinkf);
+  head_rows<Q8, CAP, H16>(a, S, R, hr, sinkf);
   if (lane == 0 && wave == 1) stamp(a.trace, 50);
 
   // Epilogue: the last workgroup to finish checks the placement (XCD(b) - b one
