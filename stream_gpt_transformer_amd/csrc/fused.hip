@@ -84,8 +84,11 @@ constexpr int HEAD_TOTAL = (V + HEAD_SET_WAVES - 1) / HEAD_SET_WAVES;  // rows p
 #ifndef FUSED_HEAD_N0_F32
 #define FUSED_HEAD_N0_F32 31
 #endif
+#ifndef FUSED_HEAD_N0_Q8
+#define FUSED_HEAD_N0_Q8 31
+#endif
 template <bool Q8>
-constexpr int head_n0() { return Q8 ? HEAD_TOTAL / 2 : FUSED_HEAD_N0_F32; }
+constexpr int head_n0() { return Q8 ? FUSED_HEAD_N0_Q8 : FUSED_HEAD_N0_F32; }
 template <bool Q8>
 constexpr int head_nmax() { return head_n0<Q8>() > HEAD_TOTAL - head_n0<Q8>() ? head_n0<Q8>() : HEAD_TOTAL - head_n0<Q8>(); }
 struct HeadRows {
