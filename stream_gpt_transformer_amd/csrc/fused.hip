@@ -94,17 +94,9 @@ constexpr int head_nmax() { return head_n0<Q8>() > HEAD_TOTAL - head_n0<Q8>() ? 
 struct HeadRows {
   int first, n;  // rows first + HEAD_SET_WAVES * k, k < n
 };
-#ifndef FUSED_DELAY
-#define FUSED_DELAY 0
-#endif
-#ifndef FUSED_DEFER
-#define FUSED_DEFER 1
-#endif
-#ifndef FUSED_MASKED
-#define FUSED_MASKED 0
-#endif
-// lanes that store a value every lane of the group holds: one per group, or all
-__device__ __forceinline__ bool store_lane(int group) { return !FUSED_MASKED || (lane_id() % group) == 0; }
+// Where every lane of a group holds the same value, every lane stores it (one wave
+// instruction, the same address in each lane of the group): masking all but one lane
+// per group measured slower.
 // Output projection of a head unit: 768 outputs x 64 inputs as 1536 half dots of
 // 32 inputs, three per thread.
 constexpr int O_HALF_PER_THREAD = 2 * D / FT;
@@ -610,7 +602,7 @@ __device__ __forceinline__ float embed(const FusedArgs& a, float* xs, int q) {
 // rows: at launch both sets would otherwise share the HBM bandwidth and delay block
 // 0, while set 1's weights are only needed a block later.
 __device__ __forceinline__ void defer_set1(const Ctx& c, uint32_t* hdr) {
-  if (!FUSED_DEFER || c.set == 0) return;
+  if (c.set == 0) return;
   float v[1];
   poll<1, true>(loc_of(c, 0) + LO_QKV, 1, [](int k) { return k; }, c.E, v, hdr);
 }
@@ -820,11 +812,6 @@ __device__ __forceinline__ void regular_io(const FusedArgs& a, FusedSmem& S, con
     }
     // the next block of this set: its LayerNorm parameters and reduce-scatter biases
     const int ln = l + 2;
-    if (FUSED_DELAY && ln < L) {
-      float v[12];
-      poll<12, true>(loc + LO_X2, D, [](int k) { return k; }, E, v, hdr);
-      wg_barrier();  // BD
-    }
     if (ln < L) {
       stage_ln(S, a.w, ln);
       bo = small_p(a.w, ln, sp::B_O)[o];
@@ -891,10 +878,8 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
           y = q8_dot768q(R.c[k], R.sc[k], S.xc, S.xsc, ca);
         }
         y = y + R.b[k];
-        if (store_lane(64)) {
-          st_loc(own ? loc + LO_QKV + n : sinkw, pack(y, E));
-          *(own && r >= D ? a.cache + ((size_t)a.pos * L + l) * KV_ROW + (r - D) : sinkf) = y;
-        }
+        st_loc(own ? loc + LO_QKV + n : sinkw, pack(y, E));
+        *(own && r >= D ? a.cache + ((size_t)a.pos * L + l) * KV_ROW + (r - D) : sinkf) = y;
         if (CAP && own && lane == 0) ((float*)(a.capture + cap_offset(l, M_QKV) + cap_item(M_QKV).y))[r] = y;
       }
     }
@@ -922,7 +907,7 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
         }
         y = y + R.b[UPW + k];
         const float gy = Q8 ? gelu_tanh(y) : gelu_f32(y);
-        if (store_lane(64)) st_loc(own ? loc + LO_G + n : sinkw, pack(gy, E));
+        st_loc(own ? loc + LO_G + n : sinkw, pack(gy, E));
         if (CAP && own && lane == 0) ((float*)(a.capture + cap_offset(l, M_FC) + cap_item(M_FC).y))[r] = y;
       }
     }
@@ -956,7 +941,7 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
         }
         // lanes 0..31 store row 2u, lanes 32..63 row 2u+1
         const int half = lane >> 5;
-        if (store_lane(32)) st_sc1(own ? glb + GL_P + (size_t)U.X * D + 2 * u + half : sinkw, pack(half ? p1 : p0, E));
+        st_sc1(own ? glb + GL_P + (size_t)U.X * D + 2 * u + half : sinkw, pack(half ? p1 : p0, E));
       }
     } else {
 #pragma unroll
@@ -967,13 +952,12 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
         const i4 xv = *(const i4*)(S.xc + 64 * g + 16 * (lane % 4));
         const int acc = quad_acc(R.c[2 * UPW + k], xv);
         const float t = ((float)acc * R.sc[2 * UPW + k]) * S.xsc[g];
-        if (store_lane(4)) st_sc1(own ? glb + GL_P + (size_t)g * D + i : sinkw, pack(t, E));
+        st_sc1(own ? glb + GL_P + (size_t)g * D + i : sinkw, pack(t, E));
         if (CAP && own && lane % 4 == 0)
           ((int32_t*)(a.capture + cap_offset(l, M_PR) + cap_item(M_PR).acc))[(size_t)i * NG_PR + g] = acc;
       }
     }
     if (wave == 1) dstamp(a.trace, l, 63);
-    if (FUSED_DELAY && l + 2 < L) wg_barrier();  // BD: the other set has its block input
     // this block is done: the weights of the set's next block (or the first head rows).
     // The MLP terms have reached memory before that stream starts: stores still queued
     // behind a wave's weight loads would hold up the other set's reduce-scatter.
@@ -1102,7 +1086,7 @@ __device__ __forceinline__ void head_unit(const FusedArgs& a, FusedSmem& S, cons
         t = ((float)acc * R.sc[k]) * S.xsc[0];
         if (CAP && half == 0) ((int32_t*)(a.capture + cap_offset(l, M_O) + cap_item(M_O).acc))[(size_t)i * H + h] = acc;
       }
-      if (store_lane(2)) st_sc1(glb + i, pack(t, E));
+      st_sc1(glb + i, pack(t, E));
     }
     if (wave == 1) dstamp(a.trace, l, 56);
     if (wave == 0) {
@@ -1111,14 +1095,6 @@ __device__ __forceinline__ void head_unit(const FusedArgs& a, FusedSmem& S, cons
     }
     wg_barrier();  // the keys/values of block l are no longer read
     const int ln = l + 2;
-    if (FUSED_DELAY && ln < L) {
-      // start streaming once the other set has gathered its block input
-      if (wave == 0) {
-        float v[12];
-        poll<12, true>(loc_of(c, l) + LO_X2, D, [](int k) { return k; }, E, v, hdr);
-      }
-      wg_barrier();
-    }
     if (ln < L) {
       load_o_head<Q8, H16>(R, (char*)&S.pr, a.w, ln, h);
       stage_kv(a, S, ln, h);
