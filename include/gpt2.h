@@ -248,10 +248,15 @@ int gpt2_workspace_status(const void* ws_host_copy);
 void gpt2_test_force_phase_kernels(int on);
 
 /* Timeline of the single-launch step: with trace_dev non-null (device buffer of
- * grid x 64 uint64), later steps write a 100 MHz timestamp per workgroup at each
- * phase boundary (slot 0 start; 1+4l+{0..3} inputs of the QKV/O/FC/MLP-projection
- * phases of block l received; 49 head input received; 50 head rows done; 51 end).
- * NULL turns it off. */
+ * 256 x 64 uint64, row = workgroup), later steps write the device's 100 MHz
+ * real-time counter per workgroup at its phase boundaries: slot 0 start; for
+ * block l, on the units of the set that computes it, 1+4l the block input x in LDS
+ * (head units: their share of the previous reduce-scatter done), 2+4l the unit's
+ * QKV rows published (head units: attention output ready), 3+4l x1 in LDS (head
+ * units: x1 share published), 4+4l the XCD's GELU slice in LDS (regular units);
+ * 49 head input received, 55 head LayerNorm done, 50 head rows done, 51 end;
+ * 52..63 finer points inside block 6.  Slots a unit does not reach are left as
+ * they were.  The values computed are unchanged.  NULL turns it off. */
 void gpt2_test_fused_trace(void* trace_dev);
 
 /* Prefill that hands the session over to the cached step.  This is an extension:

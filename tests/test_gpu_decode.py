@@ -129,3 +129,50 @@ def test_rejections_leave_outputs_untouched():
     assert g.gpt2_q8_cached_step(mf.handle, c, 0, 0, 0, ws, l) == g.GPT2_ENOTPACKED
     torch.cuda.synchronize()
     assert torch.all(lg == 7.0) and torch.all(cache == 0)
+
+
+@pytest.mark.parametrize("q8", [False, True], ids=["fp32", "int8"])
+def test_timestamp_hook_changes_no_bits_and_orders_phases(q8):
+    """With the single-launch step's timestamp hook on, a session computes the same bits.
+    Every workgroup stamps its start, head input, head rows done and end in that order;
+    the units of the set that computes block l stamp that block's phase inputs in causal
+    order (regular units: x in, own QKV rows published, x1 in, GELU slice in; head
+    units: reduce-scatter share, attention output, x1 published), and no unit stamps a
+    block of the other set.  Turned off, the hook writes nothing."""
+    need_gpu()
+    m = model()
+    toks = synth.make_tokens(23, 6)
+    ref, cref = gpu_session(m, toks, q8=q8)
+    trace = torch.zeros(256 * 64, dtype=torch.int64, device="cuda")
+    g.gpt2_test_fused_trace(trace.data_ptr())
+    try:
+        got, cgot = gpu_session(m, toks, q8=q8)  # the trace holds the last step's stamps
+    finally:
+        g.gpt2_test_fused_trace(None)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    assert np.array_equal(cgot.view(np.uint32), cref.view(np.uint32))
+    tr = trace.view(256, 64).cpu().numpy()
+    for b in range(256):
+        X, rank = b % 8, b // 8
+        st, q = rank % 2, rank // 2
+        head = q < (2 if X < 4 else 1)
+        t = tr[b]
+        assert 0 < t[0] <= t[49] <= t[55] <= t[50] <= t[51], (b, t[[0, 49, 55, 50, 51]])
+        slots = (1, 2, 3) if head else (1, 2, 3, 4)
+        prev = t[0]
+        for l in range(12):
+            s = [t[k + 4 * l] for k in slots]
+            if l % 2 != st:
+                assert all(v == 0 for v in s), (b, l, s)
+                continue
+            assert prev <= s[0] and all(s[i] <= s[i + 1] for i in range(len(s) - 1)), (b, l, prev, s)
+            prev = s[-1]
+        assert prev <= t[49]
+    # off: a later step leaves the buffer untouched
+    trace.zero_()
+    cache = m.new_cache(1)
+    lg = torch.empty(g.GPT2_VOCAB, dtype=torch.float32, device="cuda")
+    m.step(cache, 0, int(toks[0]), lg, q8=q8)
+    torch.cuda.synchronize()
+    assert int(trace.abs().sum().item()) == 0
+    assert m.status() == 0
