@@ -234,23 +234,16 @@ __device__ __forceinline__ void gather(const u64* src, uint32_t E, float* dst, u
 }
 
 // Reduce-scatter: the unit's outputs o = RSN*q + i (i < RSN) of a sum of NT terms
-// stored term-major at terms[t*D + o].  Lanes i < RSN return
-// y = 0 + term_0 + ... + term_{NT-1} (fixed order).
+// stored term-major at terms[t*D + o], read by one wave with lane i holding the NT
+// terms of output RSN*q + i (lanes >= RSN read lane RSN-1's words).  Lanes i < RSN
+// return y = 0 + term_0 + ... + term_{NT-1} (fixed order).
 template <int NT>
-__device__ __forceinline__ float reduce_scatter(const u64* terms, int q, uint32_t E, float* scratch, uint32_t* hdr) {
-  constexpr int N = NT * RSN, PL = (N + 63) / 64;
-  const int lane = lane_id();
-  float v[PL];
-  poll<PL, false>(terms, N, [&](int k) { return (k / RSN) * D + RSN * q + k % RSN; }, E, v, hdr);
-#pragma unroll
-  for (int j = 0; j < PL; ++j)
-    if (lane + 64 * j < N) scratch[lane + 64 * j] = v[j];
-  wave_lds_sync();
+__device__ __forceinline__ float rs_lanes(const u64* terms, int q, uint32_t E, uint32_t* hdr) {
+  float v[NT];
+  poll<NT, false>(terms, 64 * NT, [&](int k) { return (k >> 6) * D + RSN * q + min(k & 63, RSN - 1); }, E, v, hdr);
   float y = 0.0f;
-  if (lane < RSN) {
-#pragma unroll 8
-    for (int t = 0; t < NT; ++t) y = y + scratch[t * RSN + lane];
-  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) y = y + v[t];
   return y;
 }
 
@@ -608,12 +601,14 @@ __device__ __forceinline__ void defer_set1(const Ctx& c, uint32_t* hdr) {
 }
 
 // Reduce-scatter of block l's MLP projection by a unit of the set that computes
-// block l+1: every wave polls its share of the terms (rs_pr_poll), then after a
-// workgroup barrier wave 0 forms x_{l+1}[o] = x1_l[o] + (sum + bias) and publishes
-// it into the XCD's copy (rs_pr).  Lanes < RSN return it.
+// block l+1: wave 0 forms x_{l+1}[o] = x1_l[o] + (sum + bias) and publishes it into
+// the XCD's copy (rs_pr); lanes < RSN return it.  int8 (48 group terms per output):
+// every wave first polls its share of the terms into LDS (rs_pr_poll), and rs_pr
+// adds them after a workgroup barrier.  fp32 (8 slice terms): rs_pr reads them
+// itself (rs_lanes), so the other waves take no part.
 template <bool Q8>
 __device__ __forceinline__ void rs_pr_poll(const FusedArgs& a, FusedSmem& S, const Ctx& c, int l, int wave) {
-  rs_poll_part<Q8 ? NG_PR : NX>(glb_of(c, l) + GL_P, c.q, c.E, S.rs, a.header, wave);
+  if constexpr (Q8) rs_poll_part<NG_PR>(glb_of(c, l) + GL_P, c.q, c.E, S.rs, a.header, wave);
 }
 // The unit's share of x1 of block l (lanes < RSN), published inside the XCD in the
 // middle of block l: the wave that takes the reduce-scatter reads it before it polls
@@ -626,7 +621,9 @@ __device__ __forceinline__ float x1_share(const FusedArgs& a, const Ctx& c, int 
 template <bool Q8, bool CAP>
 __device__ __forceinline__ float rs_pr(const FusedArgs& a, FusedSmem& S, const Ctx& c, int l, float bpr, float x1) {
   const int lane = lane_id();
-  float y = rs_sum<Q8 ? NG_PR : NX>(S.rs);
+  float y;
+  if constexpr (Q8) y = rs_sum<NG_PR>(S.rs);
+  else y = rs_lanes<NX>(glb_of(c, l) + GL_P, c.q, c.E, a.header);
   float xr = 0.0f;
   if (lane < RSN) {
     const int o = RSN * c.q + lane;
@@ -641,7 +638,7 @@ __device__ __forceinline__ float rs_pr(const FusedArgs& a, FusedSmem& S, const C
 template <bool Q8, bool CAP>
 __device__ __forceinline__ float rs_o(const FusedArgs& a, FusedSmem& S, const Ctx& c, int l, float xr, float bo) {
   const int lane = lane_id();
-  float y = reduce_scatter<H>(glb_of(c, l) + GL_O, c.q, c.E, S.rs, a.header);
+  float y = rs_lanes<H>(glb_of(c, l) + GL_O, c.q, c.E, a.header);
   float x1 = 0.0f;
   if (lane < RSN) {
     const int o = RSN * c.q + lane;
