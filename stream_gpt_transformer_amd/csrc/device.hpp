@@ -614,16 +614,6 @@ __device__ __forceinline__ void layernorm_seq_wg(const float* xs, const float* _
   }
 }
 
-// LayerNorm of a 768-vector in LDS by one wave (layernorm_frag), written to ys
-// (which may be xs).
-__device__ __forceinline__ void layernorm_lds(const float* xs, const float* __restrict__ gamma,
-                                              const float* __restrict__ beta, float* ys) {
-  f4 x[3];
-  load_frag<3>(x, xs);
-  layernorm_frag(x, gamma, beta);
-  store_frag<3>(ys, x);
-}
-
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations, not
 // for its outstanding global loads and stores (a __syncthreads would also wait for
 // every store of the wave to be acknowledged).

@@ -233,6 +233,19 @@ __device__ __forceinline__ void gather(const u64* src, uint32_t E, float* dst, u
   for (int j = 0; j < PL; ++j) dst[lane_id() + 64 * j] = v[j];
 }
 
+// All-gather of a 768-vector inside the XCD straight into the lane-fragment layout
+// (lane l: elements 256i + 4l .. 256i + 4l + 3, i < 3), the layout load_frag reads
+// from LDS, without the pass through LDS.
+__device__ __forceinline__ void gather_frag(const u64* src, uint32_t E, f4 (&x)[3], uint32_t* hdr) {
+  float v[12];
+  poll<12, true>(src, 768, [](int k) {
+    const int j = k >> 6;
+    return 256 * (j >> 2) + 4 * (k & 63) + (j & 3);
+  }, E, v, hdr);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) x[i] = f4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+}
+
 // Reduce-scatter: the unit's outputs o = RSN*q + i (i < RSN) of a sum of NT terms
 // stored term-major at terms[t*D + o], read by one wave with lane i holding the NT
 // terms of output RSN*q + i (lanes >= RSN read lane RSN-1's words).  Lanes i < RSN
@@ -738,8 +751,9 @@ __device__ __forceinline__ void head_rows(const FusedArgs a, FusedSmem& S, WRegs
 
 // ---- regular units -------------------------------------------------------------
 // Wave 0 receives (reduce-scatters, all-gathers) and holds no weights; it also
-// takes the block's two LayerNorms once for the workgroup (fp32: layernorm_lds into
-// xn and lntmp; int8: with the whole workgroup, layernorm_seq_wg).  Waves 1..7
+// takes the block's two LayerNorms once for the workgroup (fp32: layernorm_frag on x
+// and x1 gathered straight into registers, written to xn and lntmp; int8: with the
+// whole workgroup, layernorm_seq_wg).  Waves 1..7
 // compute from registers (and the fp32 MLP weights from LDS).  The two roles meet
 // at the same sequence of workgroup barriers.
 template <bool Q8, bool CAP, bool TOKP, bool H16>
@@ -768,19 +782,23 @@ __device__ __forceinline__ void regular_io(const FusedArgs& a, FusedSmem& S, con
     dstamp(a.trace, l, 52);
     wg_barrier();  // BA: the reduce-scatter terms are in LDS
     dstamp(a.trace, l, 53);
+    f4 xf[3];  // fp32: the block input in the lane-fragment layout
     if (l == 0) {
       xr = embed<TOKP>(a, S.xs, c.q);
+      if constexpr (!Q8) load_frag<3>(xf, S.xs);
     } else {
       xr = rs_pr<Q8, CAP>(a, S, c, l - 1, bpr, x1p);
       dstamp(a.trace, l, 54);
-      gather<12>(loc_of(c, l - 1) + LO_X2, E, S.xs, hdr);
+      if constexpr (Q8) gather<12>(loc_of(c, l - 1) + LO_X2, E, S.xs, hdr);
+      else gather_frag(loc_of(c, l - 1) + LO_X2, E, xf, hdr);
     }
     if (lane == 0) stamp(a.trace, 1 + 4 * l);
     if constexpr (Q8) {
       wg_barrier();  // the block input is in LDS
       layernorm_seq_wg<1>(S.xs, S.lnp[0], S.lnp[1], S.xn, S.lntmp, seq_tab(S), S.xc, S.xsc);
     } else {
-      layernorm_lds(S.xs, S.lnp[0], S.lnp[1], S.xn);  // once for the workgroup
+      layernorm_frag(xf, S.lnp[0], S.lnp[1]);  // once for the workgroup
+      store_frag<3>(S.xn, xf);
     }
     wg_barrier();  // B1: QKV (int8: its input codes are in LDS)
     if constexpr (Q8) {
@@ -788,13 +806,16 @@ __device__ __forceinline__ void regular_io(const FusedArgs& a, FusedSmem& S, con
     }
     xr = rs_o<Q8, CAP>(a, S, c, l, xr, bo);
     dstamp(a.trace, l, 56);
-    gather<12>(loc + LO_X1, E, S.x1s, hdr);
-    if (lane == 0) stamp(a.trace, 3 + 4 * l);
     if constexpr (Q8) {
+      gather<12>(loc + LO_X1, E, S.x1s, hdr);
+      if (lane == 0) stamp(a.trace, 3 + 4 * l);
       wg_barrier();  // x1 is in LDS
       layernorm_seq_wg<1>(S.x1s, S.lnp[2], S.lnp[3], S.xn, S.lntmp, seq_tab(S), S.xc, S.xsc);
     } else {
-      layernorm_lds(S.x1s, S.lnp[2], S.lnp[3], S.lntmp);
+      gather_frag(loc + LO_X1, E, xf, hdr);
+      if (lane == 0) stamp(a.trace, 3 + 4 * l);
+      layernorm_frag(xf, S.lnp[2], S.lnp[3]);
+      store_frag<3>(S.lntmp, xf);
     }
     wg_barrier();  // B3: FC (int8: its input codes are in LDS)
     if constexpr (Q8) {
