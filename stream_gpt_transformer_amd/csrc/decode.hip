@@ -255,7 +255,7 @@ __global__ __launch_bounds__(attn_threads<SEQ>()) void k_attn(const ProjArgs a) 
   auto kv = [&](int j) { return cache + ((size_t)j * L + l) * KV_ROW + h * DH; };
   attn_stage(sm, kv, npos, a.k.qkv + (size_t)b * D3 + h * DH, NT);
   __syncthreads();
-  const float o = SEQ ? attn_compute_seq(sm, npos) : attn_compute(sm, npos, NT);
+  const float o = SEQ ? attn_compute_seq(sm, npos) : attn_compute<NT>(sm, npos);
   if (threadIdx.x < DH) a.k.att[(size_t)b * D + h * DH + threadIdx.x] = o;
 }
 

@@ -631,8 +631,8 @@ __device__ __forceinline__ void wave_lds_wait() { asm volatile("s_waitcnt lgkmcn
 //   w_t = e_t * rcp(Z) (the hardware reciprocal);
 //   p_b = sum over t in [8b, 8b+8), t < npos, ascending, of w_t*V_t,d (b < 16);
 //   a_d = ((((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7))) + (((p8+p9)+(p10+p11))+((p12+p13)+(p14+p15)))).
-// Every value is the same for any block size of 128 or more threads (the work is
-// dealt out in fixed units).
+// Every value is the same for a block of 128, 256 or 512 threads (the work is dealt
+// out in fixed units).
 constexpr int ATT_VB = 16;  // key blocks of the weighted sum
 struct AttnSmem {
   float k[PMAX][DH + 4];  // padded rows, 16-byte aligned
@@ -691,9 +691,12 @@ __device__ __forceinline__ void attn_stage(AttnSmem& sm, RowPtr kv, int npos, co
 }
 
 // Returns a_d in threads 0..63 (d = thread index); other threads return 0.  Every
-// thread of the block (nthr threads, a multiple of 128) must call it; it
+// thread of the block (NTHR threads: 128, 256 or 512) must call it; it
 // synchronises the block through LDS-only barriers.
-__device__ __forceinline__ float attn_compute(AttnSmem& sm, int npos, int nthr) {
+template <int NTHR>
+__device__ __forceinline__ float attn_compute(AttnSmem& sm, int npos) {
+  static_assert(NTHR == 128 || NTHR == 256 || NTHR == 512, "key blocks are dealt out two per wave per pass");
+  constexpr int nthr = NTHR;
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
   // scores: unit u = 4*key + quarter, a lane quad per key
   for (int u = t; u < 4 * PMAX; u += nthr) {
@@ -727,16 +730,28 @@ __device__ __forceinline__ float attn_compute(AttnSmem& sm, int npos, int nthr) 
     sm.w[64 + lane] = e1 * rz;
   }
   lds_barrier();
-  for (int b = wv; b < ATT_VB; b += nthr / 64) {
-    float p = 0.0f;
-    const int j0 = 8 * b, j1 = min(j0 + 8, npos);
-    if (j1 - j0 == 8) {
+  // Two key blocks per pass (b0 and b0 + nw), their 32 LDS reads issued before the
+  // two chains; a key past npos is skipped (its row holds no value of this step).
+  constexpr int nw = NTHR / 64;
+  for (int b0 = wv; b0 < ATT_VB; b0 += 2 * nw) {
+    const int b1 = b0 + nw;
+    const int n0 = min(max(npos - 8 * b0, 0), 8), n1 = min(max(npos - 8 * b1, 0), 8);
+    float w0[8], v0[8], w1[8], v1[8];
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) p = p + sm.w[j0 + jj] * sm.v[j0 + jj][lane];
-    } else {
-      for (int j = j0; j < j1; ++j) p = p + sm.w[j] * sm.v[j][lane];
+    for (int jj = 0; jj < 8; ++jj) {
+      w0[jj] = sm.w[8 * b0 + jj];
+      v0[jj] = sm.v[8 * b0 + jj][lane];
+      w1[jj] = sm.w[8 * b1 + jj];
+      v1[jj] = sm.v[8 * b1 + jj][lane];
     }
-    sm.part[b][lane] = p;
+    float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      if (jj < n0) p0 = p0 + w0[jj] * v0[jj];
+      if (jj < n1) p1 = p1 + w1[jj] * v1[jj];
+    }
+    sm.part[b0][lane] = p0;
+    sm.part[b1][lane] = p1;
   }
   lds_barrier();
   float acc = 0.0f;

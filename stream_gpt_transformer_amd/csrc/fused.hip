@@ -1044,7 +1044,7 @@ __device__ __forceinline__ void head_unit(const FusedArgs& a, FusedSmem& S, cons
       sm.v[pos][lane] = v[2];
     }
     wg_barrier();
-    const float at = Q8 ? attn_compute_seq(sm, pos + 1) : attn_compute(sm, pos + 1, FT);
+    const float at = Q8 ? attn_compute_seq(sm, pos + 1) : attn_compute<FT>(sm, pos + 1);
     if (wave == 0) {
       S.att[lane] = at;
       if constexpr (Q8) {
