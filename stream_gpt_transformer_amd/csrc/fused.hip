@@ -68,6 +68,9 @@ constexpr int GPS = GS / 64;             // groups per slice (6)
 constexpr int NG_PR = F / 64;            // int8 MLP-projection groups (48)
 constexpr int NCW = NWV - 1;             // compute waves of a regular unit (waves 1..7)
 constexpr int UPW = 4;                   // units per compute wave per phase
+#ifndef FUSED_TRED
+#define FUSED_TRED 1
+#endif
 #ifndef FUSED_NHS_F32
 #define FUSED_NHS_F32 16
 #endif
@@ -339,6 +342,43 @@ __device__ __forceinline__ float dot_slots(WRegs<false, H16>& R, int s, const f4
   } else {
     return dot_frag<3>(*reinterpret_cast<f4(*)[3]>(&R.r[s]), x);
   }
+}
+
+// dot_slots' lane partial (before the wave sum)
+template <bool H16>
+__device__ __forceinline__ float dot_slots_lane(WRegs<false, H16>& R, int s, const f4 (&x)[3]) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const f4 w = wslot(R, s + i);
+    acc = fmaf(w.x, x[i].x, acc);
+    acc = fmaf(w.y, x[i].y, acc);
+    acc = fmaf(w.z, x[i].z, acc);
+    acc = fmaf(w.w, x[i].w, acc);
+  }
+  return acc;
+}
+// A compute wave's UPW rows of one phase (slots and biases B0..B0+UPW-1) reduced
+// together (wave_treduce: wave_sum's bits for each row): lane t returns row
+// k = treduce_out<UPW>(t % 16) plus its bias, and k.
+template <int B0, bool H16>
+__device__ __forceinline__ float rows_treduce(WRegs<false, H16>& R, const f4 (&x)[3], int& k) {
+  float lp[UPW];
+#pragma unroll
+  for (int j = 0; j < UPW; ++j) lp[j] = dot_slots_lane(R, 3 * (B0 + j), x);
+  k = treduce_out<UPW>(lane_id() & 15);
+  // the lane's bias by selects on register values (a select between elements of R.b
+  // would be folded into an indexed load, which puts R in scratch memory)
+  float bb[UPW];
+#pragma unroll
+  for (int j = 0; j < UPW; ++j) {
+    bb[j] = R.b[B0 + j];
+    asm volatile("" : "+v"(bb[j]));
+  }
+  float b = bb[0];
+#pragma unroll
+  for (int j = 1; j < UPW; ++j) b = k == j ? bb[j] : b;
+  return wave_treduce<UPW>(lp) + b;
 }
 
 // QKV row n of XCD X (n < 192 per head): head hh = n/192, part (q,k,v) = n%192/64,
@@ -882,6 +922,18 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
       f4 x[3];
       if constexpr (!Q8) load_frag<3>(x, S.xn);
       if (wave == 1) dstamp(a.trace, l, 60);
+      if constexpr (!Q8 && FUSED_TRED) {
+        // the four rows reduced together; lanes 0..3 hold rows 0, 1, 3, 2 and store them
+        int k;
+        const float y = rows_treduce<0>(R, x, k);
+        if (lane < UPW) {
+          const int n = U.qkv(k);
+          const bool own = n < 192 * U.nh;
+          const int r = qkv_row(U.X, own ? n : 0);
+          st_loc(own ? loc + LO_QKV + n : sinkw, pack(y, E));
+          *(own && r >= D ? a.cache + ((size_t)a.pos * L + l) * KV_ROW + (r - D) : sinkf) = y;
+        }
+      } else
 #pragma unroll
       for (int k = 0; k < UPW; ++k) {
         const int n = U.qkv(k);
@@ -910,6 +962,15 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
     {
       f4 x[3];
       if constexpr (!Q8) load_frag<3>(x, S.lntmp);
+      if constexpr (!Q8 && FUSED_TRED) {
+        int k;
+        const float y = rows_treduce<UPW>(R, x, k);
+        const float gy = gelu_f32(y);
+        if (lane < UPW) {
+          const int n = U.cw + U.cwn * k;
+          st_loc(n < GS ? loc + LO_G + n : sinkw, pack(gy, E));
+        }
+      } else
 #pragma unroll
       for (int k = 0; k < UPW; ++k) {
         const int n = U.cw + U.cwn * k;
