@@ -36,6 +36,9 @@ __device__ __forceinline__ f4 widen(const h4 h) { return __builtin_convertvector
 enum : int {
   DPP_QUAD_1032 = 0xB1,
   DPP_QUAD_2301 = 0x4E,
+  DPP_ROW_SL4 = 0x104,   // row_shl:4 (lane l of a row reads lane l + 4)
+  DPP_ROW_SL8 = 0x108,
+  DPP_ROW_SL12 = 0x10C,
   DPP_QUAD_3210 = 0x1B,
   DPP_ROW_MIRROR = 0x140,
   DPP_ROW_HALF_MIRROR = 0x141,
@@ -1007,6 +1010,67 @@ __device__ __forceinline__ float q8_dot768q(const i4 wc, float swq, const int8_t
   for (int g = 0; g < 12; ++g) y = y + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 4 * g));
   return y;
 }
+// Four int8 rows in quad layout evaluated together, each to q8_dot768q's value.
+// The exact group accumulators are summed over each quad transposed (partners
+// lane^1 then lane^2, each lane keeping one of the rows it shares with its partner),
+// so lane 4g + i holds row i's accumulator of group g; its term is
+// t = ((float)acc * sw_i) * sx_g, and the twelve ordered adds
+// y = ((0 + t_0) + t_1) + ... + t_11 run once for the four rows, lane i of row 0
+// taking t_g from lane 4g + i (a row shift inside rows 0..2 of the wave, those rows
+// first moved to row 0).  Lanes 0..3 return rows 0..3; other lanes, any value.
+// cap_acc[i] (or null) receives row i's twelve group accumulators.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add_f(float y, float t) {
+  return dpp_f<CTRL>(t) + y;  // t + y == y + t exactly
+}
+__device__ __forceinline__ float q8_dot768q_x4(const i4 (&wc)[4], const float (&swq)[4], const int8_t* xc,
+                                               const float* xsc, int32_t* const (&cap_acc)[4]) {
+  const int lane = lane_id();
+  const i4 xv = *(const i4*)(xc + 16 * min(lane, 47));
+  int p[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    int a = 0;
+    a = __builtin_amdgcn_sdot4(wc[k].x, xv.x, a, false);
+    a = __builtin_amdgcn_sdot4(wc[k].y, xv.y, a, false);
+    a = __builtin_amdgcn_sdot4(wc[k].z, xv.z, a, false);
+    a = __builtin_amdgcn_sdot4(wc[k].w, xv.w, a, false);
+    p[k] = a;
+  }
+  const bool b0 = (lane & 1) != 0, b1 = (lane & 2) != 0;
+  const int a0 = (b0 ? p[1] : p[0]) + dpp_i<DPP_QUAD_1032>(b0 ? p[0] : p[1]);  // row b0
+  const int a1 = (b0 ? p[3] : p[2]) + dpp_i<DPP_QUAD_1032>(b0 ? p[2] : p[3]);  // row 2 + b0
+  const int acc = (b1 ? a1 : a0) + dpp_i<DPP_QUAD_2301>(b1 ? a0 : a1);         // row lane & 3
+  const int i = lane & 3;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (cap_acc[k] && lane < 48 && i == k) cap_acc[k][lane >> 2] = acc;
+  // the lane's row scale by selects on register values (an indexed read of swq would
+  // put the caller's registers in scratch memory)
+  float sv[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    sv[k] = swq[k];
+    asm volatile("" : "+v"(sv[k]));
+  }
+  const float sw = i == 0 ? sv[0] : i == 1 ? sv[1] : i == 2 ? sv[2] : sv[3];
+  const float t = lane < 48 ? ((float)acc * sw) * xsc[min(lane >> 2, 11)] : 0.0f;
+  const float t1 = row1_to_row0(t), t2 = row2_to_row0(t);
+  float y = 0.0f + t;
+  y = dpp_add_f<DPP_ROW_SL4>(y, t);
+  y = dpp_add_f<DPP_ROW_SL8>(y, t);
+  y = dpp_add_f<DPP_ROW_SL12>(y, t);
+  y = y + t1;
+  y = dpp_add_f<DPP_ROW_SL4>(y, t1);
+  y = dpp_add_f<DPP_ROW_SL8>(y, t1);
+  y = dpp_add_f<DPP_ROW_SL12>(y, t1);
+  y = y + t2;
+  y = dpp_add_f<DPP_ROW_SL4>(y, t2);
+  y = dpp_add_f<DPP_ROW_SL8>(y, t2);
+  y = dpp_add_f<DPP_ROW_SL12>(y, t2);
+  return y;
+}
+
 // Codes of int8 row r of a [rows][768] matrix and its group scales in quad layout,
 // for q8_dot768q (nontemporal loads).  Lanes 48..63 hold copies of lane 47's codes
 // and scale: q8_dot768q takes no term from those lanes, so nothing here uses the

@@ -765,22 +765,30 @@ __device__ __forceinline__ void head_rows(const FusedArgs a, FusedSmem& S, WRegs
 #pragma unroll
     for (int k0 = 0; k0 < NMAX; k0 += HG) {
       __builtin_amdgcn_sched_barrier(0);
-      float y[HG];
+      if (k0 < hr.n) {
+        // the group's rows together (q8_dot768q_x4): lane u < 4 returns row k0 + u; a
+        // row past hr.n computes on a stale slot and is not stored
+        i4 wc[HG];
+        float sw[HG];
+        int32_t* ca[HG];
 #pragma unroll
-      for (int u = 0; u < HG; ++u) {
-        const int k = k0 + u, r = hr.first + k * HEAD_SET_WAVES, s = k % NS;
-        if (k < hr.n) {
-          int32_t* ca = CAP && r < V ? (int32_t*)(a.capture + cap_offset(0, M_HEAD) + cap_item(M_HEAD).acc) + (size_t)r * 12
-                                     : nullptr;
-          y[u] = q8_dot768q(R.c[s], R.sc[s], S.xc, S.xsc, ca);
+        for (int u = 0; u < HG; ++u) {
+          const int k = k0 + u, r = hr.first + k * HEAD_SET_WAVES, s = k % NS;
+          wc[u] = R.c[s];
+          sw[u] = R.sc[s];
+          ca[u] = CAP && k < hr.n && r < V
+                      ? (int32_t*)(a.capture + cap_offset(0, M_HEAD) + cap_item(M_HEAD).acc) + (size_t)r * 12
+                      : nullptr;
         }
-      }
+        const float y = q8_dot768q_x4(wc, sw, S.xc, S.xsc, ca);
+        if (lane < HG && k0 + lane < hr.n) {
+          const int r = hr.first + (k0 + lane) * HEAD_SET_WAVES;
+          if (CAP && r < V) ((float*)(a.capture + cap_offset(0, M_HEAD) + cap_item(M_HEAD).y))[r] = y;
+          *(r < V ? a.logits + r : sinkf) = y;
+        }
 #pragma unroll
-      for (int u = 0; u < HG; ++u) {
-        const int k = k0 + u, r = hr.first + k * HEAD_SET_WAVES, s = k % NS;
-        if (k < hr.n) {
-          if (CAP && r < V && lane == 0) ((float*)(a.capture + cap_offset(0, M_HEAD) + cap_item(M_HEAD).y))[r] = y[u];
-          *(r < V ? a.logits + r : sinkf) = y[u];
+        for (int u = 0; u < HG; ++u) {
+          const int k = k0 + u, r = hr.first + k * HEAD_SET_WAVES, s = k % NS;
           if (k + NS < hr.n) load_head<Q8, H16>(R, a.w, s, r + NS * HEAD_SET_WAVES);
         }
       }
@@ -933,6 +941,33 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
           st_loc(own ? loc + LO_QKV + n : sinkw, pack(y, E));
           *(own && r >= D ? a.cache + ((size_t)a.pos * L + l) * KV_ROW + (r - D) : sinkf) = y;
         }
+      } else if constexpr (Q8 && FUSED_TRED) {
+        // the four rows together (q8_dot768q_x4): lanes 0..3 hold rows 0..3
+        i4 wc[UPW];
+        float sw[UPW], bb[UPW];
+        int32_t* ca[UPW];
+#pragma unroll
+        for (int k = 0; k < UPW; ++k) {
+          const int n = U.qkv(k);
+          const bool own = n < 192 * U.nh;
+          wc[k] = R.c[k];
+          sw[k] = R.sc[k];
+          bb[k] = R.b[k];
+          asm volatile("" : "+v"(bb[k]));
+          ca[k] = CAP && own ? (int32_t*)(a.capture + cap_offset(l, M_QKV) + cap_item(M_QKV).acc) +
+                                   (size_t)qkv_row(U.X, n) * 12
+                             : nullptr;
+        }
+        const int k = lane & 3;
+        const float y = q8_dot768q_x4(wc, sw, S.xc, S.xsc, ca) + (k == 0 ? bb[0] : k == 1 ? bb[1] : k == 2 ? bb[2] : bb[3]);
+        if (lane < UPW) {
+          const int n = U.qkv(k);
+          const bool own = n < 192 * U.nh;
+          const int r = qkv_row(U.X, own ? n : 0);
+          st_loc(own ? loc + LO_QKV + n : sinkw, pack(y, E));
+          *(own && r >= D ? a.cache + ((size_t)a.pos * L + l) * KV_ROW + (r - D) : sinkf) = y;
+          if (CAP && own) ((float*)(a.capture + cap_offset(l, M_QKV) + cap_item(M_QKV).y))[r] = y;
+        }
       } else
 #pragma unroll
       for (int k = 0; k < UPW; ++k) {
@@ -969,6 +1004,30 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
         if (lane < UPW) {
           const int n = U.cw + U.cwn * k;
           st_loc(n < GS ? loc + LO_G + n : sinkw, pack(gy, E));
+        }
+      } else if constexpr (Q8 && FUSED_TRED) {
+        i4 wc[UPW];
+        float sw[UPW], bb[UPW];
+        int32_t* ca[UPW];
+#pragma unroll
+        for (int k = 0; k < UPW; ++k) {
+          const int n = U.cw + U.cwn * k;
+          wc[k] = R.c[UPW + k];
+          sw[k] = R.sc[UPW + k];
+          bb[k] = R.b[UPW + k];
+          asm volatile("" : "+v"(bb[k]));
+          ca[k] = CAP && n < GS ? (int32_t*)(a.capture + cap_offset(l, M_FC) + cap_item(M_FC).acc) +
+                                      (size_t)(GS * U.X + n) * 12
+                                : nullptr;
+        }
+        const int k = lane & 3;
+        const float y = q8_dot768q_x4(wc, sw, S.xc, S.xsc, ca) + (k == 0 ? bb[0] : k == 1 ? bb[1] : k == 2 ? bb[2] : bb[3]);
+        const float gy = gelu_tanh(y);
+        if (lane < UPW) {
+          const int n = U.cw + U.cwn * k;
+          const bool own = n < GS;
+          st_loc(own ? loc + LO_G + n : sinkw, pack(gy, E));
+          if (CAP && own) ((float*)(a.capture + cap_offset(l, M_FC) + cap_item(M_FC).y))[GS * U.X + n] = y;
         }
       } else
 #pragma unroll
