@@ -492,13 +492,19 @@ __global__ __launch_bounds__(256) void k_special_bits(int kind, uint32_t first, 
 
 // ---- launchers ---------------------------------------------------------------
 
-// Batched step (B > 1) launch shape: rows per wave, sessions staged per pass for the
-// 768- and 3,072-input projections, sessions per workgroup (grid.y = B / BATCH_SB).
+// Batched step (B > 1) launch shape: rows per wave (the 768-input projections; the
+// MLP projection's 3,072-input rows take BATCH_RPW_PR), sessions staged per pass for
+// the 768- and 3,072-input projections, sessions per workgroup (grid.y = B /
+// BATCH_SB).  Four rows a wave reuse each staged input fragment for four outputs
+// (0.877 -> 0.863 ms a step against two rows and eight sessions a pass).
 #ifndef BATCH_RPW
-#define BATCH_RPW 2
+#define BATCH_RPW 4
+#endif
+#ifndef BATCH_RPW_PR
+#define BATCH_RPW_PR 2
 #endif
 #ifndef BATCH_BT768
-#define BATCH_BT768 8
+#define BATCH_BT768 4
 #endif
 #ifndef BATCH_BT3072
 #define BATCH_BT3072 4
@@ -536,7 +542,7 @@ static void launch_proj_ln(const ProjArgs& a, hipStream_t s) {
   if (a.preln) hipLaunchKernelGGL(k_bln<MODE>, dim3(a.ss.B), dim3(64), 0, s, a);
   launch_proj<MODE, RPW, BT, H16>(a, s);
 }
-template <int RPW, int BT768, int BT3072, bool H16>
+template <int RPW, int BT768, int BT3072, bool H16, int RPW_PR = RPW>
 static void launch_layers(ProjArgs& a, hipStream_t s) {
   const int B = a.ss.B;
   hipLaunchKernelGGL(k_embed, dim3(B), dim3(192), 0, s, a.w, a.ss, a.k.x, a.tokp);
@@ -546,7 +552,7 @@ static void launch_layers(ProjArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_attn<false>, dim3(H, B), dim3(attn_threads<false>()), 0, s, a);
     launch_proj<MODE_O, RPW, BT768, H16>(a, s);
     launch_proj_ln<MODE_FC, RPW, BT768, H16>(a, s);
-    launch_proj<MODE_PR, RPW, BT3072, H16>(a, s);
+    launch_proj<MODE_PR, RPW_PR, BT3072, H16>(a, s);
   }
   if (B > 1) {
     ProjArgs ah = a;
@@ -577,7 +583,7 @@ hipError_t launch_step_f32(const Weights& w, const Work& k, const Sessions& ss, 
     launch_layers<2, 1, 1, false>(a, s);
   } else {
     a.preln = BATCH_PRELN;
-    launch_layers<BATCH_RPW, BATCH_BT768, BATCH_BT3072, false>(a, s);
+    launch_layers<BATCH_RPW, BATCH_BT768, BATCH_BT3072, false, BATCH_RPW_PR>(a, s);
   }
   return hipGetLastError();
 }
