@@ -235,11 +235,11 @@ def _block_phases(tr):
     head_rows_start, head_preloaded = med(55, allu), med(57, allu)
     for l in range(12):
         rows[l]["next"] = rows[l + 1]["in"] if l < 11 else head_in
-    # inside block 6 (set 0): regular units' wave 0 (52 own reduce-scatter share polled, 53
-    # all terms in LDS, 54 x published, 56 x1 published) and wave 1 (59 after the QKV
-    # barrier, 60 LayerNorm output loaded, 62 MLP phase start, 63 MLP partials
-    # published); head units' wave 0 (52 terms in LDS, 54 q/k/v received, 56
-    # output-projection terms published)
+    # inside block 6 (set 0): regular units' wave 0 (52 the MLP terms' reduce-scatter
+    # begins, 53 after the workgroup barrier, 54 x published, 56 x1 published) and wave 1
+    # (59 after the QKV barrier, 60 LayerNorm output loaded, 62 MLP phase start, 63 MLP
+    # partials published); head units' wave 0 (52 its reduce-scatter begins, 54 q/k/v
+    # received, 56 output-projection terms published)
     det = {f"r{k}": med(k, reg[0]) for k in (52, 53, 54, 56, 59, 60, 62, 63)}
     det.update({f"h{k}": med(k, head[0]) for k in (52, 54, 56)})
     det.update({"head_rows_start": head_rows_start, "head_preloaded": head_preloaded})
@@ -293,11 +293,11 @@ def timeline_report(g, m, call, filled_cache, stream, positions, reps) -> int:
                   f"preloaded rows used by {det['head_preloaded']:.2f} us")
             b6 = rows[6]["in"]
             print("- inside block 6, us after its x is in LDS (previous block's MLP terms polled -> next input): "
-                  f"regular wave 0: own reduce-scatter share polled {det['r52'] - b6:.2f}, all terms in LDS "
+                  f"regular wave 0: reduce-scatter begins {det['r52'] - b6:.2f}, after the barrier "
                   f"{det['r53'] - b6:.2f}, x published {det['r54'] - b6:.2f}, x1 published {det['r56'] - b6:.2f}; "
                   f"regular wave 1: after QKV barrier {det['r59'] - b6:.2f}, LayerNorm output loaded "
                   f"{det['r60'] - b6:.2f}, MLP phase start {det['r62'] - b6:.2f}, MLP partials published "
-                  f"{det['r63'] - b6:.2f}; head wave 0: terms in LDS {det['h52'] - b6:.2f}, "
+                  f"{det['r63'] - b6:.2f}; head wave 0: reduce-scatter begins {det['h52'] - b6:.2f}, "
                   f"q/k/v received {det['h54'] - b6:.2f}, output-projection terms published "
                   f"{det['h56'] - b6:.2f}\n")
         # per-position step time over the session (events around each launch), median of 3 passes

@@ -155,11 +155,12 @@ __device__ __forceinline__ void stamp(const uint64_t* trace, int slot) {
   if (trace) ((uint64_t*)trace)[blockIdx.x * 64 + slot] = __builtin_amdgcn_s_memrealtime();
 }
 // Head phase (wave 1): 55 head LayerNorm done (rows start), 57 the preloaded rows used.
-// Detail stamps 52..63 inside block 6 (set 0): regular wave 0: 52 own share of the
-// reduce-scatter polled, 53 terms of all waves in LDS, 54 x published, 56 x1
+// Detail stamps 52..63 inside block 6 (set 0): regular wave 0: 52 the MLP terms'
+// reduce-scatter begins (fp32: its x1 share read; int8: its share of the terms
+// polled into LDS), 53 after the workgroup barrier, 54 x published, 56 x1
 // published; regular wave 1: 59 after the QKV barrier, 60 LayerNorm done, 62 MLP
-// phase start, 63 MLP partials published; head wave 0: 52 terms in LDS, 53 x
-// published, 54 q/k/v received, 56 output-projection terms published.
+// phase start, 63 MLP partials published; head wave 0: 52 its reduce-scatter
+// begins, 54 q/k/v received, 56 output-projection terms published.
 constexpr int DETAIL_L = 6;
 __device__ __forceinline__ void dstamp(const uint64_t* trace, int l, int slot) {
   if (l == DETAIL_L && lane_id() == 0) stamp(trace, slot);
