@@ -626,13 +626,13 @@ __device__ __forceinline__ void wave_lds_wait() { asm volatile("s_waitcnt lgkmcn
 
 // ---- attention (one session, one head) --------------------------------------
 // fp32 path, npos keys (1..128):
-//   P_t,r = ((a.x + a.y) + (a.z + a.w)) with a = the float4 sum over i = 0..3
+//   P_t,r = ((a.x + a.y) + (a.z + a.w)) with a = the float4 fmaf chain over i = 0..3
 //     ascending of q[16r+4i..] * K_t[16r+4i..] (quarter r of the 64 dims);
 //   s_t = ((P_t,0 + P_t,1) + (P_t,2 + P_t,3)) * 0.125   (1/sqrt(64));
 //   m = max_t s_t;  e_t = exp_f32(s_t - m);
 //   Z = Z_0 + Z_1 with Z_w = wave_sum of e_t over t in [64w, 64w+64);
 //   w_t = e_t * rcp(Z) (the hardware reciprocal);
-//   p_b = sum over t in [8b, 8b+8), t < npos, ascending, of w_t*V_t,d (b < 16);
+//   p_b = the fmaf chain over t in [8b, 8b+8), t < npos, ascending, of w_t*V_t,d (b < 16);
 //   a_d = ((((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7))) + (((p8+p9)+(p10+p11))+((p12+p13)+(p14+p15)))).
 // Every value is the same for a block of 128, 256 or 512 threads (the work is dealt
 // out in fixed units).
@@ -709,7 +709,10 @@ __device__ __forceinline__ float attn_compute(AttnSmem& sm, int npos) {
     for (int i = 0; i < 4; ++i) {
       const f4 kr = *(const f4*)&sm.k[key][16 * r + 4 * i];
       const f4 qq = *(const f4*)&sm.q[16 * r + 4 * i];
-      acc = acc + qq * kr;
+      acc.x = fmaf(qq.x, kr.x, acc.x);
+      acc.y = fmaf(qq.y, kr.y, acc.y);
+      acc.z = fmaf(qq.z, kr.z, acc.z);
+      acc.w = fmaf(qq.w, kr.w, acc.w);
     }
     float P = (acc.x + acc.y) + (acc.z + acc.w);
     P = P + dpp_f<DPP_QUAD_1032>(P);
@@ -750,8 +753,8 @@ __device__ __forceinline__ float attn_compute(AttnSmem& sm, int npos) {
     float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
-      if (jj < n0) p0 = p0 + w0[jj] * v0[jj];
-      if (jj < n1) p1 = p1 + w1[jj] * v1[jj];
+      if (jj < n0) p0 = fmaf(w0[jj], v0[jj], p0);
+      if (jj < n1) p1 = fmaf(w1[jj], v1[jj], p1);
     }
     sm.part[b0][lane] = p0;
     sm.part[b1][lane] = p1;
