@@ -240,32 +240,37 @@ __device__ __forceinline__ void store_frag(float* __restrict__ dst, const f4 (&x
 
 // LayerNorm of a 768-vector held as a fragment (one wave):
 // mean = (sum x)/768, d = x - mean, var = (sum d*d)/768, r = 1/sqrt(var + 1e-5),
-// y = (d*r)*gamma + beta.  Each lane sums its 12 values in (i, e) order, then the
-// wave_sum combines lanes.
+// y = fmaf(d*r, gamma, beta).  Each lane sums its 12 values as a tree (pairs inside
+// each float4, then the float4 sums), the squares as an fmaf chain per float4, then
+// the wave_sum combines lanes; the statistics are products by 1/768 and the hardware
+// reciprocal square root (within an ulp or two of s/768 and 1/sqrt).  Every fp32 path
+// uses this same function, so they stay identical to each other.
 __device__ __forceinline__ void layernorm_frag(f4 (&x)[3], const float* __restrict__ gamma,
                                                const float* __restrict__ beta) {
-  float s = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 3; ++i) { s = s + x[i].x; s = s + x[i].y; s = s + x[i].z; s = s + x[i].w; }
-  s = wave_sum(s);
-  // the binary32 path's statistics: products by 1/768 and the hardware reciprocal
-  // square root (within an ulp or two of s/768 and 1/sqrt; every fp32 path uses this
-  // same function, so they stay identical to each other)
-  const float mean = s * (1.0f / 768.0f);
-  float v = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    x[i] = x[i] - mean;
-    v = v + x[i].x * x[i].x; v = v + x[i].y * x[i].y; v = v + x[i].z * x[i].z; v = v + x[i].w * x[i].w;
-  }
-  v = wave_sum(v);
-  const float var = v * (1.0f / 768.0f);
-  const float r = __builtin_amdgcn_rsqf(var + 1e-5f);
+  // gamma and beta first, so their reads overlap the statistics
   f4 g[3], b[3];
   load_frag<3>(g, gamma);
   load_frag<3>(b, beta);
+  float s = ((x[0].x + x[0].y) + (x[0].z + x[0].w)) + ((x[1].x + x[1].y) + (x[1].z + x[1].w));
+  s = s + ((x[2].x + x[2].y) + (x[2].z + x[2].w));
+  s = wave_sum(s);
+  const float mean = s * (1.0f / 768.0f);
 #pragma unroll
-  for (int i = 0; i < 3; ++i) x[i] = (x[i] * r) * g[i] + b[i];
+  for (int i = 0; i < 3; ++i) x[i] = x[i] - mean;
+  float q[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) q[i] = fmaf(x[i].w, x[i].w, fmaf(x[i].z, x[i].z, fmaf(x[i].y, x[i].y, x[i].x * x[i].x)));
+  float v = (q[0] + q[1]) + q[2];
+  v = wave_sum(v);
+  const float var = v * (1.0f / 768.0f);
+  const float r = __builtin_amdgcn_rsqf(var + 1e-5f);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    x[i].x = fmaf(x[i].x * r, g[i].x, b[i].x);
+    x[i].y = fmaf(x[i].y * r, g[i].y, b[i].y);
+    x[i].z = fmaf(x[i].z * r, g[i].z, b[i].z);
+    x[i].w = fmaf(x[i].w * r, g[i].w, b[i].w);
+  }
 }
 
 // One output of an fp32 projection: lane l accumulates its 4*NI products with an
