@@ -1057,20 +1057,24 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
       wg_barrier();
     }
     if constexpr (!Q8) {
+      // every LDS read of the phase first (the slice's inputs of the three passes and
+      // the four units' weights), so the dots wait for LDS once
+      const int qq = lane / 16, j = lane % 16;
+      f4 xv[3], wv[UPW][3];
+#pragma unroll
+      for (int p = 0; p < 3; ++p) xv[p] = *(const f4*)(S.xg + 64 * ((4 * p + qq) % GPS) + 4 * j);
+#pragma unroll
+      for (int k = 0; k < UPW; ++k)
+#pragma unroll
+        for (int p = 0; p < 3; ++p) wv[k][p] = H16 ? pr_w16(S.pr, wave, k, p) : pr_w(S.pr, wave, k, p);
 #pragma unroll
       for (int k = 0; k < UPW; ++k) {
         const int u0 = U.cw + U.cwn * k;
         const bool own = u0 < D / 2;
         const int u = own ? u0 : 0;
-        const int qq = lane / 16, j = lane % 16;
         float qv[3];
 #pragma unroll
-        for (int p = 0; p < 3; ++p) {
-          const int kk = 4 * p + qq;
-          const f4 xv = *(const f4*)(S.xg + 64 * (kk % GPS) + 4 * j);
-          if constexpr (H16) qv[p] = dot_q16(pr_w16(S.pr, wave, k, p), xv);
-          else qv[p] = dot_q16(pr_w(S.pr, wave, k, p), xv);
-        }
+        for (int p = 0; p < 3; ++p) qv[p] = dot_q16(wv[k][p], xv[p]);
         auto val = [&](int kk) { return lane_val(qv[kk / 4], 16 * (kk % 4)); };
         float p0 = val(0), p1 = val(GPS);
 #pragma unroll
