@@ -551,16 +551,27 @@ __device__ __forceinline__ float seq_sum768_wg(const float* t, float* tab) {
       sc[k] = eb < 0 ? ~((uint32_t)eb + (uint32_t)(SEQ_NC / 2)) : (uint32_t)eb - (uint32_t)(SEQ_NC / 2);
       asm volatile("" : "+s"(sm[k]), "+s"(sc[k]));  // formed before the walk, not inside its steps
     }
-    // The steps run straight through; a miss runs the segment's chain in place.
-    uint32_t sb = 0;
+    // The steps run straight through with no branch (an index out of range is only
+    // recorded); if one was out of range, the walk runs again, and a miss there runs
+    // the segment's chain in place.
+    uint32_t sb = 0, seen = 0;
 #pragma unroll
     for (int k = 0; k < SEQ_NS; ++k) {
       const uint32_t dd = (sb ^ sm[k]) - sc[k];
-      if (__builtin_expect(dd < (uint32_t)SEQ_NC, 1))
-        sb = (uint32_t)__builtin_amdgcn_readlane(__float_as_int(tv[k / 4][k % 4]), (int)dd);
-      else
-        sb = (uint32_t)__builtin_amdgcn_readfirstlane(
-            __float_as_int(seq_chain96(__uint_as_float(sb), t + SEQ_LEN * k)));
+      seen |= dd;  // >= SEQ_NC iff some step's index was out of range
+      sb = (uint32_t)__builtin_amdgcn_readlane(__float_as_int(tv[k / 4][k % 4]), (int)(dd & (SEQ_NC - 1)));
+    }
+    if (__builtin_expect(seen >= (uint32_t)SEQ_NC, 0)) {
+      sb = 0;
+#pragma unroll
+      for (int k = 0; k < SEQ_NS; ++k) {
+        const uint32_t dd = (sb ^ sm[k]) - sc[k];
+        if (dd < (uint32_t)SEQ_NC)
+          sb = (uint32_t)__builtin_amdgcn_readlane(__float_as_int(tv[k / 4][k % 4]), (int)dd);
+        else
+          sb = (uint32_t)__builtin_amdgcn_readfirstlane(
+              __float_as_int(seq_chain96(__uint_as_float(sb), t + SEQ_LEN * k)));
+      }
     }
     if (lane == 0) tab[SEQ_TAB_RESULT] = __uint_as_float(sb);
   }
