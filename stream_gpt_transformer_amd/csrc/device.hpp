@@ -176,6 +176,16 @@ __device__ __forceinline__ int treduce_out(int t) {
   for (int k = 0; (1 << k) < N; ++k) o |= treduce_c(t, k) << k;
   return o;
 }
+// The first lane t of a row with treduce_out<N>(t) == o (a compile-time constant).
+template <int N>
+__host__ __device__ constexpr int treduce_lane(int o) {
+  for (int t = 0; t < 16; ++t) {
+    int oo = 0;
+    for (int k = 0; (1 << k) < N; ++k) oo |= (k < 3 ? ((t >> k) ^ (t >> (k + 1))) & 1 : (t >> 3) & 1) << k;
+    if (oo == o) return t;
+  }
+  return -1;
+}
 template <int CTRL, int N>
 __device__ __forceinline__ void treduce_level(float (&a)[16], int& n, bool c) {
   if (n >= 2) {

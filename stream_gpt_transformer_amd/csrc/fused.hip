@@ -68,6 +68,9 @@ constexpr int GPS = GS / 64;             // groups per slice (6)
 constexpr int NG_PR = F / 64;            // int8 MLP-projection groups (48)
 constexpr int NCW = NWV - 1;             // compute waves of a regular unit (waves 1..7)
 constexpr int UPW = 4;                   // units per compute wave per phase
+#ifndef FUSED_MLP_TRED
+#define FUSED_MLP_TRED 1
+#endif
 #ifndef FUSED_TRED
 #define FUSED_TRED 1
 #endif
@@ -1072,6 +1075,52 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
       for (int k = 0; k < UPW; ++k)
 #pragma unroll
         for (int p = 0; p < 3; ++p) wv[k][p] = H16 ? pr_w16(S.pr, wave, k, p) : pr_w(S.pr, wave, k, p);
+#if FUSED_MLP_TRED
+      // The four units' group dots of a pass reduced together (row_treduce: the adds of
+      // dot_q16's row16_sum): g[p] in lane t of row qq holds group kk = 4p + qq of unit
+      // treduce_out<4>(t).  The slice sums then run in group order in the lanes of row
+      // 0 for all four units at once, each group moved there from its row: row 2u adds
+      // groups 0..5, row 2u+1 groups 6..11 (pr_row's order).
+      static_assert(UPW == 4 && GPS == 6, "MLP phase layout");
+      float g[3];
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        float lp[UPW];
+#pragma unroll
+        for (int k = 0; k < UPW; ++k) {
+          float acc = 0.0f;
+          acc = fmaf(wv[k][p].x, xv[p].x, acc);
+          acc = fmaf(wv[k][p].y, xv[p].y, acc);
+          acc = fmaf(wv[k][p].z, xv[p].z, acc);
+          acc = fmaf(wv[k][p].w, xv[p].w, acc);
+          lp[k] = acc;
+        }
+        g[p] = row_treduce<UPW>(lp);
+      }
+      float p0 = g[0];
+      p0 = p0 + row1_to_row0(g[0]);
+      p0 = p0 + row2_to_row0(g[0]);
+      p0 = p0 + row3_to_row0(g[0]);
+      p0 = p0 + g[1];
+      p0 = p0 + row1_to_row0(g[1]);
+      float p1 = row2_to_row0(g[1]);
+      p1 = p1 + row3_to_row0(g[1]);
+      p1 = p1 + g[2];
+      p1 = p1 + row1_to_row0(g[2]);
+      p1 = p1 + row2_to_row0(g[2]);
+      p1 = p1 + row3_to_row0(g[2]);
+#pragma unroll
+      for (int k = 0; k < UPW; ++k) {
+        const int u0 = U.cw + U.cwn * k;
+        const bool own = u0 < D / 2;
+        const int u = own ? u0 : 0;
+        constexpr int TK[4] = {treduce_lane<4>(0), treduce_lane<4>(1), treduce_lane<4>(2), treduce_lane<4>(3)};
+        const float a0 = lane_val(p0, TK[k]), a1 = lane_val(p1, TK[k]);
+        // lanes 0..31 store row 2u, lanes 32..63 row 2u+1
+        const int half = lane >> 5;
+        st_sc1(own ? glb + GL_P + (size_t)U.X * D + 2 * u + half : sinkw, pack(half ? a1 : a0, E));
+      }
+#else
 #pragma unroll
       for (int k = 0; k < UPW; ++k) {
         const int u0 = U.cw + U.cwn * k;
@@ -1091,6 +1140,7 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
         const int half = lane >> 5;
         st_sc1(own ? glb + GL_P + (size_t)U.X * D + 2 * u + half : sinkw, pack(half ? p1 : p0, E));
       }
+#endif
     } else {
 #pragma unroll
       for (int k = 0; k < UPW; ++k) {
