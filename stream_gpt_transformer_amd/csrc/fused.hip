@@ -748,17 +748,27 @@ __device__ __forceinline__ void head_rows(const FusedArgs a, FusedSmem& S, WRegs
     layernorm_frag(x, S.lnf[0], S.lnf[1]);
   }
   if constexpr (!Q8) {
+    // four rows at a time: their lane partials reduced together (wave_treduce, the
+    // adds of dot_slots' wave_sum); lane t stores row k0 + treduce_out<4>(t)
+    constexpr int HR = 4;
+    static_assert(NS % HR == 0, "head row groups");
 #pragma unroll
-    for (int k = 0; k < NMAX; ++k) {
+    for (int k0 = 0; k0 < NMAX; k0 += HR) {
       // keep the loads in slot order: at most NHS rows in flight per wave
       __builtin_amdgcn_sched_barrier(0);
-      if (k < hr.n) {  // a uniform guard, not a break: the loop stays fully unrolled
-        const int r = hr.first + k * HEAD_SET_WAVES;
-        const int s = k % NS;
-        const float y = dot_slots(R, 3 * s, x);
-        *(r < V ? a.logits + r : sinkf) = y;
-        if (k + NS < hr.n) load_head<Q8, H16>(R, a.w, s, r + NS * HEAD_SET_WAVES);
-        if (k == NS - 1 && lane == 0 && (threadIdx.x >> 6) == 1) stamp(a.trace, 57);
+      if (k0 < hr.n) {  // a uniform guard, not a break: the loop stays fully unrolled
+        float lp[HR];
+#pragma unroll
+        for (int u = 0; u < HR; ++u) lp[u] = dot_slots_lane<H16>(R, 3 * ((k0 + u) % NS), x);
+        const float y = wave_treduce<HR>(lp);
+        const int k = k0 + treduce_out<HR>(lane & 15), r = hr.first + k * HEAD_SET_WAVES;
+        *(k < hr.n && r < V ? a.logits + r : sinkf) = y;  // a row past hr.n used a stale slot
+#pragma unroll
+        for (int u = 0; u < HR; ++u) {
+          const int ku = k0 + u;
+          if (ku + NS < hr.n) load_head<Q8, H16>(R, a.w, ku % NS, hr.first + (ku + NS) * HEAD_SET_WAVES);
+        }
+        if (k0 + HR == NS && lane == 0 && (threadIdx.x >> 6) == 1) stamp(a.trace, 57);
       }
     }
   } else {
