@@ -1168,9 +1168,17 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
     if (wave == 1) dstamp(a.trace, l, 63);
     // this block is done: the weights of the set's next block (or the first head rows).
     // The MLP terms have reached memory before that stream starts: stores still queued
-    // behind a wave's weight loads would hold up the other set's reduce-scatter.
+    // behind a wave's weight loads would hold up the other set's reduce-scatter.  The
+    // stream then waits a little longer (s_sleep: 64 clocks a unit, ~2.8 µs binary32, ~1.8
+    // µs int8), so that its first burst does not meet the other set's reduce-scatter of
+    // these terms and the start of the next block; it still has most of a block to land.
+    // Measured: fp32 126.7 -> 125.6 µs, int8 208.3 -> 207.1 µs; at 127 units (3.5 µs) the
+    // fp32 step is slower (127.9 µs).
     wave_vmem_sync();
-    if (l + 2 < L) load_block<Q8, H16>(R, S.pr, a.w, l + 2, U, wave);
+    if (l + 2 < L) {
+      __builtin_amdgcn_s_sleep(Q8 ? 64 : 100);
+      load_block<Q8, H16>(R, S.pr, a.w, l + 2, U, wave);
+    }
   }
   // The first head rows, outside the loop, so the slots past the block weights are not
   // live across it.  (Filling the slots whose block rows are used up during set 1's last
