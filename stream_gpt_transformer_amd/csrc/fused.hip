@@ -554,6 +554,11 @@ __device__ __forceinline__ void load_head(WRegs<Q8, H16>& R, const Weights& w, i
     q8_load_row768q(R.c[s], R.sc[s], q8_codes(w, 0, M_HEAD), q8_scales(w, 0, M_HEAD), r);
   }
 }
+// Set 0 fills its head slots while set 1 computes the last block.  It waits ~1.8 µs
+// first (s_sleep: 64 clocks a unit), so that the 50 MB burst does not meet set 1's
+// reduce-scatter of block 10's MLP terms and the start of block 11: fp32 125.5 -> 125.05
+// µs (binary32 and binary16; int8 0.25 µs slower with it, so it does not wait).
+__device__ __forceinline__ void head_fill_wait() { __builtin_amdgcn_s_sleep(64); }
 template <bool Q8, bool H16>
 __device__ __forceinline__ void load_head_slots(WRegs<Q8, H16>& R, const Weights& w, HeadRows hr) {
 #pragma unroll
@@ -903,7 +908,10 @@ __device__ __forceinline__ void regular_io(const FusedArgs& a, FusedSmem& S, con
   // block 11 (they land long before its block-11 polls, which would otherwise return
   // behind them); otherwise the input wave fills them when the head starts (int8:
   // filling them here measured 4.7 µs slower).
-  if (!Q8 && c.set == 0) load_head_slots<Q8, H16>(R, a.w, head_rows_of<Q8>(c, 0));
+  if (!Q8 && c.set == 0) {
+    head_fill_wait();
+    load_head_slots<Q8, H16>(R, a.w, head_rows_of<Q8>(c, 0));
+  }
   float x1p = 0.0f;
   if (c.set == 0) {
     x1p = x1_share(a, c, L - 1);
@@ -1183,6 +1191,7 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
   // The first head rows, outside the loop, so the slots past the block weights are not
   // live across it.  (Filling the slots whose block rows are used up during set 1's last
   // block, to start its head stream earlier, delays that block's MLP terms: slower.)
+  if (!Q8 && c.set == 0) head_fill_wait();
   load_head_slots<Q8, H16>(R, a.w, head_rows_of<Q8>(c, wave));
   if (c.set == 0) rs_pr_poll<Q8>(a, S, c, L - 1, wave);
   wg_barrier();  // BT
@@ -1321,6 +1330,7 @@ __device__ __forceinline__ void head_unit(const FusedArgs& a, FusedSmem& S, cons
     }
     wg_barrier();
   }
+  if (!Q8 && c.set == 0) head_fill_wait();
   load_head_slots<Q8, H16>(R, a.w, head_rows_of<Q8>(c, wave));
   float x1p = 0.0f;
   if (c.set == 0) {
