@@ -937,6 +937,10 @@ __device__ __forceinline__ void regular_compute(const FusedArgs& a, FusedSmem& S
   U.cw = (wave - 1) * (NQ - c.nh) + (c.q - c.nh);
   const int l0 = c.set;
   defer_set1(c, a.header);
+  // Binary32: set 0's block-0 stream starts ~0.2 µs after the head units' output-projection
+  // staging, which the block-0 attention waits for (124.8 -> 124.5 µs; the int8 and
+  // binary16 steps are 0.5 µs slower with it, so they do not wait).
+  if (!Q8 && !H16 && c.set == 0) __builtin_amdgcn_s_sleep(8);
   load_block<Q8, H16>(R, S.pr, a.w, l0, U, wave);
   wg_barrier();  // B0
   for (int l = l0; l < L; l += 2) {
