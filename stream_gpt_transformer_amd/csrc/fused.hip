@@ -1325,6 +1325,9 @@ __device__ __forceinline__ void head_unit(const FusedArgs& a, FusedSmem& S, cons
     wg_barrier();  // the keys/values of block l are no longer read
     const int ln = l + 2;
     if (ln < L) {
+      // int8: the next block's staging waits ~0.9 µs, past this block's reduce-scatter of
+      // the output-projection terms (206.85 -> 206.4 µs; binary32 unchanged, so it does not)
+      if constexpr (Q8) __builtin_amdgcn_s_sleep(32);
       load_o_head<Q8, H16>(R, (char*)&S.pr, a.w, ln, h);
       stage_kv(a, S, ln, h);
     }
