@@ -131,8 +131,8 @@ def test_rejections_leave_outputs_untouched():
     assert torch.all(lg == 7.0) and torch.all(cache == 0)
 
 
-@pytest.mark.parametrize("q8", [False, True], ids=["fp32", "int8"])
-def test_timestamp_hook_changes_no_bits_and_orders_phases(q8):
+@pytest.mark.parametrize("q8,f16", [(False, False), (True, False), (False, True)], ids=["fp32", "int8", "binary16"])
+def test_timestamp_hook_changes_no_bits_and_orders_phases(q8, f16):
     """With the single-launch step's timestamp hook on, a session computes the same bits.
     Every workgroup stamps its start, head input, head rows done and end in that order;
     the units of the set that computes block l stamp that block's phase inputs in causal
@@ -140,13 +140,13 @@ def test_timestamp_hook_changes_no_bits_and_orders_phases(q8):
     units: reduce-scatter share, attention output, x1 published), and no unit stamps a
     block of the other set.  Turned off, the hook writes nothing."""
     need_gpu()
-    m = model()
+    m = model(flags=g.GPT2_PACK_F32 | g.GPT2_PACK_Q8 | g.GPT2_PACK_F16) if f16 else model()
     toks = synth.make_tokens(23, 6)
-    ref, cref = gpu_session(m, toks, q8=q8)
+    ref, cref = gpu_session(m, toks, q8=q8, f16=f16)
     trace = torch.zeros(256 * 64, dtype=torch.int64, device="cuda")
     g.gpt2_test_fused_trace(trace.data_ptr())
     try:
-        got, cgot = gpu_session(m, toks, q8=q8)  # the trace holds the last step's stamps
+        got, cgot = gpu_session(m, toks, q8=q8, f16=f16)  # the trace holds the last step's stamps
     finally:
         g.gpt2_test_fused_trace(None)
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
@@ -172,7 +172,7 @@ def test_timestamp_hook_changes_no_bits_and_orders_phases(q8):
     trace.zero_()
     cache = m.new_cache(1)
     lg = torch.empty(g.GPT2_VOCAB, dtype=torch.float32, device="cuda")
-    m.step(cache, 0, int(toks[0]), lg, q8=q8)
+    m.step(cache, 0, int(toks[0]), lg, q8=q8, f16=f16)
     torch.cuda.synchronize()
     assert int(trace.abs().sum().item()) == 0
     assert m.status() == 0
